@@ -1,0 +1,140 @@
+"""Planted mistakes in the oracle must be caught by the pins.
+
+Each mutant below is a plausible bug (wrong rounding, wrong format variant,
+wrong scale formula, wrong grouping axis, a dropped transpose or scale).  The
+test asserts that at least one pin from tests/pins.py rejects it, which shows
+the pins that hold for the real oracle are not vacuous.  Everything runs on
+the CPU.
+"""
+import numpy as np
+import pytest
+
+import pins
+from oracle import e4m3_decode, e4m3_encode, gemm_ref, quantize_act, quantize_act_transposed
+
+DEC = e4m3_decode(np.arange(256, dtype=np.uint8))
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except AssertionError:
+        return True
+    return False
+
+
+# ---- codec mutants -------------------------------------------------------
+
+def enc_round_half_away(y):
+    y = np.asarray(y, np.float32)
+    out = e4m3_encode(y)
+    # replace ties-to-even by ties-away on exact midpoints
+    a = np.abs(y.astype(np.float64))
+    lo = e4m3_encode(np.nextafter(np.abs(y), np.float32(0)))
+    hi = e4m3_encode(np.nextafter(np.abs(y), np.float32(np.inf)))
+    mid = (lo != hi) & (np.abs(DEC[lo & 0x7F] - a) == np.abs(DEC[hi & 0x7F] - a))
+    return np.where(mid, hi | (out & 0x80), out).astype(np.uint8)
+
+
+def enc_fnuz_max240(y):
+    y = np.clip(np.asarray(y, np.float32), -240.0, 240.0)
+    return e4m3_encode(y)
+
+
+def enc_truncate(y):
+    y = np.asarray(y, np.float32)
+    out = e4m3_encode(y)
+    back = DEC[out & 0x7F]
+    over = back > np.abs(y.astype(np.float64))
+    return np.where(over & ((out & 0x7F) > 0), out - 1, out).astype(np.uint8)
+
+
+@pytest.mark.parametrize("mutant", [enc_round_half_away, enc_fnuz_max240, enc_truncate])
+def test_codec_mutants_are_caught(mutant):
+    assert _fails(pins.check_encode_points, mutant, pins.critical_points())
+
+
+# ---- quantiser mutants ---------------------------------------------------
+
+def _group(x, denom=448.0, mult_by_scale=False, fmt_max=448.0):
+    x = np.asarray(x, np.float32)
+    amax = np.float32(np.max(np.abs(x)))
+    if amax == 0:
+        return e4m3_encode(x), np.float32(1)
+    s = np.float32(amax / np.float32(denom))
+    inv = s if mult_by_scale else np.float32(np.float32(denom) / amax)
+    return e4m3_encode(np.clip(x * inv, -fmt_max, fmt_max)), s
+
+
+def q_denominator_447(x):
+    return _group(x, denom=447.0)
+
+
+def q_mult_by_scale(x):
+    return _group(x, mult_by_scale=True)
+
+
+def q_scale_for_240(x):
+    return _group(x, denom=240.0, fmt_max=240.0)
+
+
+def q_nonzero_scale_for_zero_group(x):
+    x = np.asarray(x, np.float32)
+    if np.max(np.abs(x)) == 0:
+        return e4m3_encode(x), np.float32(0.0)
+    return _group(x)
+
+
+@pytest.mark.parametrize("mutant", [q_denominator_447, q_mult_by_scale, q_scale_for_240,
+                                    q_nonzero_scale_for_zero_group])
+def test_quantiser_mutants_are_caught(mutant):
+    rng = np.random.default_rng(0)
+    caught = (_fails(pins.check_amax_maps_to_448, mutant, rng)
+              or _fails(pins.check_exact_representability, mutant, DEC, rng)
+              or _fails(pins.check_roundtrip_bound, mutant, rng)
+              or _fails(pins.check_zero_group, mutant))
+    assert caught
+
+
+def test_transposed_grouping_mutant_is_caught():
+    # groups taken along the channel axis instead of the token axis
+    def bad_transposed(x):
+        q, s = quantize_act(x)  # groups along channels
+        return np.ascontiguousarray(q.T), None
+
+    rng = np.random.default_rng(1)
+    x = rng.standard_t(3, (256, 256)).astype(np.float32)
+    qt, _ = quantize_act_transposed(x)
+    qb, _ = bad_transposed(x)
+    q2, _ = quantize_act(np.ascontiguousarray(x.T))
+    assert (qt == q2).all() and not (qb == q2).all()
+
+
+# ---- GEMM mutants --------------------------------------------------------
+
+def gemm_dropped_b_scale(layout, qa, sa, ma, qb, sb, mb):
+    return gemm_ref(layout, qa, sa, ma, qb, np.ones_like(sb), mb)
+
+
+def gemm_transposed_block_grid(layout, qa, sa, ma, qb, sb, mb):
+    if mb == "block" and sb.shape[0] == sb.shape[1]:
+        sb = np.ascontiguousarray(sb.T)
+    return gemm_ref(layout, qa, sa, ma, qb, sb, mb)
+
+
+@pytest.mark.parametrize("mutant", [gemm_dropped_b_scale, gemm_transposed_block_grid])
+def test_gemm_mutants_are_caught(mutant):
+    rng = np.random.default_rng(2)
+    qa, sa, qb, sb = pins.integer_exact_operands(rng, "NT", "act", "block", 256, 256, 256)
+    E = pins.exact_gemm_int("NT", qa, sa, "act", qb, sb, "block")
+    assert (gemm_ref("NT", qa, sa, "act", qb, sb, "block") == E).all()
+    assert not (mutant("NT", qa, sa, "act", qb, sb, "block") == E).all()
+
+
+def test_gemm_wrong_operand_orientation_is_caught():
+    rng = np.random.default_rng(3)
+    qa, sa, qb, sb = pins.integer_exact_operands(rng, "NN", "act", "block", 256, 256, 256)
+    E = pins.exact_gemm_int("NN", qa, sa, "act", qb, sb, "block")
+    # reading the NN operand as if it were NT (B stored [N][K]) is a transpose bug
+    wrong = gemm_ref("NT", qa, sa, "act", qb, np.ascontiguousarray(sb.T), "block")
+    assert not (wrong == E).all()
