@@ -38,7 +38,7 @@ from .quant import (
     quantize_weight,
     GROUP,
 )
-from .gemm import dequantize_operand, gemm_ref, rel_error
+from .gemm import dequantize_operand, gemm_ref, normwise_error, rel_error
 
 __all__ = [
     "e4m3_decode",
@@ -52,4 +52,5 @@ __all__ = [
     "dequantize_operand",
     "gemm_ref",
     "rel_error",
+    "normwise_error",
 ]
