@@ -1,0 +1,161 @@
+// libbfp8 C ABI: argument validation and dispatch.
+//
+// Every entry point checks its arguments on the host before the first HIP
+// call and reports problems as bfp8_status codes; the kernels themselves
+// live in quantize.hip and gemm.hip.  See include/bfp8.h for the contract.
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+using namespace bfp8;
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int64_t elem_bytes(bfp8_in_dtype dt) { return dt == BFP8_IN_F32 ? 4 : 2; }
+
+inline bool valid_dtype(bfp8_in_dtype dt) { return dt == BFP8_IN_BF16 || dt == BFP8_IN_F32; }
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int64_t kMaxGridY = 65535;
+
+// The GEMM reads every layout in place (no transposed copies), so no
+// workspace is needed; the argument is kept in the ABI for variants that do.
+inline size_t gemm_workspace(bfp8_layout, bfp8_scale_mode, bfp8_scale_mode, int64_t, int64_t,
+                             int64_t) {
+  return 0;
+}
+
+// Largest leading dimension (bytes) the GEMM addresses with 32-bit offsets.
+constexpr int64_t kMaxGemmLd = int64_t(1) << 22;
+
+inline bfp8_status check_quant_common(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
+                                      int64_t ldx, const void* q, int64_t ldq, const void* s) {
+  if (!valid_dtype(dt)) return BFP8_ERR_DTYPE;
+  if (rows < 0 || cols < 0) return BFP8_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return BFP8_OK;
+  if (x == nullptr || q == nullptr || s == nullptr) return BFP8_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return BFP8_ERR_ALIGN;
+  if (ldx < cols || ldq < 0) return BFP8_ERR_SHAPE;
+  if ((ldx * elem_bytes(dt)) % 16 != 0 || ldq % 16 != 0) return BFP8_ERR_ALIGN;
+  return BFP8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bfp8_abi_version(void) { return BFP8_ABI_VERSION; }
+
+const char* bfp8_status_str(bfp8_status status) {
+  switch (status) {
+    case BFP8_OK: return "ok";
+    case BFP8_ERR_NULL: return "null pointer";
+    case BFP8_ERR_SHAPE: return "invalid shape (negative size, grouped axis not a multiple of 128, "
+                                "leading dimension too small, or size limit exceeded)";
+    case BFP8_ERR_ALIGN: return "pointer or leading dimension not 16-byte aligned";
+    case BFP8_ERR_DTYPE: return "unknown input dtype";
+    case BFP8_ERR_LAYOUT: return "unknown GEMM layout";
+    case BFP8_ERR_SCALE_MODE: return "unknown scale mode";
+    case BFP8_ERR_WORKSPACE: return "workspace missing or too small";
+    case BFP8_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+bfp8_status bfp8_quantize_act(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
+                              int64_t ldx, uint8_t* q, int64_t ldq, float* s,
+                              hipStream_t stream) {
+  if (cols % 128 != 0 && cols > 0) return valid_dtype(dt) ? BFP8_ERR_SHAPE : BFP8_ERR_DTYPE;
+  bfp8_status st = check_quant_common(x, dt, rows, cols, ldx, q, ldq, s);
+  if (st != BFP8_OK || rows == 0 || cols == 0) return st;
+  if (ldq < cols) return BFP8_ERR_SHAPE;
+  if (rows * (cols / 128) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+  return launch_quantize_act(x, dt, rows, cols, ldx, q, ldq, s, stream);
+}
+
+bfp8_status bfp8_quantize_act_transposed(const void* x, bfp8_in_dtype dt, int64_t rows,
+                                         int64_t cols, int64_t ldx, uint8_t* qt,
+                                         int64_t ldqt, float* st_, hipStream_t stream) {
+  if (rows % 128 != 0 && rows > 0) return valid_dtype(dt) ? BFP8_ERR_SHAPE : BFP8_ERR_DTYPE;
+  bfp8_status st = check_quant_common(x, dt, rows, cols, ldx, qt, ldqt, st_);
+  if (st != BFP8_OK || rows == 0 || cols == 0) return st;
+  if (ldqt < rows) return BFP8_ERR_SHAPE;
+  if (rows / 128 > kMaxGridY || cdiv(cols, 64) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+  return launch_quantize_act_transposed(x, dt, rows, cols, ldx, qt, ldqt, st_, stream);
+}
+
+bfp8_status bfp8_quantize_weight(const void* w, bfp8_in_dtype dt, int64_t rows, int64_t cols,
+                                 int64_t ldw, uint8_t* q, int64_t ldq, float* s,
+                                 hipStream_t stream) {
+  bfp8_status st = check_quant_common(w, dt, rows, cols, ldw, q, ldq, s);
+  if (st != BFP8_OK || rows == 0 || cols == 0) return st;
+  if (ldq < cols) return BFP8_ERR_SHAPE;
+  if (cdiv(rows, 128) > kMaxGridY || cdiv(cols, 128) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+  return launch_quantize_weight(w, dt, rows, cols, ldw, q, ldq, s, stream);
+}
+
+size_t bfp8_gemm_workspace_bytes(bfp8_layout layout, bfp8_scale_mode modeA,
+                                 bfp8_scale_mode modeB, int64_t M, int64_t N, int64_t K) {
+  if (layout != BFP8_NN && layout != BFP8_NT && layout != BFP8_TN) return static_cast<size_t>(-1);
+  if ((modeA != BFP8_SCALE_1x128 && modeA != BFP8_SCALE_128x128) ||
+      (modeB != BFP8_SCALE_1x128 && modeB != BFP8_SCALE_128x128))
+    return static_cast<size_t>(-1);
+  if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return static_cast<size_t>(-1);
+  return gemm_workspace(layout, modeA, modeB, M, N, K);
+}
+
+bfp8_status bfp8_gemm(bfp8_layout layout, int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                      int64_t lda, const float* sA, bfp8_scale_mode modeA, const uint8_t* B,
+                      int64_t ldb, const float* sB, bfp8_scale_mode modeB, void* C,
+                      int64_t ldc, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  if (layout != BFP8_NN && layout != BFP8_NT && layout != BFP8_TN) return BFP8_ERR_LAYOUT;
+  if ((modeA != BFP8_SCALE_1x128 && modeA != BFP8_SCALE_128x128) ||
+      (modeB != BFP8_SCALE_1x128 && modeB != BFP8_SCALE_128x128))
+    return BFP8_ERR_SCALE_MODE;
+  if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return BFP8_ERR_SHAPE;
+  if (M == 0 || N == 0) return BFP8_OK;
+  if (C == nullptr) return BFP8_ERR_NULL;
+  if (!aligned16(C)) return BFP8_ERR_ALIGN;
+  if (ldc < N) return BFP8_ERR_SHAPE;
+  if (ldc % 8 != 0) return BFP8_ERR_ALIGN;
+  if (cdiv(M, 256) * cdiv(N, 256) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+  if (K == 0) return launch_fill_bf16_zero(static_cast<uint16_t*>(C), M, N, ldc, stream);
+
+  if (A == nullptr || B == nullptr || sA == nullptr || sB == nullptr) return BFP8_ERR_NULL;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(sA) || !aligned16(sB)) return BFP8_ERR_ALIGN;
+  const bool a_kmajor = layout == BFP8_TN;   // A 'T' stored [K][M]
+  const bool b_kmajor = layout != BFP8_NT;   // B 'N' stored [K][N]
+  const int64_t a_row = a_kmajor ? M : K;    // stored row length
+  const int64_t b_row = b_kmajor ? N : K;
+  if (lda < a_row || ldb < b_row) return BFP8_ERR_SHAPE;
+  if (lda % 16 != 0 || ldb % 16 != 0) return BFP8_ERR_ALIGN;
+  if (lda > kMaxGemmLd || ldb > kMaxGemmLd) return BFP8_ERR_SHAPE;
+  const size_t need = gemm_workspace(layout, modeA, modeB, M, N, K);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return BFP8_ERR_WORKSPACE;
+
+  GemmArgs g;
+  g.A = A;
+  g.lda = lda;
+  g.sA = sA;
+  g.modeA = modeA == BFP8_SCALE_1x128 ? 0 : 1;
+  g.a_kmajor = a_kmajor;
+  g.B = B;
+  g.ldb = ldb;
+  g.sB = sB;
+  g.modeB = modeB == BFP8_SCALE_1x128 ? 0 : 1;
+  g.b_kmajor = b_kmajor;
+  g.C = static_cast<uint16_t*>(C);
+  g.ldc = ldc;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  return launch_gemm(g, stream);
+}
+
+}  // extern "C"

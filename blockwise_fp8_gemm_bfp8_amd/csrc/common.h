@@ -1,0 +1,116 @@
+// Internal helpers shared by the libbfp8 HIP sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bfp8.h"
+
+namespace bfp8 {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kGroup = 128;        // elements per activation group / block edge
+constexpr float kE4M3Max = 448.0f; // largest finite OCP E4M3 value
+
+// Exact widening of a bfloat16 bit pattern to float32.
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+  return __uint_as_float(b16 << 16);
+}
+
+// float32 -> bfloat16 bits, round to nearest even (inputs are finite here).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Group scale and its reciprocal multiplier.  s = fl32(amax / 448) and
+// inv = fl32(448 / amax), both IEEE-rounded divisions; an all-zero group
+// gets s = inv = 1 so its (signed) zeros encode as zeros.
+__device__ __forceinline__ void group_scale(float amax, float& s, float& inv) {
+  if (amax == 0.0f) {
+    s = 1.0f;
+    inv = 1.0f;
+  } else {
+    s = amax / kE4M3Max;
+    inv = kE4M3Max / amax;
+  }
+}
+
+// Four float32 -> four E4M3 codes packed little-endian in one dword.
+// Saturation is done by the clamp (the conversion instruction's own
+// overflow result is NaN); the conversion rounds to nearest even and keeps
+// the sign of zero.
+__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -kE4M3Max), kE4M3Max);
+  b = fminf(fmaxf(b, -kE4M3Max), kE4M3Max);
+  c = fminf(fmaxf(c, -kE4M3Max), kE4M3Max);
+  d = fminf(fmaxf(d, -kE4M3Max), kE4M3Max);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+// Max over the 16 lanes of a DPP row (the value is replicated to all 16).
+__device__ __forceinline__ float row16_max(float v) {
+  // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
+
+// Max over the 4 lanes of a quad.
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  return v;
+}
+
+// Max over all 64 lanes of a wave (result valid in every lane).
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+// Host-side launch helpers (defined in the .hip files).
+bfp8_status launch_quantize_act(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
+                                int64_t ldx, uint8_t* q, int64_t ldq, float* s,
+                                hipStream_t stream);
+bfp8_status launch_quantize_act_transposed(const void* x, bfp8_in_dtype dt, int64_t rows,
+                                           int64_t cols, int64_t ldx, uint8_t* qt,
+                                           int64_t ldqt, float* st, hipStream_t stream);
+bfp8_status launch_quantize_weight(const void* w, bfp8_in_dtype dt, int64_t rows, int64_t cols,
+                                   int64_t ldw, uint8_t* q, int64_t ldq, float* s,
+                                   hipStream_t stream);
+
+struct GemmArgs {
+  // Operands as stored.  a_kmajor: A stored [K][M] (else [M][K]);
+  // b_kmajor: B stored [K][N] (else [N][K]).  Scale layouts follow the
+  // stored orientation (see include/bfp8.h).
+  const uint8_t* A;
+  int64_t lda;
+  const float* sA;
+  int modeA;  // 0 = 1x128 act groups, 1 = 128x128 blocks
+  bool a_kmajor;
+  const uint8_t* B;
+  int64_t ldb;
+  const float* sB;
+  int modeB;
+  bool b_kmajor;
+  uint16_t* C;  // bf16 bits
+  int64_t ldc;
+  int64_t M, N, K;
+};
+
+bfp8_status launch_gemm(const GemmArgs& a, hipStream_t stream);
+bfp8_status launch_fill_bf16_zero(uint16_t* C, int64_t M, int64_t N, int64_t ldc,
+                                  hipStream_t stream);
+
+}  // namespace bfp8

@@ -1,0 +1,414 @@
+// Blockwise FP8 GEMM for gfx950: C = sum_kb (A_kb . B_kb) * sA * sB -> bf16.
+//
+// Puro-2B paper, zh-TW translation (papers.lianghsun.dev), section 2 and
+// section 3.2: the main Transformer linear-layer GEMMs run on E4M3 operands
+// with fine-grained (DeepSeek-V3 style) scales -- 1x128 groups along K for
+// activations and activation gradients, 128x128 blocks for weights.  Each
+// 128-deep K block yields an fp32 partial from the matrix cores that is
+// multiplied by a_scale * b_scale and added into an fp32 accumulator; the
+// result is stored as bf16.
+//
+// Kernel shape (one 256x256 output tile per 512-thread workgroup, one
+// workgroup per CU):
+//   * global -> LDS with buffer_load ... lds (no VGPR staging), two stages
+//     of 256x128 A bytes + 256x128 B bytes + 2x256 act-mode scales;
+//   * K-contiguous operands sit in LDS as [row][128 B] with their 16-byte
+//     chunks XOR-swizzled by row and are read with ds_read_b128;
+//     K-major operands (A of TN, B of NN/TN) sit as [k][256 B] with chunks
+//     swizzled by k and are read with ds_read_b64_tr_b8, which transposes
+//     8 k-rows x 16 columns of bytes across a 16-lane group -- no separate
+//     transpose pass and no workspace;
+//   * 8 waves as 4 (M) x 2 (N), wave tile 64 x 128 = 4 x 8 subtiles;
+//   * v_mfma_f32_16x16x128_f8f6f4 (E4M3 x E4M3 -> fp32), one instruction per
+//     16x16 subtile per K block, issued with the B tile as the first operand
+//     so each lane owns 4 consecutive output columns of one row;
+//   * promotion acc += P * (sA * sB) on the VALU, software-pipelined one
+//     subtile column behind the MFMAs so it overlaps matrix-core work; the
+//     last column of a K block is promoted after the barrier, under the LDS
+//     reads of the next block's fragments;
+//   * XCD-aware tile order: consecutive tiles go to the same XCD (the
+//     hardware deals workgroups to the 8 XCDs round robin) and tiles are
+//     grouped along M so concurrent tiles on an XCD share A rows and B
+//     columns in that XCD's L2.
+
+#include "common.h"
+
+namespace bfp8 {
+namespace {
+
+constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int kWavesM = 4, kWavesN = 2;
+constexpr int WM = BM / kWavesM;  // 64
+constexpr int WN = BN / kWavesN;  // 128
+constexpr int TM = WM / 16;       // 4 row subtiles
+constexpr int TN = WN / 16;       // 8 column subtiles
+constexpr int kThreads = 64 * kWavesM * kWavesN;  // 512
+constexpr int kTileABytes = BM * BK;              // 32 KiB
+constexpr int kTileBBytes = BN * BK;              // 32 KiB
+constexpr int kScaleBytes = (BM + BN) * 4;        // 2 KiB
+constexpr int kStageBytes = kTileABytes + kTileBBytes + kScaleBytes;
+constexpr int kStages = 2;
+constexpr int kGroupM = 8;  // tile-order grouping along M
+constexpr int kXcds = 8;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+
+// Map the hardware block id to a (tile_m, tile_n) pair: first undo the
+// round-robin XCD dealing so each XCD owns a contiguous range of logical
+// tiles, then walk tiles in column-major groups of kGroupM rows.
+__device__ __forceinline__ void tile_coords(int bid, int nblk, int tiles_m, int tiles_n, int& tm,
+                                            int& tn) {
+  const int q = nblk / kXcds, r = nblk % kXcds;
+  const int xcd = bid % kXcds, local = bid / kXcds;
+  const int logical = xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+  const int per_group = kGroupM * tiles_n;
+  const int group = logical / per_group;
+  const int first_m = group * kGroupM;
+  const int gsize = min(tiles_m - first_m, kGroupM);
+  const int in_group = logical - group * per_group;
+  tm = first_m + in_group % gsize;
+  tn = in_group / gsize;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t cap = 0x7FFFFFFF;
+  const int n = static_cast<int>(bytes < 0 ? 0 : (bytes > cap ? cap : bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kRsrcWord3);
+}
+
+// Per-operand loader/reader.  KMAJOR == false: stored [rows][K] (K
+// contiguous); KMAJOR == true: stored [K][rows].  `rows` is M for A, N for B.
+template <bool KMAJOR>
+struct Operand {
+  const uint8_t* base;  // start of the tile's first row (K-contig) / first column (K-major)
+  int64_t ld;
+  int64_t rows_left;    // valid rows (or columns) from the tile start
+  int64_t K;
+  uint32_t voff[4];     // per-lane byte offsets of the four 1 KiB copies
+
+  __device__ __forceinline__ void init(const uint8_t* p, int64_t ld_, int64_t r0, int64_t rows,
+                                       int64_t K_, int wave, int lane) {
+    ld = ld_;
+    K = K_;
+    rows_left = rows - r0;
+    base = KMAJOR ? p + r0 : p + r0 * ld_;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (!KMAJOR) {
+        // LDS [256 rows][128 B]; copy (wave*4+j) fills rows 8(wave*4+j)..+7
+        const int row = (wave * 4 + j) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ (row & 7);
+        voff[j] = static_cast<uint32_t>(row * ld_ + c * 16);
+      } else {
+        // LDS [128 k][256 B]; copy (wave*4+j) fills k rows 4(wave*4+j)..+3
+        const int k = (wave * 4 + j) * 4 + (lane >> 4);
+        const int c = (lane & 15) ^ (k & 7);
+        voff[j] = static_cast<uint32_t>(k * ld_ + c * 16);
+      }
+    }
+  }
+
+  // Copy K block kb into the LDS tile at `dst` (wave-uniform copy bases).
+  __device__ __forceinline__ void load(int64_t kb, uint8_t* dst, int wave) const {
+    __amdgpu_buffer_rsrc_t r;
+    if (!KMAJOR) {
+      // bytes from (row 0, k = kb*128) to the end of the last valid row
+      const int64_t ext = (rows_left > 256 ? 256 : rows_left) * ld - (ld - K) - kb * BK;
+      r = make_rsrc(base + kb * BK, ext);
+    } else {
+      // whole 16-byte chunks: a ragged last column chunk is read up to the
+      // next 16-byte boundary, which the padded leading dimension covers
+      const int64_t cols = rows_left > 256 ? 256 : ((rows_left + 15) & ~int64_t(15));
+      const int64_t ext = (BK - 1) * ld + cols;
+      r = make_rsrc(base + kb * BK * ld, ext);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + (wave * 4 + j) * 1024), 16,
+                                               voff[j], 0, 0, 0);
+  }
+
+  // Fragment of 16 rows starting at tile row `r0` (multiple of 16): 32 bytes
+  // per lane, lane group g = lane/16 holding K bytes [32g, 32g+32).
+  __device__ __forceinline__ v8i frag(const uint8_t* tile, int r0, int lane) const {
+    const int g = lane >> 4, q = lane & 15;
+    if (!KMAJOR) {
+      const int row = r0 + q;
+      const uint8_t* p = tile + row * BK;
+      const uint4 lo = *reinterpret_cast<const uint4*>(p + (((2 * g) ^ (row & 7)) << 4));
+      const uint4 hi = *reinterpret_cast<const uint4*>(p + (((2 * g + 1) ^ (row & 7)) << 4));
+      return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                 (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    } else {
+      // lane q supplies half (q&1) of k row 32g + 8t + q/2; the chunk holding
+      // columns r0..r0+15 is r0/16, swizzled by k&7 == q/2.
+      const int kr = 32 * g + (q >> 1);
+      const uint8_t* p = tile + kr * 256 + (((r0 >> 4) ^ (q >> 1)) << 4) + ((q & 1) << 3);
+      const v2i t0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p));
+      const v2i t1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p + 8 * 256));
+      const v2i t2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p + 16 * 256));
+      const v2i t3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p + 24 * 256));
+      return v8i{t0.x, t0.y, t1.x, t1.y, t2.x, t2.y, t3.x, t3.y};
+    }
+  }
+};
+
+// Act-mode scale staging: 256 consecutive rows (A) or columns (B) of one K
+// block, one dword per lane, four waves per operand.  Rows past the end are
+// clamped to the last valid one (their products are never stored).
+template <bool KMAJOR>
+__device__ __forceinline__ void load_act_scales(const float* s, int64_t r0, int64_t rows,
+                                                int64_t KB, int64_t kb, uint8_t* dst, int sub,
+                                                int lane) {
+  int64_t r = sub * 64 + lane;  // relative to r0
+  if (r > rows - r0 - 1) r = rows - r0 - 1;
+  // K-contig operand: scales [rows][KB]; K-major: [KB][rows]
+  const float* base = KMAJOR ? s + kb * rows + r0 : s + r0 * KB + kb;
+  const int64_t ext = KMAJOR ? (rows - r0) * 4 : ((rows - r0) * KB - kb) * 4;
+  const uint32_t voff = static_cast<uint32_t>(KMAJOR ? r * 4 : r * KB * 4);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base, ext), (lds_void*)(dst + sub * 256), 4,
+                                           voff, 0, 0, 0);
+}
+
+template <bool A_KM, bool B_KM, int MODE_A, int MODE_B>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(2, 2))) void
+gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ sA,
+            const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ sB,
+            uint16_t* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K, int tiles_m,
+            int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % kWavesM;
+  const int wn = wave / kWavesM;
+  const int g = lane >> 4, r16 = lane & 15;
+
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = static_cast<int64_t>(tm) * BM;
+  const int64_t n0 = static_cast<int64_t>(tn) * BN;
+  const int64_t KB = K / BK;
+  const int64_t MBk = (M + 127) / 128, NBk = (N + 127) / 128;
+
+  Operand<A_KM> opa;
+  Operand<B_KM> opb;
+  opa.init(A, lda, m0, M, K, wave, lane);
+  opb.init(B, ldb, n0, N, K, wave, lane);
+
+  auto issue_loads = [&](int64_t kb, int stage) {
+    uint8_t* st = smem + stage * kStageBytes;
+    opa.load(kb, st, wave);
+    opb.load(kb, st + kTileABytes, wave);
+    uint8_t* sdst = st + kTileABytes + kTileBBytes;
+    if (MODE_A == 0 && wave < 4) load_act_scales<A_KM>(sA, m0, M, KB, kb, sdst, wave, lane);
+    if (MODE_B == 0 && wave >= 4)
+      load_act_scales<B_KM>(sB, n0, N, KB, kb, sdst + 1024, wave - 4, lane);
+  };
+
+  // block-mode scale rows (a wave's 64 rows / 128 columns sit in one block)
+  int64_t a_blk = (m0 + wm * WM) / 128, b_blk = (n0 + wn * WN) / 128;
+  if (a_blk > MBk - 1) a_blk = MBk - 1;
+  if (b_blk > NBk - 1) b_blk = NBk - 1;
+  auto block_scale_a = [&](int64_t kb) { return A_KM ? sA[kb * MBk + a_blk] : sA[a_blk * KB + kb]; };
+  auto block_scale_b = [&](int64_t kb) { return B_KM ? sB[kb * NBk + b_blk] : sB[b_blk * KB + kb]; };
+
+  // per-row multipliers of one K block: sA (act) or sA_blk, times sB_blk
+  // when B is block-scaled
+  auto row_mults = [&](const uint8_t* st, int64_t kb, float (&ra)[TM]) {
+    const float* s_lds = reinterpret_cast<const float*>(st + kTileABytes + kTileBBytes);
+    float sb = 1.0f;
+    if (MODE_B == 1) sb = block_scale_b(kb);
+    if (MODE_A == 0) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) ra[i] = s_lds[wm * WM + 16 * i + r16] * sb;
+    } else {
+      const float sa = block_scale_a(kb) * sb;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) ra[i] = sa;
+    }
+  };
+  auto col_mults = [&](const uint8_t* st, int j, float (&cb)[4]) {
+    if (MODE_B == 0) {
+      const float* s_lds = reinterpret_cast<const float*>(st + kTileABytes + kTileBBytes);
+      const float4 v = *reinterpret_cast<const float4*>(s_lds + BM + wn * WN + 16 * j + 4 * g);
+      cb[0] = v.x; cb[1] = v.y; cb[2] = v.z; cb[3] = v.w;
+    }
+  };
+
+  v4f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // Promotion of one 16x16 partial: acc += P * (row multiplier * column
+  // multiplier).  The partial of subtile (i, j) is promoted right after the
+  // MFMA of the next subtile is issued, so the VALU work of one subtile hides
+  // under the matrix-core time of the next.
+  // The empty asm pins each updated accumulator at this point of the
+  // program: without it the optimizer sinks all promotions below the K
+  // block's last MFMA, which keeps every partial live at once.
+  auto promote = [&](v4f& a, const v4f& p, float rmul, const float (&cm)[4]) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x = a[r];
+      x = fmaf(p[r], MODE_B == 0 ? rmul * cm[r] : rmul, x);
+      asm volatile("" : "+v"(x));
+      a[r] = x;
+    }
+  };
+
+  // ---- prologue -----------------------------------------------------------
+  issue_loads(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  if (KB > 1) issue_loads(1, 1);
+
+  v8i af[TM];
+  v8i bq;
+  float ra[TM];
+  {
+    const uint8_t* st = smem;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[i] = opa.frag(st, wm * WM + 16 * i, lane);
+    bq = opb.frag(st + kTileABytes, wn * WN, lane);
+    row_mults(st, 0, ra);
+  }
+
+  // Partials are promoted kLag MFMAs behind their issue (subtile order
+  // t = j*TM + i), so the VALU never waits on a result still in the matrix
+  // pipe; the last kLag partials of a K block are promoted after the barrier.
+  constexpr int kLag = 3;
+  v4f pend[kLag];
+#pragma unroll
+  for (int q = 0; q < kLag; ++q) pend[q] = v4f{0.f, 0.f, 0.f, 0.f};
+  float cm_cur[4] = {1.f, 1.f, 1.f, 1.f}, cm_prev[4] = {1.f, 1.f, 1.f, 1.f};
+  float ra_last[TM];
+
+  for (int64_t kb = 0; kb < KB; ++kb) {
+    const int stage = static_cast<int>(kb & 1);
+    const uint8_t* st = smem + stage * kStageBytes;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      v8i bn = bq;
+      if (j + 1 < TN) bn = opb.frag(st + kTileABytes, wn * WN + 16 * (j + 1), lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cm_prev[r] = cm_cur[r];
+      col_mults(st, j, cm_cur);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int t = j * TM + i;
+        const v4f pc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            bq, af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+        if (t >= kLag) {
+          const int i2 = (t - kLag) % TM, j2 = (t - kLag) / TM;
+          promote(acc[i2][j2], pend[t % kLag], ra[i2], j2 == j ? cm_cur : cm_prev);
+        }
+        pend[t % kLag] = pc;
+        // one MFMA and the promotion of the partial kLag issues back per
+        // scheduling region: the machine scheduler would otherwise pull each
+        // promotion up against the MFMA that produces it and stall on it
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      bq = bn;
+    }
+    // all MFMAs of this K block are issued; the last kLag subtiles (all in
+    // column TN-1) are pending with this block's multipliers
+#pragma unroll
+    for (int i = 0; i < TM; ++i) ra_last[i] = ra[i];
+    if (kb + 1 < KB) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's copies of block kb+1 landed
+      __syncthreads();                     // everyone's did, and stage kb is free
+      if (kb + 2 < KB) issue_loads(kb + 2, stage);
+      const uint8_t* nst = smem + (stage ^ 1) * kStageBytes;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = opa.frag(nst, wm * WM + 16 * i, lane);
+      bq = opb.frag(nst + kTileABytes, wn * WN, lane);
+      row_mults(nst, kb + 1, ra);
+    }
+#pragma unroll
+    for (int q = 0; q < kLag; ++q) {
+      const int t = TM * TN - kLag + q;
+      promote(acc[t % TM][TN - 1], pend[t % kLag], ra_last[t % TM], cm_cur);
+    }
+  }
+
+  // ---- epilogue: bf16 RNE, 4 consecutive columns (8 bytes) per store -----
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t m = m0 + wm * WM + 16 * i + r16;
+    if (m >= M) continue;
+    uint16_t* crow = C + m * ldc;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int64_t n = n0 + wn * WN + 16 * j + 4 * g;
+      const uint32_t h0 = f32_to_bf16_bits(acc[i][j][0]);
+      const uint32_t h1 = f32_to_bf16_bits(acc[i][j][1]);
+      const uint32_t h2 = f32_to_bf16_bits(acc[i][j][2]);
+      const uint32_t h3 = f32_to_bf16_bits(acc[i][j][3]);
+      if (n + 3 < N) {
+        *reinterpret_cast<uint2*>(crow + n) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+      } else {
+        const uint32_t h[4] = {h0, h1, h2, h3};
+        for (int r = 0; r < 4; ++r)
+          if (n + r < N) crow[n + r] = static_cast<uint16_t>(h[r]);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_bf16_kernel(uint16_t* __restrict__ C, int64_t M,
+                                                             int64_t N, int64_t ldc) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= M * N) return;
+  const int64_t r = i / N, c = i - r * N;
+  C[r * ldc + c] = 0;
+}
+
+inline bfp8_status last_launch_status() {
+  return hipPeekAtLastError() == hipSuccess ? BFP8_OK : BFP8_ERR_HIP;
+}
+
+}  // namespace
+
+template <bool A_KM, bool B_KM>
+static void launch_layout(const GemmArgs& a, dim3 grid, int tm, int tn, hipStream_t stream) {
+#define BFP8_LAUNCH(MA, MB)                                                              \
+  gemm_kernel<A_KM, B_KM, MA, MB><<<grid, dim3(kThreads), 0, stream>>>(                  \
+      a.A, a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K, tm, tn)
+  if (a.modeA == 0 && a.modeB == 1) BFP8_LAUNCH(0, 1);
+  else if (a.modeA == 0 && a.modeB == 0) BFP8_LAUNCH(0, 0);
+  else if (a.modeA == 1 && a.modeB == 0) BFP8_LAUNCH(1, 0);
+  else BFP8_LAUNCH(1, 1);
+#undef BFP8_LAUNCH
+}
+
+bfp8_status launch_gemm(const GemmArgs& a, hipStream_t stream) {
+  const int64_t tiles_m = (a.M + BM - 1) / BM;
+  const int64_t tiles_n = (a.N + BN - 1) / BN;
+  const int64_t nblk = tiles_m * tiles_n;
+  if (nblk == 0) return BFP8_OK;
+  const dim3 grid(static_cast<unsigned>(nblk));
+  const int tm = static_cast<int>(tiles_m), tn = static_cast<int>(tiles_n);
+  if (!a.a_kmajor && !a.b_kmajor) launch_layout<false, false>(a, grid, tm, tn, stream);
+  else if (!a.a_kmajor && a.b_kmajor) launch_layout<false, true>(a, grid, tm, tn, stream);
+  else if (a.a_kmajor && a.b_kmajor) launch_layout<true, true>(a, grid, tm, tn, stream);
+  else return BFP8_ERR_LAYOUT;
+  return last_launch_status();
+}
+
+bfp8_status launch_fill_bf16_zero(uint16_t* C, int64_t M, int64_t N, int64_t ldc,
+                                  hipStream_t stream) {
+  const int64_t n = M * N;
+  if (n == 0) return BFP8_OK;
+  fill_zero_bf16_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream>>>(
+      C, M, N, ldc);
+  return last_launch_status();
+}
+
+}  // namespace bfp8

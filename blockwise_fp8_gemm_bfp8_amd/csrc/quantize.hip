@@ -1,0 +1,292 @@
+// Blockwise E4M3 quantisers for gfx950.
+//
+// Puro-2B paper, zh-TW translation (papers.lianghsun.dev), section 3.2:
+// scales are computed online for every local group; activations and
+// activation gradients use 1-D groups of 128 consecutive values along the
+// GEMM reduction dimension, weights 128x128 2-D blocks.  Scale = amax/448 and
+// the saturating round-to-nearest-even E4M3 cast are the readings stated in
+// include/bfp8.h.
+//
+// All three kernels are HBM-bound (about 3 bytes moved per bf16 element and
+// a handful of VALU operations), so the design goal is wide coalesced loads,
+// enough bytes in flight per CU, and reductions that stay in registers
+// (DPP within 16 lanes) or in a few LDS words.
+
+#include "common.h"
+
+namespace bfp8 {
+namespace {
+
+// Eight consecutive input elements as float32.  bf16 elements are widened
+// exactly; `nvalid` (0..8) masks a ragged tail to +0.
+template <typename T>
+struct Load8;
+
+template <>
+struct Load8<uint16_t> {
+  static __device__ __forceinline__ void run(const uint16_t* p, float (&v)[8], int nvalid) {
+    if (nvalid >= 8) {
+      uint4 u = *reinterpret_cast<const uint4*>(p);
+      uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+        v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = i < nvalid ? bf16_bits_to_f32(p[i]) : 0.0f;
+    }
+  }
+};
+
+template <>
+struct Load8<float> {
+  static __device__ __forceinline__ void run(const float* p, float (&v)[8], int nvalid) {
+    if (nvalid >= 8) {
+      float4 a = reinterpret_cast<const float4*>(p)[0];
+      float4 b = reinterpret_cast<const float4*>(p)[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = i < nvalid ? p[i] : 0.0f;
+    }
+  }
+};
+
+__device__ __forceinline__ float absmax8(const float (&v)[8]) {
+  float m = fabsf(v[0]);
+#pragma unroll
+  for (int i = 1; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  return m;
+}
+
+__device__ __forceinline__ uint2 encode8(const float (&v)[8], float inv) {
+  uint2 r;
+  r.x = encode4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+  r.y = encode4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// K1: 1x128 groups along rows.  16 lanes own one group (8 elements each, one
+// 16-byte load for bf16); a 256-thread block covers 16 groups per unrolled
+// step and issues all UNROLL steps' loads before any reduction.
+// ---------------------------------------------------------------------------
+constexpr int kActUnroll = 4;
+
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_act_kernel(const T* __restrict__ x, int64_t ldx,
+                                                           uint8_t* __restrict__ q, int64_t ldq,
+                                                           float* __restrict__ s, uint32_t gpr,
+                                                           uint32_t n_groups) {
+  const uint32_t lane16 = threadIdx.x & 15u;
+  const uint32_t slot = threadIdx.x >> 4;  // 0..15: group within a step
+  const uint32_t per_block = 16u * kActUnroll;
+  for (uint32_t base = blockIdx.x * per_block; base < n_groups; base += gridDim.x * per_block) {
+    float v[kActUnroll][8];
+    uint32_t row[kActUnroll], gc[kActUnroll];
+#pragma unroll
+    for (int u = 0; u < kActUnroll; ++u) {
+      const uint32_t g = base + u * 16u + slot;
+      const bool ok = g < n_groups;
+      row[u] = ok ? g / gpr : 0u;
+      gc[u] = ok ? g - row[u] * gpr : 0u;
+      const T* p = x + static_cast<int64_t>(row[u]) * ldx + gc[u] * kGroup + lane16 * 8u;
+      Load8<T>::run(p, v[u], ok ? 8 : 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kActUnroll; ++u) {
+      const uint32_t g = base + u * 16u + slot;
+      const float amax = row16_max(absmax8(v[u]));
+      float sc, inv;
+      group_scale(amax, sc, inv);
+      if (g < n_groups) {
+        uint2 codes = encode8(v[u], inv);
+        *reinterpret_cast<uint2*>(q + static_cast<int64_t>(row[u]) * ldq + gc[u] * kGroup +
+                                  lane16 * 8u) = codes;
+        if (lane16 == 0) s[static_cast<int64_t>(row[u]) * gpr + gc[u]] = sc;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K2: token-axis groups, transposed output.  A block owns 128 tokens x 64
+// channels: coalesced row loads into an fp32 LDS tile, then thread
+// (channel c, quarter p) walks 32 tokens of its channel, the four quarters
+// combine their amax through LDS, and each thread writes its 32 codes as two
+// 16-byte stores into row c of qt.
+// ---------------------------------------------------------------------------
+constexpr int kTrTok = 128;
+constexpr int kTrCh = 64;
+constexpr int kTrLd = kTrCh + 4;  // padded fp32 row stride (16-byte aligned)
+
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_act_t_kernel(const T* __restrict__ x, int64_t ldx,
+                                                             int64_t cols, uint8_t* __restrict__ qt,
+                                                             int64_t ldqt, float* __restrict__ st,
+                                                             int64_t n_tok_blocks) {
+  __shared__ __attribute__((aligned(16))) float tile[kTrTok * kTrLd];
+  __shared__ float part[4][kTrCh];
+  const int tid = threadIdx.x;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kTrCh;
+  const int64_t tb = blockIdx.y;
+  const int64_t m0 = tb * kTrTok;
+
+  // load 128 x 64 elements: 1024 vectors of 8, four per thread
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int u = tid + 256 * j;
+    const int r = u >> 3;
+    const int cu = u & 7;
+    const int64_t c = c0 + cu * 8;
+    const int64_t left = cols - c;
+    const int nvalid = left >= 8 ? 8 : (left > 0 ? static_cast<int>(left) : 0);
+    float v[8];
+    Load8<T>::run(x + (m0 + r) * ldx + (nvalid > 0 ? c : 0), v, nvalid);
+    float4* dst = reinterpret_cast<float4*>(&tile[r * kTrLd + cu * 8]);
+    dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+    dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  __syncthreads();
+
+  const int c = tid & 63;
+  const int p = tid >> 6;
+  float v[32];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    v[i] = tile[(32 * p + i) * kTrLd + c];
+    m = fmaxf(m, fabsf(v[i]));
+  }
+  part[p][c] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(part[0][c], part[1][c]), fmaxf(part[2][c], part[3][c]));
+  float sc, inv;
+  group_scale(amax, sc, inv);
+  if (c0 + c < cols) {
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      w[i] = encode4(v[4 * i] * inv, v[4 * i + 1] * inv, v[4 * i + 2] * inv, v[4 * i + 3] * inv);
+    uint4* dst = reinterpret_cast<uint4*>(qt + (c0 + c) * ldqt + m0 + 32 * p);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    if (p == 0) st[(c0 + c) * n_tok_blocks + tb] = sc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K3: one 128x128 block per 256-thread workgroup.  Each thread keeps its 64
+// elements in registers between the block-wide amax and the encode; partial
+// edge blocks mask their missing elements to zero and store byte-wise.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_weight_kernel(const T* __restrict__ w, int64_t ldw,
+                                                              int64_t rows, int64_t cols,
+                                                              uint8_t* __restrict__ q, int64_t ldq,
+                                                              float* __restrict__ s,
+                                                              int64_t n_col_blocks) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int64_t bm = blockIdx.y, bk = blockIdx.x;
+  const int64_t r0 = bm * kGroup, k0 = bk * kGroup;
+  float v[8][8];
+  int nv[8];
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int u = tid + 256 * j;
+    const int64_t r = r0 + (u >> 4);
+    const int64_t c = k0 + (u & 15) * 8;
+    const int64_t left = cols - c;
+    int n = left >= 8 ? 8 : (left > 0 ? static_cast<int>(left) : 0);
+    if (r >= rows) n = 0;
+    nv[j] = n;
+    Load8<T>::run(w + (n > 0 ? r * ldw + c : 0), v[j], n);
+    m = fmaxf(m, absmax8(v[j]));
+  }
+  m = wave_max(m);
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float sc, inv;
+  group_scale(amax, sc, inv);
+  if (tid == 0) s[bm * n_col_blocks + bk] = sc;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int u = tid + 256 * j;
+    const int64_t r = r0 + (u >> 4);
+    const int64_t c = k0 + (u & 15) * 8;
+    if (nv[j] == 0) continue;
+    uint2 codes = encode8(v[j], inv);
+    uint8_t* dst = q + r * ldq + c;
+    if (nv[j] == 8) {
+      *reinterpret_cast<uint2*>(dst) = codes;
+    } else {
+      for (int e = 0; e < nv[j]; ++e)
+        dst[e] = static_cast<uint8_t>((e < 4 ? codes.x >> (8 * e) : codes.y >> (8 * (e - 4))) & 0xFFu);
+    }
+  }
+}
+
+inline bfp8_status last_launch_status() {
+  return hipPeekAtLastError() == hipSuccess ? BFP8_OK : BFP8_ERR_HIP;
+}
+
+}  // namespace
+
+bfp8_status launch_quantize_act(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
+                                int64_t ldx, uint8_t* q, int64_t ldq, float* s,
+                                hipStream_t stream) {
+  const int64_t gpr = cols / kGroup;
+  const int64_t n_groups = rows * gpr;
+  if (n_groups == 0) return BFP8_OK;
+  const int64_t per_block = 16 * kActUnroll;
+  int64_t blocks = (n_groups + per_block - 1) / per_block;
+  if (blocks > 16384) blocks = 16384;
+  if (dt == BFP8_IN_BF16)
+    quantize_act_kernel<uint16_t><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(
+        static_cast<const uint16_t*>(x), ldx, q, ldq, s, static_cast<uint32_t>(gpr),
+        static_cast<uint32_t>(n_groups));
+  else
+    quantize_act_kernel<float><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(
+        static_cast<const float*>(x), ldx, q, ldq, s, static_cast<uint32_t>(gpr),
+        static_cast<uint32_t>(n_groups));
+  return last_launch_status();
+}
+
+bfp8_status launch_quantize_act_transposed(const void* x, bfp8_in_dtype dt, int64_t rows,
+                                           int64_t cols, int64_t ldx, uint8_t* qt,
+                                           int64_t ldqt, float* st, hipStream_t stream) {
+  if (rows == 0 || cols == 0) return BFP8_OK;
+  const int64_t tok_blocks = rows / kTrTok;
+  dim3 grid(static_cast<unsigned>((cols + kTrCh - 1) / kTrCh), static_cast<unsigned>(tok_blocks));
+  if (dt == BFP8_IN_BF16)
+    quantize_act_t_kernel<uint16_t><<<grid, dim3(256), 0, stream>>>(
+        static_cast<const uint16_t*>(x), ldx, cols, qt, ldqt, st, tok_blocks);
+  else
+    quantize_act_t_kernel<float><<<grid, dim3(256), 0, stream>>>(
+        static_cast<const float*>(x), ldx, cols, qt, ldqt, st, tok_blocks);
+  return last_launch_status();
+}
+
+bfp8_status launch_quantize_weight(const void* w, bfp8_in_dtype dt, int64_t rows, int64_t cols,
+                                   int64_t ldw, uint8_t* q, int64_t ldq, float* s,
+                                   hipStream_t stream) {
+  if (rows == 0 || cols == 0) return BFP8_OK;
+  const int64_t rb = (rows + kGroup - 1) / kGroup;
+  const int64_t cb = (cols + kGroup - 1) / kGroup;
+  dim3 grid(static_cast<unsigned>(cb), static_cast<unsigned>(rb));
+  if (dt == BFP8_IN_BF16)
+    quantize_weight_kernel<uint16_t><<<grid, dim3(256), 0, stream>>>(
+        static_cast<const uint16_t*>(w), ldw, rows, cols, q, ldq, s, cb);
+  else
+    quantize_weight_kernel<float><<<grid, dim3(256), 0, stream>>>(
+        static_cast<const float*>(w), ldw, rows, cols, q, ldq, s, cb);
+  return last_launch_status();
+}
+
+}  // namespace bfp8

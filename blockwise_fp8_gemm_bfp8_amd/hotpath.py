@@ -1,0 +1,96 @@
+"""One training pass of the blockwise-FP8 linear layers, on preallocated buffers.
+
+For each Transformer linear y = x W^T (W stored [out][in]) the pass runs, per
+the Puro-2B paper translation (papers.lianghsun.dev), section 3.2:
+  fprop:  quantize_act(x), quantize_weight(W), gemm NT     -> y  [M][out]
+  dgrad:  quantize_act(dy), gemm NN with W's codes as stored -> dx [M][in]
+  wgrad:  quantize_act_transposed(dy), quantize_act_transposed(x),
+          gemm NT on the two token-grouped operands          -> dW [out][in]
+All buffers (codes, scales, outputs, workspaces) are allocated once, so a
+pass only enqueues kernels on the current stream.  This module only calls
+the binding; every step runs in libbfp8's kernels.
+"""
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import torch
+
+from . import gemm, quantize_act, quantize_act_transposed, quantize_weight
+
+
+@dataclass
+class LinearState:
+    name: str
+    x: torch.Tensor                      # [M][in]
+    w: torch.Tensor                      # [out][in]
+    dy: Optional[torch.Tensor] = None    # [M][out]
+    buf: Dict[str, torch.Tensor] = field(default_factory=dict)
+
+
+class HotPath:
+    """Preallocated fprop/dgrad/wgrad pass over a list of linear layers."""
+
+    def __init__(self, tensors: Dict[str, torch.Tensor], names: List[str], roles: List[str]):
+        self.roles = list(roles)
+        self.layers: List[LinearState] = []
+        for n in names:
+            L = LinearState(n, tensors["x." + n], tensors["w." + n], tensors.get("dy." + n))
+            self._alloc(L)
+            self.layers.append(L)
+        self.gemm_events = None
+
+    def _alloc(self, L: LinearState):
+        dev = L.x.device
+        M, din = L.x.shape
+        dout = L.w.shape[0]
+        u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+        b = L.buf
+        b["wq"] = torch.empty((dout, din), dtype=u8, device=dev)
+        b["ws"] = torch.empty(((dout + 127) // 128, din // 128), dtype=f32, device=dev)
+        if "fprop" in self.roles:
+            b["xq"] = torch.empty((M, din), dtype=u8, device=dev)
+            b["xs"] = torch.empty((M, din // 128), dtype=f32, device=dev)
+            b["y"] = torch.empty((M, dout), dtype=bf, device=dev)
+        if "dgrad" in self.roles:
+            b["dyq"] = torch.empty((M, dout), dtype=u8, device=dev)
+            b["dys"] = torch.empty((M, dout // 128), dtype=f32, device=dev)
+            b["dx"] = torch.empty((M, din), dtype=bf, device=dev)
+        if "wgrad" in self.roles:
+            b["dyqt"] = torch.empty((dout, M), dtype=u8, device=dev)
+            b["dyst"] = torch.empty((dout, M // 128), dtype=f32, device=dev)
+            b["xqt"] = torch.empty((din, M), dtype=u8, device=dev)
+            b["xst"] = torch.empty((din, M // 128), dtype=f32, device=dev)
+            b["dw"] = torch.empty((dout, din), dtype=bf, device=dev)
+
+    def _gemm(self, *args, **kw):
+        ev = self.gemm_events
+        if ev is not None:
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record()
+            out = gemm(*args, **kw)
+            e.record()
+            ev.append((s, e))
+            return out
+        return gemm(*args, **kw)
+
+    def run(self):
+        """Enqueue one full pass (every quantiser and GEMM) on the current stream."""
+        for L in self.layers:
+            b = L.buf
+            quantize_weight(L.w, b["wq"], b["ws"])
+            if "fprop" in self.roles:
+                quantize_act(L.x, b["xq"], b["xs"])
+                self._gemm("NT", b["xq"], b["xs"], b["wq"], b["ws"], "act", "block", out=b["y"])
+        for L in self.layers:
+            b = L.buf
+            if "dgrad" in self.roles:
+                quantize_act(L.dy, b["dyq"], b["dys"])
+                self._gemm("NN", b["dyq"], b["dys"], b["wq"], b["ws"], "act", "block",
+                           out=b["dx"])
+            if "wgrad" in self.roles:
+                quantize_act_transposed(L.dy, b["dyqt"], b["dyst"])
+                quantize_act_transposed(L.x, b["xqt"], b["xst"])
+                self._gemm("NT", b["dyqt"], b["dyst"], b["xqt"], b["xst"], "act", "act",
+                           out=b["dw"])

@@ -1,0 +1,172 @@
+/*
+ * bfp8.h -- C ABI of libbfp8: blockwise FP8 (E4M3) linear-layer kernels for
+ * AMD MI355X (gfx950).
+ *
+ * What is computed (the pages this follows):
+ *   Puro-2B paper, zh-TW translation (papers.lianghsun.dev), section 3.2
+ *   "FP8 mixed-precision training": every Transformer linear layer runs on
+ *   E4M3 operands; scales are computed online per local group; activations
+ *   and activation gradients use 1-D groups of 128 consecutive values along
+ *   the reduction dimension of the GEMM they feed; weights use 128x128 2-D
+ *   blocks (the DeepSeek-V3 fine-grained design).  Puro-2B tutorial
+ *   (bloombook.cn), FP8/MuonH section, MXFP figure: an element decodes as
+ *   code * shared scale.
+ *
+ * Readings where the pages are silent (fixed here, shared with the tests):
+ *   - E4M3 is the OCP "E4M3FN" format (bias 7, max 448, no infinities,
+ *     S.1111.111 = NaN), from FP8 Formats for Deep Learning (Micikevicius et
+ *     al., 2022), which the translation cites.
+ *   - scale s = fl32(amax / 448.0f) (IEEE float32 division); element code =
+ *     E4M3(saturate(fl32(x * fl32(448.0f / amax)))), round to nearest even,
+ *     saturating to +-448; signed zeros kept.  amax == 0 gives s = 1.0f.
+ *   - Groups with 0 < amax < 448 * 2^-126 and non-finite inputs are outside
+ *     the contract (output unspecified, no fault).
+ *   - GEMM: C[m][n] = bf16_rne( sum_kb P_kb[m][n] * sA * sB ), where P_kb is
+ *     the fp32 MFMA partial over one 128-deep K block and the sum is an fp32
+ *     accumulator ("promotion" once per 128-K block).
+ *
+ * Layout letters (a reading; all matrices are row-major in memory):
+ *   A 'N' stored [M][K] (lda >= K);   A 'T' stored [K][M] (lda >= M)
+ *   B 'N' stored [K][N] (ldb >= N);   B 'T' stored [N][K] (ldb >= K)
+ *   The three training GEMMs:
+ *     fprop  Y  = X  W^T   : NT, A = quantize_act(X) [M][in],
+ *                             B = quantize_weight(W) [out][in]
+ *     dgrad  dX = dY W     : NN, A = quantize_act(dY) [M][out],
+ *                             B = quantize_weight(W) as stored ([K=out][N=in])
+ *     wgrad  dW = dY^T X   : NT, A = quantize_act_transposed(dY) [out][M],
+ *                             B = quantize_act_transposed(X) [in][M]
+ *   TN (A stored [K][M], B stored [K][N]) is provided for callers that keep
+ *   token-grouped data in natural order.
+ *
+ * Scale tensors are dense row-major float32 arrays in the orientation of the
+ * stored operand, with the grouped axis divided by 128:
+ *   act mode (1x128 along K):  A 'N' [M][K/128]   A 'T' [K/128][M]
+ *                              B 'T' [N][K/128]   B 'N' [K/128][N]
+ *   block mode (128x128):      A 'N' [ceil(M/128)][K/128]   A 'T' [K/128][ceil(M/128)]
+ *                              B 'T' [ceil(N/128)][K/128]   B 'N' [K/128][ceil(N/128)]
+ *
+ * Ownership and threading: the caller allocates every buffer (inputs,
+ * codes, scales, outputs, workspace) in device memory.  The library keeps
+ * no state, allocates nothing, never synchronises, and enqueues all work on
+ * the given stream; calls on different streams may run concurrently.
+ *
+ * Errors: every entry point validates its arguments on the host BEFORE any
+ * HIP call and returns a bfp8_status; nothing aborts or throws.  A launch
+ * failure returns BFP8_ERR_HIP (the HIP error stays readable through
+ * hipGetLastError / hipPeekAtLastError).
+ *
+ * Preconditions common to all calls: pointers of non-empty operands are
+ * non-null and 16-byte aligned; leading dimensions are >= the row length
+ * and keep every row 16-byte aligned (multiples of 16 bytes); sizes >= 0.
+ * Empty problems (a zero extent) are valid and launch nothing, except a
+ * GEMM with K == 0 and M, N > 0, which writes C = 0.
+ */
+#ifndef BFP8_H_
+#define BFP8_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BFP8_ABI_VERSION 1
+
+typedef enum {
+  BFP8_OK = 0,
+  BFP8_ERR_NULL = 1,        /* a required pointer is NULL                  */
+  BFP8_ERR_SHAPE = 2,       /* negative size, or a grouped axis % 128 != 0 */
+  BFP8_ERR_ALIGN = 3,       /* pointer or leading dimension misaligned     */
+  BFP8_ERR_DTYPE = 4,       /* unknown input dtype                         */
+  BFP8_ERR_LAYOUT = 5,      /* unknown GEMM layout                         */
+  BFP8_ERR_SCALE_MODE = 6,  /* unknown scale mode                          */
+  BFP8_ERR_WORKSPACE = 7,   /* workspace smaller than required             */
+  BFP8_ERR_HIP = 8          /* a HIP launch failed                         */
+} bfp8_status;
+
+typedef enum { BFP8_IN_BF16 = 0, BFP8_IN_F32 = 1 } bfp8_in_dtype;
+typedef enum { BFP8_NN = 0, BFP8_NT = 1, BFP8_TN = 2 } bfp8_layout;
+typedef enum { BFP8_SCALE_1x128 = 0, BFP8_SCALE_128x128 = 1 } bfp8_scale_mode;
+
+/*
+ * Activation / activation-gradient quantiser: 1x128 groups along each row.
+ * (Puro-2B translation, section 3.2: 1-D groups of 128 consecutive values
+ * along the GEMM reduction dimension; here the reduction axis is the
+ * contiguous axis.)
+ *
+ *   x   [rows][ldx] elements of dtype dt (bf16 or fp32); cols % 128 == 0
+ *   q   [rows][ldq] uint8 E4M3 codes (ldq >= cols)
+ *   s   [rows][cols/128] float32 scales, dense
+ * rows may be any value >= 0 (no tail restriction on the token axis).
+ */
+bfp8_status bfp8_quantize_act(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
+                              int64_t ldx, uint8_t* q, int64_t ldq, float* s,
+                              hipStream_t stream);
+
+/*
+ * Token-axis quantiser for wgrad operands, written transposed.
+ * (Puro-2B translation, section 3.2: for the weight-gradient GEMM the
+ * reduction dimension is the token axis, so the 1x128 groups run along
+ * tokens.)  Bytes and scales equal bfp8_quantize_act applied to x^T.
+ *
+ *   x   [rows][ldx] (rows = tokens, rows % 128 == 0; cols = channels, any)
+ *   qt  [cols][ldqt] uint8 (ldqt >= rows): qt[c][m] is the code of x[m][c]
+ *   st  [cols][rows/128] float32: scale of tokens 128b..128b+127 of channel c
+ */
+bfp8_status bfp8_quantize_act_transposed(const void* x, bfp8_in_dtype dt, int64_t rows,
+                                         int64_t cols, int64_t ldx, uint8_t* qt,
+                                         int64_t ldqt, float* st, hipStream_t stream);
+
+/*
+ * Weight quantiser: one scale per 128x128 block.
+ * (Puro-2B translation, section 3.2; Puro-2B tutorial, FP8/MuonH section:
+ * weights are cut into 128x128 2-D blocks that share one scale.)
+ *
+ *   w   [rows][ldw] (any rows, cols >= 0; edge blocks may be partial and
+ *       take the amax of their valid elements only)
+ *   q   [rows][ldq] uint8
+ *   s   [ceil(rows/128)][ceil(cols/128)] float32, dense
+ */
+bfp8_status bfp8_quantize_weight(const void* w, bfp8_in_dtype dt, int64_t rows, int64_t cols,
+                                 int64_t ldw, uint8_t* q, int64_t ldq, float* s,
+                                 hipStream_t stream);
+
+/*
+ * Blockwise FP8 GEMM with per-128-K-block scale promotion and bf16 output.
+ * (Puro-2B translation, section 2 and section 3.2: the main Transformer
+ * linear-layer GEMMs run in blockwise FP8; non-FP8 tensors stay in BF16.)
+ *
+ *   C[m][n] (bf16, [M][ldc], ldc >= N) = sum over 128-deep K blocks of the
+ *   fp32 partial times sA * sB, accumulated in fp32, rounded to bf16 (RNE).
+ *   K % 128 == 0; M and N may have ragged tails.  modeA / modeB select the
+ *   scale layout of each operand (see the table at the top of this file).
+ *   Every stored row of A and B must be backed by a full leading dimension
+ *   of memory (lda / ldb bytes, including the last row): a K-major operand
+ *   with a ragged extent is read in whole 16-byte chunks.  lda, ldb <= 2^22.
+ *   workspace may be NULL when bfp8_gemm_workspace_bytes(...) == 0.
+ */
+bfp8_status bfp8_gemm(bfp8_layout layout, int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                      int64_t lda, const float* sA, bfp8_scale_mode modeA, const uint8_t* B,
+                      int64_t ldb, const float* sB, bfp8_scale_mode modeB, void* C,
+                      int64_t ldc, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* Workspace bytes bfp8_gemm needs for this problem (0 if none).  Returns
+ * (size_t)-1 for an invalid layout or negative size. */
+size_t bfp8_gemm_workspace_bytes(bfp8_layout layout, bfp8_scale_mode modeA,
+                                 bfp8_scale_mode modeB, int64_t M, int64_t N, int64_t K);
+
+/* Static description of a status code; never NULL. */
+const char* bfp8_status_str(bfp8_status status);
+
+/* BFP8_ABI_VERSION of the built library. */
+int bfp8_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BFP8_H_ */

@@ -1,0 +1,138 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/bfp8.h declares, and rejects bad arguments with status codes before
+any HIP call (so these run on a host without a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import blockwise_fp8_gemm_bfp8_amd as bfp8
+from blockwise_fp8_gemm_bfp8_amd import build as bfp8_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bfp8.h")
+
+OK, NULL, SHAPE, ALIGN, DTYPE, LAYOUT, SMODE, WS = range(8)
+P = 0x10000  # a 16-byte aligned fake address; never dereferenced on error paths
+
+
+@pytest.fixture(scope="session")
+def L():
+    if not os.path.exists(bfp8_build.LIB_PATH):
+        bfp8_build.build()
+    return bfp8.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:bfp8_status|size_t|const char\*|int)\s+(bfp8_\w+)\s*\(",
+                                 src, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted(["bfp8_quantize_act", "bfp8_quantize_act_transposed",
+                            "bfp8_quantize_weight", "bfp8_gemm", "bfp8_gemm_workspace_bytes",
+                            "bfp8_status_str", "bfp8_abi_version"])
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings(L):
+    assert L.bfp8_abi_version() == 1
+    for code in range(9):
+        assert len(L.bfp8_status_str(code)) > 0
+    assert L.bfp8_status_str(99) == b"unknown status"
+
+
+def qa(L, x=P, dt=0, rows=256, cols=512, ldx=512, q=P, ldq=512, s=P):
+    return L.bfp8_quantize_act(x, dt, rows, cols, ldx, q, ldq, s, None)
+
+
+def test_quantize_act_errors(L):
+    assert qa(L, x=None) == NULL
+    assert qa(L, q=None) == NULL
+    assert qa(L, s=None) == NULL
+    assert qa(L, cols=500, ldx=512) == SHAPE      # grouped axis not a multiple of 128
+    assert qa(L, rows=-1) == SHAPE
+    assert qa(L, ldx=256) == SHAPE                # ldx < cols
+    assert qa(L, ldq=256) == SHAPE
+    assert qa(L, x=P + 8) == ALIGN
+    assert qa(L, q=P + 4) == ALIGN
+    assert qa(L, ldx=516) == ALIGN                # bf16 row not 16-byte aligned
+    assert qa(L, ldq=520) == ALIGN
+    assert qa(L, dt=7) == DTYPE
+    # empty problems are valid and touch nothing, even with null pointers
+    assert qa(L, x=None, q=None, s=None, rows=0) == OK
+    assert qa(L, x=None, q=None, s=None, cols=0) == OK
+
+
+def test_quantize_transposed_errors(L):
+    f = lambda **k: L.bfp8_quantize_act_transposed(
+        k.get("x", P), k.get("dt", 0), k.get("rows", 256), k.get("cols", 384),
+        k.get("ldx", 384), k.get("q", P), k.get("ldq", 256), k.get("s", P), None)
+    assert f(rows=200) == SHAPE                   # token axis must be a multiple of 128
+    assert f(ldq=128) == SHAPE
+    assert f(x=None) == NULL
+    assert f(dt=1, ldx=385) == ALIGN
+    assert f(rows=0, x=None, q=None, s=None) == OK
+    assert f(cols=0, x=None, q=None, s=None) == OK
+
+
+def test_quantize_weight_errors(L):
+    f = lambda **k: L.bfp8_quantize_weight(
+        k.get("x", P), k.get("dt", 0), k.get("rows", 384), k.get("cols", 512),
+        k.get("ldx", 512), k.get("q", P), k.get("ldq", 512), k.get("s", P), None)
+    assert f(s=None) == NULL
+    assert f(ldx=500) == SHAPE
+    assert f(q=P + 1) == ALIGN
+    assert f(dt=-1) == DTYPE
+    assert f(rows=0, x=None, q=None, s=None) == OK
+
+
+def gemm(L, layout=1, M=256, N=384, K=512, A=P, lda=512, sA=P, ma=0, B=P, ldb=512, sB=P,
+         mb=1, C=P, ldc=384, ws=None, wsb=0):
+    return L.bfp8_gemm(layout, M, N, K, A, lda, sA, ma, B, ldb, sB, mb, C, ldc, ws, wsb, None)
+
+
+def test_gemm_errors(L):
+    assert gemm(L, layout=3) == LAYOUT
+    assert gemm(L, ma=2) == SMODE
+    assert gemm(L, mb=-1) == SMODE
+    assert gemm(L, K=500) == SHAPE
+    assert gemm(L, M=-1) == SHAPE
+    assert gemm(L, A=None) == NULL
+    assert gemm(L, sB=None) == NULL
+    assert gemm(L, C=None) == NULL
+    assert gemm(L, A=P + 4) == ALIGN
+    assert gemm(L, C=P + 2) == ALIGN
+    assert gemm(L, ldc=388) == ALIGN
+    assert gemm(L, ldc=256) == SHAPE
+    assert gemm(L, lda=256) == SHAPE              # NT: A row is K long
+    assert gemm(L, lda=520) == ALIGN
+    # NN: B stored [K][N], read in place (no workspace)
+    assert L.bfp8_gemm_workspace_bytes(0, 0, 1, 256, 384, 512) == 0
+    assert gemm(L, layout=0, ldb=256) == SHAPE    # NN: B row is N long
+    assert gemm(L, layout=2, lda=128) == SHAPE    # TN: A row is M long
+    assert gemm(L, lda=1 << 23) == SHAPE          # beyond 32-bit tile offsets
+    # empty problems
+    assert gemm(L, M=0, A=None, B=None, C=None) == OK
+    assert gemm(L, N=0, A=None, B=None, C=None) == OK
+
+
+def test_workspace_query(L):
+    for layout in (0, 1, 2):
+        assert L.bfp8_gemm_workspace_bytes(layout, 0, 1, 8192, 4096, 2048) == 0
+    assert L.bfp8_gemm_workspace_bytes(3, 0, 1, 1, 1, 128) == ctypes.c_size_t(-1).value
+    assert L.bfp8_gemm_workspace_bytes(1, 0, 1, 1, 1, 100) == ctypes.c_size_t(-1).value
+    assert L.bfp8_gemm_workspace_bytes(1, 5, 1, 1, 1, 128) == ctypes.c_size_t(-1).value
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        bfp8.lib(str(tmp_path / "missing.so"))
