@@ -133,7 +133,6 @@ def main():
     tensors = {k: v.cuda() for k, v in make_inputs(wl.name).items()}
     hp = HotPath(tensors, [L.name for L in wl.linears], wl.roles)
     flops_step = wl.flops
-    gemm_flops = [g.flops for g in wl.gemms]
     # HotPath.run launches the GEMMs in this order:
     order = [g for g in wl.gemms if g.role == "fprop"]
     for L in wl.linears:
@@ -175,7 +174,7 @@ def main():
     achieved = avg_flops / (avg_launch_ms * 1e-3) / 1e12
     traffic = load_traffic()
     roofline = {
-        "kernel": "gemm_nt_kernel (blockwise FP8 GEMM, all 12 launches of a step)",
+        "kernel": "gemm_kernel (blockwise FP8 GEMM; mean over the step's GEMM launches)",
         "bound": "mfma",
         "achieved": round(achieved, 1),
         "peak": FP8_DENSE_PEAK_TFLOPS,

@@ -47,12 +47,10 @@ constexpr int kTileABytes = BM * BK;              // 32 KiB
 constexpr int kTileBBytes = BN * BK;              // 32 KiB
 constexpr int kScaleBytes = (BM + BN) * 4;        // 2 KiB
 constexpr int kStageBytes = kTileABytes + kTileBBytes + kScaleBytes;
-constexpr int kStages = 2;
 constexpr int kGroupM = 8;  // tile-order grouping along M
 constexpr int kXcds = 8;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 
 // Map the hardware block id to a (tile_m, tile_n) pair: first undo the
@@ -72,11 +70,52 @@ __device__ __forceinline__ void tile_coords(int bid, int nblk, int tiles_m, int 
   tn = in_group / gsize;
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (wave-uniform): base address, stride 0, `bytes`
+// records (accesses at or past the end read as zero instead of faulting).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
   const int64_t cap = 0x7FFFFFFF;
   const int n = static_cast<int>(bytes < 0 ? 0 : (bytes > cap ? cap : bytes));
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kRsrcWord3);
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xFFFFFFFFu));
+  r.y = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xFFFFu));
+  r.z = __builtin_amdgcn_readfirstlane(n);
+  r.w = kRsrcWord3;
+  return r;
 }
+
+// Asynchronous buffer -> LDS copies (16 or 4 bytes per lane, the 64 lanes
+// landing contiguously at LDS byte address `lds`).  They are issued from
+// inline asm so the compiler does not treat them as stores that may alias
+// every later LDS read: it would otherwise wait for the copy into one stage
+// before reading fragments of the other.  Completion is awaited explicitly
+// (s_waitcnt vmcnt(0) before the barrier that publishes a stage).  The asm
+// has no result registers; its inputs are read when it issues.  The s_nop
+// covers the wait state an LDS-DMA load needs after an SALU write of M0.
+__device__ __forceinline__ void copy16_to_lds(uint32_t lds, uint32_t voff, i32x4 rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void copy4_to_lds(uint32_t lds, uint32_t voff, i32x4 rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// 16-byte chunk swizzle of a K-major LDS tile row k (256 B per row): the
+// low three bits spread the 8 rows one tr8 read touches over 8 chunks, the
+// fourth bit moves lane groups g and g+1 (k differs by 16) to different
+// halves of the row.
+__device__ __forceinline__ int kmajor_swizzle(int k) { return (k & 7) | (((k >> 4) & 1) << 3); }
 
 // Per-operand loader/reader.  KMAJOR == false: stored [rows][K] (K
 // contiguous); KMAJOR == true: stored [K][rows].  `rows` is M for A, N for B.
@@ -104,7 +143,7 @@ struct Operand {
       } else {
         // LDS [128 k][256 B]; copy (wave*4+j) fills k rows 4(wave*4+j)..+3
         const int k = (wave * 4 + j) * 4 + (lane >> 4);
-        const int c = (lane & 15) ^ (k & 7);
+        const int c = (lane & 15) ^ kmajor_swizzle(k);
         voff[j] = static_cast<uint32_t>(k * ld_ + c * 16);
       }
     }
@@ -112,7 +151,7 @@ struct Operand {
 
   // Copy K block kb into the LDS tile at `dst` (wave-uniform copy bases).
   __device__ __forceinline__ void load(int64_t kb, uint8_t* dst, int wave) const {
-    __amdgpu_buffer_rsrc_t r;
+    i32x4 r;
     if (!KMAJOR) {
       // bytes from (row 0, k = kb*128) to the end of the last valid row
       const int64_t ext = (rows_left > 256 ? 256 : rows_left) * ld - (ld - K) - kb * BK;
@@ -124,32 +163,46 @@ struct Operand {
       const int64_t ext = (BK - 1) * ld + cols;
       r = make_rsrc(base + kb * BK * ld, ext);
     }
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(dst) + wave * 4 * 1024);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + (wave * 4 + j) * 1024), 16,
-                                               voff[j], 0, 0, 0);
+    for (int j = 0; j < 4; ++j) copy16_to_lds(base + j * 1024, voff[j], r);
   }
 
   // Fragment of 16 rows starting at tile row `r0` (multiple of 16): 32 bytes
-  // per lane, lane group g = lane/16 holding K bytes [32g, 32g+32).
+  // per lane; lane group g = lane/16 holds K bytes [16g, 16g+16) followed by
+  // [64+16g, 64+16g+16) for both operands (any K order works as long as A
+  // and B agree).  With this split the four lane groups of one ds_read_b128
+  // touch four adjacent 16-byte chunks of their rows, which the LDS serves
+  // without bank conflicts; reading chunks 2g and 2g+1 instead halves the
+  // read rate.
   __device__ __forceinline__ v8i frag(const uint8_t* tile, int r0, int lane) const {
     const int g = lane >> 4, q = lane & 15;
     if (!KMAJOR) {
       const int row = r0 + q;
       const uint8_t* p = tile + row * BK;
-      const uint4 lo = *reinterpret_cast<const uint4*>(p + (((2 * g) ^ (row & 7)) << 4));
-      const uint4 hi = *reinterpret_cast<const uint4*>(p + (((2 * g + 1) ^ (row & 7)) << 4));
+      const uint4 lo = *reinterpret_cast<const uint4*>(p + ((g ^ (row & 7)) << 4));
+      const uint4 hi = *reinterpret_cast<const uint4*>(p + (((g + 4) ^ (row & 7)) << 4));
       return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                  (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     } else {
-      // lane q supplies half (q&1) of k row 32g + 8t + q/2; the chunk holding
-      // columns r0..r0+15 is r0/16, swizzled by k&7 == q/2.
-      const int kr = 32 * g + (q >> 1);
-      const uint8_t* p = tile + kr * 256 + (((r0 >> 4) ^ (q >> 1)) << 4) + ((q & 1) << 3);
-      const v2i t0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p));
-      const v2i t1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p + 8 * 256));
-      const v2i t2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p + 16 * 256));
-      const v2i t3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p + 24 * 256));
+      // ds_read_b64_tr_b8: within each 16-lane group, lane pair (2r, 2r+1)
+      // supplies the two 8-byte halves of one 16-byte row segment (row r of
+      // 8) and lane c receives byte c of all 8 rows.  Here the 8 rows are
+      // consecutive k and the segment holds columns r0..r0+15, so lane q gets
+      // 8 consecutive K bytes of column r0+q.  Rows read: k = 16g + 8t' + r
+      // for the first 16 bytes and 64 + 16g + 8t' + r for the last 16.
+      const int kr = 16 * g + (q >> 1);
+      const int cx = (r0 >> 4);
+      const uint8_t* p0 = tile + kr * 256 + ((q & 1) << 3);
+      const uint8_t* p1 = p0 + 8 * 256;
+      const uint8_t* p2 = p0 + 64 * 256;
+      const uint8_t* p3 = p0 + 72 * 256;
+      // all four row sets have k & 7 == q/2 and (k >> 4) & 1 == g & 1
+      const int ph = (cx ^ kmajor_swizzle(kr)) << 4;
+      const v2i t0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p0 + ph));
+      const v2i t1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p1 + ph));
+      const v2i t2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p2 + ph));
+      const v2i t3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p3 + ph));
       return v8i{t0.x, t0.y, t1.x, t1.y, t2.x, t2.y, t3.x, t3.y};
     }
   }
@@ -168,8 +221,8 @@ __device__ __forceinline__ void load_act_scales(const float* s, int64_t r0, int6
   const float* base = KMAJOR ? s + kb * rows + r0 : s + r0 * KB + kb;
   const int64_t ext = KMAJOR ? (rows - r0) * 4 : ((rows - r0) * KB - kb) * 4;
   const uint32_t voff = static_cast<uint32_t>(KMAJOR ? r * 4 : r * KB * 4);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base, ext), (lds_void*)(dst + sub * 256), 4,
-                                           voff, 0, 0, 0);
+  copy4_to_lds(__builtin_amdgcn_readfirstlane(lds_addr(dst) + sub * 256), voff,
+               make_rsrc(base, ext));
 }
 
 template <bool A_KM, bool B_KM, int MODE_A, int MODE_B>
@@ -179,7 +232,9 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
             const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ sB,
             uint16_t* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K, int tiles_m,
             int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
+  // Two pipeline stages; block kb lives in stage kb % 2.
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -200,8 +255,7 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
   opa.init(A, lda, m0, M, K, wave, lane);
   opb.init(B, ldb, n0, N, K, wave, lane);
 
-  auto issue_loads = [&](int64_t kb, int stage) {
-    uint8_t* st = smem + stage * kStageBytes;
+  auto issue_loads = [&](int64_t kb, uint8_t* st) {
     opa.load(kb, st, wave);
     opb.load(kb, st + kTileABytes, wave);
     uint8_t* sdst = st + kTileABytes + kTileBBytes;
@@ -264,21 +318,18 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
   };
 
   // ---- prologue -----------------------------------------------------------
-  issue_loads(0, 0);
+  issue_loads(0, stage0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
-  if (KB > 1) issue_loads(1, 1);
+  if (KB > 1) issue_loads(1, stage1);
 
   v8i af[TM];
   v8i bq;
   float ra[TM];
-  {
-    const uint8_t* st = smem;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) af[i] = opa.frag(st, wm * WM + 16 * i, lane);
-    bq = opb.frag(st + kTileABytes, wn * WN, lane);
-    row_mults(st, 0, ra);
-  }
+  for (int i = 0; i < TM; ++i) af[i] = opa.frag(stage0, wm * WM + 16 * i, lane);
+  bq = opb.frag(stage0 + kTileABytes, wn * WN, lane);
+  row_mults(stage0, 0, ra);
 
   // Partials are promoted kLag MFMAs behind their issue (subtile order
   // t = j*TM + i), so the VALU never waits on a result still in the matrix
@@ -290,16 +341,17 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
   float cm_cur[4] = {1.f, 1.f, 1.f, 1.f}, cm_prev[4] = {1.f, 1.f, 1.f, 1.f};
   float ra_last[TM];
 
-  for (int64_t kb = 0; kb < KB; ++kb) {
-    const int stage = static_cast<int>(kb & 1);
-    const uint8_t* st = smem + stage * kStageBytes;
+  // One K block computed from `cur`; then, once every wave is past it, the
+  // copy of block kb+2 is started into `cur` and the fragments of block
+  // kb+1 are read from `nxt`.
+  auto kblock = [&](int64_t kb, uint8_t* cur, const uint8_t* nxt) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       v8i bn = bq;
-      if (j + 1 < TN) bn = opb.frag(st + kTileABytes, wn * WN + 16 * (j + 1), lane);
+      if (j + 1 < TN) bn = opb.frag(cur + kTileABytes, wn * WN + 16 * (j + 1), lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) cm_prev[r] = cm_cur[r];
-      col_mults(st, j, cm_cur);
+      col_mults(cur, j, cm_cur);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int t = j * TM + i;
@@ -323,19 +375,23 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
     for (int i = 0; i < TM; ++i) ra_last[i] = ra[i];
     if (kb + 1 < KB) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's copies of block kb+1 landed
-      __syncthreads();                     // everyone's did, and stage kb is free
-      if (kb + 2 < KB) issue_loads(kb + 2, stage);
-      const uint8_t* nst = smem + (stage ^ 1) * kStageBytes;
+      __syncthreads();                     // everyone's did, and `cur` is free
+      if (kb + 2 < KB) issue_loads(kb + 2, cur);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = opa.frag(nst, wm * WM + 16 * i, lane);
-      bq = opb.frag(nst + kTileABytes, wn * WN, lane);
-      row_mults(nst, kb + 1, ra);
+      for (int i = 0; i < TM; ++i) af[i] = opa.frag(nxt, wm * WM + 16 * i, lane);
+      bq = opb.frag(nxt + kTileABytes, wn * WN, lane);
+      row_mults(nxt, kb + 1, ra);
     }
 #pragma unroll
     for (int q = 0; q < kLag; ++q) {
       const int t = TM * TN - kLag + q;
       promote(acc[t % TM][TN - 1], pend[t % kLag], ra_last[t % TM], cm_cur);
     }
+  };
+
+  for (int64_t kb = 0; kb < KB; kb += 2) {
+    kblock(kb, stage0, stage1);
+    if (kb + 1 < KB) kblock(kb + 1, stage1, stage0);
   }
 
   // ---- epilogue: bf16 RNE, 4 consecutive columns (8 bytes) per store -----
