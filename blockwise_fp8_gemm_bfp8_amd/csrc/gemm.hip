@@ -47,6 +47,9 @@ constexpr int kTileABytes = BM * BK;              // 32 KiB
 constexpr int kTileBBytes = BN * BK;              // 32 KiB
 constexpr int kScaleBytes = (BM + BN) * 4;        // 2 KiB
 constexpr int kStageBytes = kTileABytes + kTileBBytes + kScaleBytes;
+constexpr int kEpiRowBytes = WN * 2 + 8;            // bf16 row of a wave tile, padded
+constexpr int kEpiSlotBytes = WM * kEpiRowBytes;    // one wave's output tile
+static_assert(4 * kEpiSlotBytes <= kStageBytes, "four epilogue slots per stage");
 constexpr int kGroupM = 8;  // tile-order grouping along M
 constexpr int kXcds = 8;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
@@ -149,8 +152,9 @@ struct Operand {
     }
   }
 
-  // Copy K block kb into the LDS tile at `dst` (wave-uniform copy bases).
-  __device__ __forceinline__ void load(int64_t kb, uint8_t* dst, int wave) const {
+  // Copy 1 KiB piece j (0..3) of this wave's share of K block kb into the
+  // LDS tile at `dst`.
+  __device__ __forceinline__ void load_piece(int64_t kb, uint8_t* dst, int wave, int j) const {
     i32x4 r;
     if (!KMAJOR) {
       // bytes from (row 0, k = kb*128) to the end of the last valid row
@@ -164,8 +168,7 @@ struct Operand {
       r = make_rsrc(base + kb * BK * ld, ext);
     }
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(dst) + wave * 4 * 1024);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) copy16_to_lds(base + j * 1024, voff[j], r);
+    copy16_to_lds(base + j * 1024, voff[j], r);
   }
 
   // Fragment of 16 rows starting at tile row `r0` (multiple of 16): 32 bytes
@@ -255,13 +258,25 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
   opa.init(A, lda, m0, M, K, wave, lane);
   opb.init(B, ldb, n0, N, K, wave, lane);
 
+  // The copy of one K block is split into 9 pieces per wave (4 x 1 KiB of
+  // A, 4 x 1 KiB of B, one dword per lane of act-mode scales) so the pieces
+  // can be spread over the MFMA issue slots of the block before.
+  constexpr int kLoadPieces = 9;
+  auto issue_piece = [&](int64_t kb, uint8_t* st, int piece) {
+    if (piece < 4) {
+      opa.load_piece(kb, st, wave, piece);
+    } else if (piece < 8) {
+      opb.load_piece(kb, st + kTileABytes, wave, piece - 4);
+    } else {
+      uint8_t* sdst = st + kTileABytes + kTileBBytes;
+      if (MODE_A == 0 && wave < 4) load_act_scales<A_KM>(sA, m0, M, KB, kb, sdst, wave, lane);
+      if (MODE_B == 0 && wave >= 4)
+        load_act_scales<B_KM>(sB, n0, N, KB, kb, sdst + 1024, wave - 4, lane);
+    }
+  };
   auto issue_loads = [&](int64_t kb, uint8_t* st) {
-    opa.load(kb, st, wave);
-    opb.load(kb, st + kTileABytes, wave);
-    uint8_t* sdst = st + kTileABytes + kTileBBytes;
-    if (MODE_A == 0 && wave < 4) load_act_scales<A_KM>(sA, m0, M, KB, kb, sdst, wave, lane);
-    if (MODE_B == 0 && wave >= 4)
-      load_act_scales<B_KM>(sB, n0, N, KB, kb, sdst + 1024, wave - 4, lane);
+#pragma unroll
+    for (int p = 0; p < kLoadPieces; ++p) issue_piece(kb, st, p);
   };
 
   // block-mode scale rows (a wave's 64 rows / 128 columns sit in one block)
@@ -321,7 +336,6 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
   issue_loads(0, stage0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
-  if (KB > 1) issue_loads(1, stage1);
 
   v8i af[TM];
   v8i bq;
@@ -341,10 +355,12 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
   float cm_cur[4] = {1.f, 1.f, 1.f, 1.f}, cm_prev[4] = {1.f, 1.f, 1.f, 1.f};
   float ra_last[TM];
 
-  // One K block computed from `cur`; then, once every wave is past it, the
-  // copy of block kb+2 is started into `cur` and the fragments of block
-  // kb+1 are read from `nxt`.
-  auto kblock = [&](int64_t kb, uint8_t* cur, const uint8_t* nxt) {
+  // One K block computed from `cur` while the copy of block kb+1 into `nxt`
+  // (free since the previous barrier) is issued piecewise between the first
+  // MFMAs; then, once every wave's copies have landed, the fragments of
+  // block kb+1 are read from `nxt`.
+  auto kblock = [&](int64_t kb, const uint8_t* cur, uint8_t* nxt) {
+    const bool more = kb + 1 < KB;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       v8i bn = bq;
@@ -362,6 +378,7 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
           promote(acc[i2][j2], pend[t % kLag], ra[i2], j2 == j ? cm_cur : cm_prev);
         }
         pend[t % kLag] = pc;
+        if (t >= 1 && t <= kLoadPieces && more) issue_piece(kb + 1, nxt, t - 1);
         // one MFMA and the promotion of the partial kLag issues back per
         // scheduling region: the machine scheduler would otherwise pull each
         // promotion up against the MFMA that produces it and stall on it
@@ -373,10 +390,9 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
     // column TN-1) are pending with this block's multipliers
 #pragma unroll
     for (int i = 0; i < TM; ++i) ra_last[i] = ra[i];
-    if (kb + 1 < KB) {
+    if (more) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's copies of block kb+1 landed
       __syncthreads();                     // everyone's did, and `cur` is free
-      if (kb + 2 < KB) issue_loads(kb + 2, cur);
 #pragma unroll
       for (int i = 0; i < TM; ++i) af[i] = opa.frag(nxt, wm * WM + 16 * i, lane);
       bq = opb.frag(nxt + kTileABytes, wn * WN, lane);
@@ -394,26 +410,40 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
     if (kb + 1 < KB) kblock(kb + 1, stage1, stage0);
   }
 
-  // ---- epilogue: bf16 RNE, 4 consecutive columns (8 bytes) per store -----
+  // ---- epilogue: bf16 RNE, staged through LDS so that global stores write
+  // whole 128-byte lines: each wave parks its 64 x 128 bf16 tile in its own
+  // LDS slot (rows padded to 264 B), then 16 lanes store one 256-byte row.
+  __syncthreads();  // every wave is done reading both stages
+  uint8_t* slot = (wave < 4 ? stage0 : stage1) + (wave & 3) * kEpiSlotBytes;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int64_t m = m0 + wm * WM + 16 * i + r16;
-    if (m >= M) continue;
-    uint16_t* crow = C + m * ldc;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int64_t n = n0 + wn * WN + 16 * j + 4 * g;
       const uint32_t h0 = f32_to_bf16_bits(acc[i][j][0]);
       const uint32_t h1 = f32_to_bf16_bits(acc[i][j][1]);
       const uint32_t h2 = f32_to_bf16_bits(acc[i][j][2]);
       const uint32_t h3 = f32_to_bf16_bits(acc[i][j][3]);
-      if (n + 3 < N) {
-        *reinterpret_cast<uint2*>(crow + n) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-      } else {
-        const uint32_t h[4] = {h0, h1, h2, h3};
-        for (int r = 0; r < 4; ++r)
-          if (n + r < N) crow[n + r] = static_cast<uint16_t>(h[r]);
-      }
+      *reinterpret_cast<uint2*>(slot + (16 * i + r16) * kEpiRowBytes + (16 * j + 4 * g) * 2) =
+          make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's slot is written
+  __builtin_amdgcn_wave_barrier();
+  const int64_t mw = m0 + wm * WM, nw = n0 + wn * WN;
+#pragma unroll
+  for (int u = 0; u < WM / 4; ++u) {
+    const int row = 4 * u + (lane >> 4);
+    const int chunk = lane & 15;  // 8 bf16 columns
+    const uint4 v = *reinterpret_cast<const uint4*>(slot + row * kEpiRowBytes + chunk * 16);
+    const int64_t m = mw + row, n = nw + chunk * 8;
+    if (m >= M) continue;
+    uint16_t* dst = C + m * ldc + n;
+    if (n + 7 < N) {
+      *reinterpret_cast<uint4*>(dst) = v;
+    } else if (n < N) {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      for (int e = 0; e < 8 && n + e < N; ++e)
+        dst[e] = static_cast<uint16_t>((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
     }
   }
 }
