@@ -185,8 +185,12 @@ def gemm_workspace_bytes(layout: str, mode_a: str, mode_b: str, M: int, N: int, 
 
 
 def gemm(layout: str, qa, sa, qb, sb, mode_a: str = "act", mode_b: str = "block",
-         out: torch.Tensor = None, workspace: torch.Tensor = None):
-    """Blockwise FP8 GEMM -> bf16 [M][N]; see bfp8_gemm for layouts and scales."""
+         out: torch.Tensor = None, workspace: torch.Tensor = None, split_k: bool = True):
+    """Blockwise FP8 GEMM -> bf16 [M][N]; see bfp8_gemm for layouts and scales.
+
+    A split-K workspace is allocated when the library asks for one and none
+    (or too small a one) is passed; ``split_k=False`` passes no workspace,
+    which makes the library run the GEMM unsplit."""
     if layout not in LAYOUTS:
         raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
     M, N, K = gemm_dims(layout, qa, qb)
@@ -195,7 +199,7 @@ def gemm(layout: str, qa, sa, qb, sb, mode_a: str = "act", mode_b: str = "block"
             raise ValueError(f"{name} must be a dense float32 tensor")
     if out is None:
         out = _padded_empty(M, N, torch.bfloat16, qa.device, 8)
-    ws_bytes = gemm_workspace_bytes(layout, mode_a, mode_b, M, N, K)
+    ws_bytes = gemm_workspace_bytes(layout, mode_a, mode_b, M, N, K) if split_k else 0
     if ws_bytes and (workspace is None or workspace.numel() < ws_bytes):
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=qa.device)
     _check("bfp8_gemm", lib().bfp8_gemm(

@@ -23,11 +23,13 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 constexpr int64_t kMaxGridY = 65535;
 
-// The GEMM reads every layout in place (no transposed copies), so no
-// workspace is needed; the argument is kept in the ABI for variants that do.
-inline size_t gemm_workspace(bfp8_layout, bfp8_scale_mode, bfp8_scale_mode, int64_t, int64_t,
-                             int64_t) {
-  return 0;
+// Workspace: fp32 split-K partials for shapes whose output tiles under-fill
+// the chip (zero for all other shapes).  The GEMM runs unsplit when the
+// caller passes less.
+inline size_t gemm_workspace(bfp8_layout, bfp8_scale_mode, bfp8_scale_mode, int64_t M, int64_t N,
+                             int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return gemm_split_workspace(M, N, K);
 }
 
 // Largest leading dimension (bytes) the GEMM addresses with 32-bit offsets.
@@ -136,8 +138,7 @@ bfp8_status bfp8_gemm(bfp8_layout layout, int64_t M, int64_t N, int64_t K, const
   if (lda < a_row || ldb < b_row) return BFP8_ERR_SHAPE;
   if (lda % 16 != 0 || ldb % 16 != 0) return BFP8_ERR_ALIGN;
   if (lda > kMaxGemmLd || ldb > kMaxGemmLd) return BFP8_ERR_SHAPE;
-  const size_t need = gemm_workspace(layout, modeA, modeB, M, N, K);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return BFP8_ERR_WORKSPACE;
+  if (workspace != nullptr && !aligned16(workspace)) return BFP8_ERR_ALIGN;
 
   GemmArgs g;
   g.A = A;
@@ -155,7 +156,7 @@ bfp8_status bfp8_gemm(bfp8_layout layout, int64_t M, int64_t N, int64_t K, const
   g.M = M;
   g.N = N;
   g.K = K;
-  return launch_gemm(g, stream);
+  return launch_gemm(g, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -109,7 +109,10 @@ struct GemmArgs {
   int64_t M, N, K;
 };
 
-bfp8_status launch_gemm(const GemmArgs& a, hipStream_t stream);
+bfp8_status launch_gemm(const GemmArgs& a, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+int gemm_splits(int64_t M, int64_t N, int64_t K);
+size_t gemm_split_workspace(int64_t M, int64_t N, int64_t K);
 bfp8_status launch_fill_bf16_zero(uint16_t* C, int64_t M, int64_t N, int64_t ldc,
                                   hipStream_t stream);
 

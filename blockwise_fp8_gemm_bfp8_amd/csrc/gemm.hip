@@ -234,7 +234,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ sA,
             const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ sB,
             uint16_t* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K, int tiles_m,
-            int tiles_n) {
+            int tiles_n, float* __restrict__ part, int64_t ldp) {
   // Two pipeline stages; block kb lives in stage kb % 2.
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
@@ -252,6 +252,12 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
   const int64_t n0 = static_cast<int64_t>(tn) * BN;
   const int64_t KB = K / BK;
   const int64_t MBk = (M + 127) / 128, NBk = (N + 127) / 128;
+  // split-K: blockIdx.y selects a contiguous range of K blocks; with more
+  // than one split the fp32 tile goes to part[split] and a second kernel
+  // sums the splits in order.
+  const int splits = gridDim.y, split = blockIdx.y;  // 32-bit: KB * splits < 2^31
+  const int kb_begin = static_cast<int>((split * static_cast<int>(KB)) / splits);
+  const int kb_end = static_cast<int>(((split + 1) * static_cast<int>(KB)) / splits);
 
   Operand<A_KM> opa;
   Operand<B_KM> opb;
@@ -333,7 +339,7 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
   };
 
   // ---- prologue -----------------------------------------------------------
-  issue_loads(0, stage0);
+  issue_loads(kb_begin, stage0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 
@@ -343,7 +349,7 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
 #pragma unroll
   for (int i = 0; i < TM; ++i) af[i] = opa.frag(stage0, wm * WM + 16 * i, lane);
   bq = opb.frag(stage0 + kTileABytes, wn * WN, lane);
-  row_mults(stage0, 0, ra);
+  row_mults(stage0, kb_begin, ra);
 
   // Partials are promoted kLag MFMAs behind their issue (subtile order
   // t = j*TM + i), so the VALU never waits on a result still in the matrix
@@ -360,7 +366,7 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
   // MFMAs; then, once every wave's copies have landed, the fragments of
   // block kb+1 are read from `nxt`.
   auto kblock = [&](int64_t kb, const uint8_t* cur, uint8_t* nxt) {
-    const bool more = kb + 1 < KB;
+    const bool more = kb + 1 < kb_end;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       v8i bn = bq;
@@ -405,9 +411,29 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
     }
   };
 
-  for (int64_t kb = 0; kb < KB; kb += 2) {
+  for (int kb = kb_begin; kb < kb_end; kb += 2) {
     kblock(kb, stage0, stage1);
-    if (kb + 1 < KB) kblock(kb + 1, stage1, stage0);
+    if (kb + 1 < kb_end) kblock(kb + 1, stage1, stage0);
+  }
+
+  if (part != nullptr) {
+    // split-K partial: 4 consecutive fp32 columns per lane, 16-byte stores
+    float* pbase = part + static_cast<int64_t>(split) * M * ldp;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t m = m0 + wm * WM + 16 * i + r16;
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int64_t n = n0 + wn * WN + 16 * j + 4 * g;
+        if (n < N) {
+          float* dst = pbase + m * ldp + n;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dst[r] = acc[i][j][r];
+        }
+      }
+    }
+    return;
   }
 
   // ---- epilogue: bf16 RNE, staged through LDS so that global stores write
@@ -456,6 +482,32 @@ __global__ __launch_bounds__(256) void fill_zero_bf16_kernel(uint16_t* __restric
   C[r * ldc + c] = 0;
 }
 
+// Sum of the split-K partials in split order, rounded to bf16 (RNE).
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
+                                                            int64_t ldp, int64_t splits,
+                                                            uint16_t* __restrict__ C, int64_t ldc,
+                                                            int64_t M, int64_t N) {
+  const int64_t quads = (N + 3) / 4;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= M * quads) return;
+  const int64_t m = i / quads, n = (i - m * quads) * 4;
+  const float* p = part + m * ldp + n;
+  v4f acc = *reinterpret_cast<const v4f*>(p);
+  for (int64_t s = 1; s < splits; ++s) {
+    const v4f v = *reinterpret_cast<const v4f*>(p + s * M * ldp);
+    acc[0] += v[0]; acc[1] += v[1]; acc[2] += v[2]; acc[3] += v[3];
+  }
+  const uint32_t h0 = f32_to_bf16_bits(acc[0]), h1 = f32_to_bf16_bits(acc[1]);
+  const uint32_t h2 = f32_to_bf16_bits(acc[2]), h3 = f32_to_bf16_bits(acc[3]);
+  uint16_t* dst = C + m * ldc + n;
+  if (n + 3 < N) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+  } else {
+    const uint32_t h[4] = {h0, h1, h2, h3};
+    for (int e = 0; e < 4 && n + e < N; ++e) dst[e] = static_cast<uint16_t>(h[e]);
+  }
+}
+
 inline bfp8_status last_launch_status() {
   return hipPeekAtLastError() == hipSuccess ? BFP8_OK : BFP8_ERR_HIP;
 }
@@ -463,10 +515,11 @@ inline bfp8_status last_launch_status() {
 }  // namespace
 
 template <bool A_KM, bool B_KM>
-static void launch_layout(const GemmArgs& a, dim3 grid, int tm, int tn, hipStream_t stream) {
+static void launch_layout(const GemmArgs& a, dim3 grid, int tm, int tn, float* part,
+                          int64_t ldp, hipStream_t stream) {
 #define BFP8_LAUNCH(MA, MB)                                                              \
   gemm_kernel<A_KM, B_KM, MA, MB><<<grid, dim3(kThreads), 0, stream>>>(                  \
-      a.A, a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K, tm, tn)
+      a.A, a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K, tm, tn, part, ldp)
   if (a.modeA == 0 && a.modeB == 1) BFP8_LAUNCH(0, 1);
   else if (a.modeA == 0 && a.modeB == 0) BFP8_LAUNCH(0, 0);
   else if (a.modeA == 1 && a.modeB == 0) BFP8_LAUNCH(1, 0);
@@ -474,17 +527,66 @@ static void launch_layout(const GemmArgs& a, dim3 grid, int tm, int tn, hipStrea
 #undef BFP8_LAUNCH
 }
 
-bfp8_status launch_gemm(const GemmArgs& a, hipStream_t stream) {
+// Split-K plan for shapes whose 256x256 tiles under-fill the chip: choose
+// the split count that minimises (waves of tiles) x (K blocks per split)
+// plus the cost of moving the fp32 partials.  Splits keep >= 8 K blocks.
+static int64_t split_ldp(int64_t N) { return (N + 3) & ~int64_t(3); }
+
+int gemm_splits(int64_t M, int64_t N, int64_t K) {
+  constexpr double kCUs = 256.0;       // MI355X compute units
+  constexpr double kBlockUs = 2.4;     // one 256x256x128 step of one tile, measured order
+  constexpr double kBytesPerUs = 4.0e6;
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int64_t KB = K / BK;
+  if (tiles == 0 || KB == 0) return 1;
+  auto cost = [&](int64_t S) {
+    const double waves = static_cast<double>((tiles * S + 255) / 256);
+    double t = waves * (static_cast<double>(KB) / S) * kBlockUs;
+    if (S > 1)
+      t += (static_cast<double>(S) * M * split_ldp(N) * 8.0 + M * N * 2.0) / kBytesPerUs + 4.0;
+    return t;
+  };
+  (void)kCUs;
+  int best = 1;
+  double best_t = cost(1);
+  for (int S : {2, 3, 4, 6, 8}) {
+    if (KB / S < 8) break;
+    const double t = cost(S);
+    if (t < best_t * 0.95) {
+      best_t = t;
+      best = S;
+    }
+  }
+  return best;
+}
+
+size_t gemm_split_workspace(int64_t M, int64_t N, int64_t K) {
+  const int S = gemm_splits(M, N, K);
+  return S > 1 ? static_cast<size_t>(S) * M * split_ldp(N) * sizeof(float) : 0;
+}
+
+bfp8_status launch_gemm(const GemmArgs& a, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
   const int64_t tiles_m = (a.M + BM - 1) / BM;
   const int64_t tiles_n = (a.N + BN - 1) / BN;
   const int64_t nblk = tiles_m * tiles_n;
   if (nblk == 0) return BFP8_OK;
-  const dim3 grid(static_cast<unsigned>(nblk));
+  int S = gemm_splits(a.M, a.N, a.K);
+  if (S > 1 && (workspace == nullptr || workspace_bytes < gemm_split_workspace(a.M, a.N, a.K)))
+    S = 1;  // no room for partials: run unsplit
+  float* part = S > 1 ? static_cast<float*>(workspace) : nullptr;
+  const int64_t ldp = split_ldp(a.N);
+  const dim3 grid(static_cast<unsigned>(nblk), static_cast<unsigned>(S));
   const int tm = static_cast<int>(tiles_m), tn = static_cast<int>(tiles_n);
-  if (!a.a_kmajor && !a.b_kmajor) launch_layout<false, false>(a, grid, tm, tn, stream);
-  else if (!a.a_kmajor && a.b_kmajor) launch_layout<false, true>(a, grid, tm, tn, stream);
-  else if (a.a_kmajor && a.b_kmajor) launch_layout<true, true>(a, grid, tm, tn, stream);
+  if (!a.a_kmajor && !a.b_kmajor) launch_layout<false, false>(a, grid, tm, tn, part, ldp, stream);
+  else if (!a.a_kmajor && a.b_kmajor) launch_layout<false, true>(a, grid, tm, tn, part, ldp, stream);
+  else if (a.a_kmajor && a.b_kmajor) launch_layout<true, true>(a, grid, tm, tn, part, ldp, stream);
   else return BFP8_ERR_LAYOUT;
+  if (S > 1) {
+    const int64_t n = a.M * ((a.N + 3) / 4);
+    splitk_reduce_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream>>>(
+        part, ldp, S, a.C, a.ldc, a.M, a.N);
+  }
   return last_launch_status();
 }
 

@@ -6,7 +6,7 @@ the Puro-2B paper translation (papers.lianghsun.dev), section 3.2:
   dgrad:  quantize_act(dy), gemm NN with W's codes as stored -> dx [M][in]
   wgrad:  quantize_act_transposed(dy), quantize_act_transposed(x),
           gemm NT on the two token-grouped operands          -> dW [out][in]
-All buffers (codes, scales, outputs, workspaces) are allocated once, so a
+All buffers (codes, scales, outputs, split-K workspaces) are allocated once, so a
 pass only enqueues kernels on the current stream.  This module only calls
 the binding; every step runs in libbfp8's kernels.
 """
@@ -16,7 +16,7 @@ from typing import Dict, List, Optional
 
 import torch
 
-from . import gemm, quantize_act, quantize_act_transposed, quantize_weight
+from . import gemm, gemm_workspace_bytes, quantize_act, quantize_act_transposed, quantize_weight
 
 
 @dataclass
@@ -62,6 +62,8 @@ class HotPath:
             b["xqt"] = torch.empty((din, M), dtype=u8, device=dev)
             b["xst"] = torch.empty((din, M // 128), dtype=f32, device=dev)
             b["dw"] = torch.empty((dout, din), dtype=bf, device=dev)
+            nb = gemm_workspace_bytes("NT", "act", "act", dout, din, M)
+            b["ws_wgrad"] = torch.empty((max(nb, 16),), dtype=u8, device=dev)
 
     def _gemm(self, *args, **kw):
         ev = self.gemm_events
@@ -93,4 +95,4 @@ class HotPath:
                 quantize_act_transposed(L.dy, b["dyqt"], b["dyst"])
                 quantize_act_transposed(L.x, b["xqt"], b["xst"])
                 self._gemm("NT", b["dyqt"], b["dyst"], b["xqt"], b["xst"], "act", "act",
-                           out=b["dw"])
+                           out=b["dw"], workspace=b["ws_wgrad"])

@@ -146,7 +146,12 @@ bfp8_status bfp8_quantize_weight(const void* w, bfp8_in_dtype dt, int64_t rows, 
  *   Every stored row of A and B must be backed by a full leading dimension
  *   of memory (lda / ldb bytes, including the last row): a K-major operand
  *   with a ragged extent is read in whole 16-byte chunks.  lda, ldb <= 2^22.
- *   workspace may be NULL when bfp8_gemm_workspace_bytes(...) == 0.
+ *   workspace: device memory for fp32 split-K partials, used when the
+ *   problem's 256x256 output tiles would under-fill the GPU (size from
+ *   bfp8_gemm_workspace_bytes; 16-byte aligned).  It may be NULL or smaller
+ *   than that size: the GEMM then runs unsplit (same contract, slower).
+ *   With a split the partials are summed in a fixed order, so results are
+ *   deterministic either way.
  */
 bfp8_status bfp8_gemm(bfp8_layout layout, int64_t M, int64_t N, int64_t K, const uint8_t* A,
                       int64_t lda, const float* sA, bfp8_scale_mode modeA, const uint8_t* B,
@@ -154,8 +159,9 @@ bfp8_status bfp8_gemm(bfp8_layout layout, int64_t M, int64_t N, int64_t K, const
                       int64_t ldc, void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
-/* Workspace bytes bfp8_gemm needs for this problem (0 if none).  Returns
- * (size_t)-1 for an invalid layout or negative size. */
+/* Workspace bytes that let bfp8_gemm use its split-K plan for this problem
+ * (0 when the problem runs unsplit).  Returns (size_t)-1 for an invalid
+ * layout, scale mode or size. */
 size_t bfp8_gemm_workspace_bytes(bfp8_layout layout, bfp8_scale_mode modeA,
                                  bfp8_scale_mode modeB, int64_t M, int64_t N, int64_t K);
 

@@ -128,9 +128,16 @@ def test_gemm_errors(L):
 def test_workspace_query(L):
     for layout in (0, 1, 2):
         assert L.bfp8_gemm_workspace_bytes(layout, 0, 1, 8192, 4096, 2048) == 0
+    # few output tiles and a long K: fp32 split-K partials are requested
+    ws = L.bfp8_gemm_workspace_bytes(1, 0, 0, 2048, 2048, 16384)
+    assert ws > 0 and ws % (2048 * 2048 * 4) == 0
     assert L.bfp8_gemm_workspace_bytes(3, 0, 1, 1, 1, 128) == ctypes.c_size_t(-1).value
     assert L.bfp8_gemm_workspace_bytes(1, 0, 1, 1, 1, 100) == ctypes.c_size_t(-1).value
     assert L.bfp8_gemm_workspace_bytes(1, 5, 1, 1, 1, 128) == ctypes.c_size_t(-1).value
+
+
+def test_gemm_rejects_misaligned_workspace(L):
+    assert gemm(L, ws=P + 4, wsb=1 << 20) == ALIGN
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

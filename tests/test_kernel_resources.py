@@ -1,0 +1,50 @@
+"""Compile the GEMM for gfx950 and check the hot kernels' register use.
+
+A VGPR spill in the GEMM main loop costs ~8x (scratch traffic per MFMA); the
+kernels the training pass launches (fprop NT act x block, dgrad NN act x
+block, wgrad NT act x act) must compile without spills.  CPU only (hipcc
+cross-compiles)."""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from blockwise_fp8_gemm_bfp8_amd import build as bfp8_build
+
+HOT = {
+    "fprop NT act x block": r"gemm_kernelILb0ELb0ELi0ELi1E",
+    "dgrad NN act x block": r"gemm_kernelILb0ELb1ELi0ELi1E",
+    "wgrad NT act x act": r"gemm_kernelILb0ELb0ELi0ELi0E",
+}
+
+
+@pytest.fixture(scope="module")
+def gemm_asm(tmp_path_factory):
+    if shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("asm") / "gemm.s"
+    cmd = [bfp8_build.hipcc(), *bfp8_build.compile_flags(), "-x", "hip", "-S", "--cuda-device-only",
+           os.path.join(bfp8_build.CSRC, "gemm.hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out.read_text()
+
+
+def kernel_meta(asm, pattern):
+    meta = asm[asm.index("amdhsa.kernels:"):]
+    for blk in re.split(r"\n  - ", meta)[1:]:
+        name = re.search(r"\.name:\s+(\S+)", blk)
+        if name and re.search(pattern, name.group(1)):
+            get = lambda k: int(re.search(r"\." + k + r":\s+(\d+)", blk).group(1))
+            return {k: get(k) for k in ("vgpr_count", "vgpr_spill_count", "sgpr_spill_count",
+                                        "private_segment_fixed_size", "group_segment_fixed_size")}
+    raise AssertionError(f"kernel {pattern} not found")
+
+
+@pytest.mark.parametrize("role", list(HOT))
+def test_hot_gemm_kernels_do_not_spill(gemm_asm, role):
+    m = kernel_meta(gemm_asm, HOT[role])
+    assert m["vgpr_spill_count"] == 0, (role, m)
+    assert m["private_segment_fixed_size"] == 0, (role, m)
+    assert m["group_segment_fixed_size"] <= 160 * 1024, (role, m)

@@ -188,3 +188,25 @@ def test_matrix_core_alignment_loss():
     assert 0.0 <= got <= exact
     assert abs(got - exact) <= 2.0 ** -11 * 448.0 * 448.0
     print(f"matrix-core result {got} for exact {exact}")
+
+
+@pytest.mark.parametrize("M,N,K,modes", [(512, 256, 16384, ("act", "act")),
+                                         (300, 250, 8192, ("act", "block")),
+                                         (2048, 2048, 16384, ("act", "act"))])
+def test_split_k_matches_oracle_and_unsplit(M, N, K, modes):
+    """Shapes whose tiles under-fill the GPU take the split-K plan (fp32
+    partials summed in split order); both plans must meet the tolerance."""
+    rng = np.random.default_rng(M + N + K)
+    ma, mb = modes
+    qa, sa, qb, sb = random_operands(rng, "NT", M, N, K, ma, mb)
+    assert bfp8.gemm_workspace_bytes("NT", ma, mb, M, N, K) > 0
+    R = oracle_ref_ragged("NT", qa, sa, ma, qb, sb, mb, M, N)
+    t = dev_padded
+    args = (t(qa), dense(sa), t(qb), dense(sb), ma, mb)
+    split = bfp8.gemm("NT", *args)
+    unsplit = bfp8.gemm("NT", *args, split_k=False)
+    again = bfp8.gemm("NT", *args)
+    torch.cuda.synchronize()
+    assert oracle.rel_error(split.float().cpu().numpy(), R) <= TOL
+    assert oracle.rel_error(unsplit.float().cpu().numpy(), R) <= TOL
+    assert torch.equal(split, again)  # deterministic reduction order
