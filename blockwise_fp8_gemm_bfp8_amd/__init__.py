@@ -8,6 +8,7 @@ library is missing the first call raises -- there is no fallback path.
 Functions (same names as the C ABI in include/bfp8.h, without the prefix):
   quantize_act(x)               -> (q uint8 [R][C], s f32 [R][C/128])
   quantize_act_transposed(x)    -> (qt uint8 [C][M], st f32 [C][M/128])
+  quantize_act_dual(x)          -> (q, s, qt, st): both of the above from one read
   quantize_weight(w)            -> (q uint8 [R][C], s f32 [ceil(R/128)][ceil(C/128)])
   gemm(layout, qa, sa, qb, sb, mode_a, mode_b) -> bf16 [M][N]
 """
@@ -21,6 +22,7 @@ from .build import LIB_PATH
 
 __all__ = [
     "quantize_act",
+    "quantize_act_dual",
     "quantize_act_transposed",
     "quantize_weight",
     "gemm",
@@ -55,6 +57,7 @@ _SIGNATURES = {
     "bfp8_quantize_act": [_vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _vp],
     "bfp8_quantize_act_transposed": [_vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _vp],
     "bfp8_quantize_weight": [_vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _vp],
+    "bfp8_quantize_act_dual": [_vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp],
     "bfp8_gemm": [_int, _i64, _i64, _i64, _vp, _i64, _vp, _int, _vp, _i64, _vp, _int, _vp,
                   _i64, _vp, ctypes.c_size_t, _vp],
     "bfp8_gemm_workspace_bytes": [_int, _int, _int, _i64, _i64, _i64],
@@ -147,6 +150,25 @@ def quantize_act_transposed(x: torch.Tensor, qt: torch.Tensor = None, st: torch.
         x.data_ptr(), DTYPES[x.dtype], M, C, x.stride(0), qt.data_ptr(), qt.stride(0),
         st.data_ptr(), _stream(x)))
     return qt, st
+
+
+def quantize_act_dual(x: torch.Tensor, q=None, s=None, qt=None, st=None):
+    """Row-grouped and token-grouped (transposed) codes from one read; see
+    bfp8_quantize_act_dual.  Returns (q, s, qt, st)."""
+    _check_input(x, "x")
+    M, C = x.shape
+    if q is None:
+        q = _padded_empty(M, C, torch.uint8, x.device, 16)
+    if s is None:
+        s = torch.empty((M, max(C // 128, 0)), dtype=torch.float32, device=x.device)
+    if qt is None:
+        qt = _padded_empty(C, M, torch.uint8, x.device, 16)
+    if st is None:
+        st = torch.empty((C, max(M // 128, 0)), dtype=torch.float32, device=x.device)
+    _check("bfp8_quantize_act_dual", lib().bfp8_quantize_act_dual(
+        x.data_ptr(), DTYPES[x.dtype], M, C, x.stride(0), q.data_ptr(), q.stride(0),
+        s.data_ptr(), qt.data_ptr(), qt.stride(0), st.data_ptr(), _stream(x)))
+    return q, s, qt, st
 
 
 def quantize_weight(w: torch.Tensor, q: torch.Tensor = None, s: torch.Tensor = None):

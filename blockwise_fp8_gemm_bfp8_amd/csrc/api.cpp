@@ -91,6 +91,21 @@ bfp8_status bfp8_quantize_act_transposed(const void* x, bfp8_in_dtype dt, int64_
   return launch_quantize_act_transposed(x, dt, rows, cols, ldx, qt, ldqt, st_, stream);
 }
 
+bfp8_status bfp8_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
+                                  int64_t ldx, uint8_t* q, int64_t ldq, float* s, uint8_t* qt,
+                                  int64_t ldqt, float* st_, hipStream_t stream) {
+  if (((rows % 128 != 0 && rows > 0) || (cols % 128 != 0 && cols > 0)))
+    return valid_dtype(dt) ? BFP8_ERR_SHAPE : BFP8_ERR_DTYPE;
+  bfp8_status st = check_quant_common(x, dt, rows, cols, ldx, q, ldq, s);
+  if (st != BFP8_OK || rows == 0 || cols == 0) return st;
+  if (qt == nullptr || st_ == nullptr) return BFP8_ERR_NULL;
+  if (!aligned16(qt) || !aligned16(st_)) return BFP8_ERR_ALIGN;
+  if (ldq < cols || ldqt < rows) return BFP8_ERR_SHAPE;
+  if (ldqt % 16 != 0) return BFP8_ERR_ALIGN;
+  if (rows / 128 > kMaxGridY || cols / 128 >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+  return launch_quantize_act_dual(x, dt, rows, cols, ldx, q, ldq, s, qt, ldqt, st_, stream);
+}
+
 bfp8_status bfp8_quantize_weight(const void* w, bfp8_in_dtype dt, int64_t rows, int64_t cols,
                                  int64_t ldw, uint8_t* q, int64_t ldq, float* s,
                                  hipStream_t stream) {

@@ -86,6 +86,9 @@ bfp8_status launch_quantize_act(const void* x, bfp8_in_dtype dt, int64_t rows, i
 bfp8_status launch_quantize_act_transposed(const void* x, bfp8_in_dtype dt, int64_t rows,
                                            int64_t cols, int64_t ldx, uint8_t* qt,
                                            int64_t ldqt, float* st, hipStream_t stream);
+bfp8_status launch_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
+                                     int64_t ldx, uint8_t* q, int64_t ldq, float* s, uint8_t* qt,
+                                     int64_t ldqt, float* st, hipStream_t stream);
 bfp8_status launch_quantize_weight(const void* w, bfp8_in_dtype dt, int64_t rows, int64_t cols,
                                    int64_t ldw, uint8_t* q, int64_t ldq, float* s,
                                    hipStream_t stream);

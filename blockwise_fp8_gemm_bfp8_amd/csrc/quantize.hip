@@ -232,6 +232,115 @@ __global__ __launch_bounds__(256) void quantize_weight_kernel(const T* __restric
   }
 }
 
+// ---------------------------------------------------------------------------
+// K1+K2 fused: one read of a 128-token x 128-channel tile emits both the
+// row-grouped codes (1x128 along channels: the fprop / dgrad operand) and
+// the token-grouped codes written transposed (1x128 along tokens: the wgrad
+// operand).  Phase 1 works from registers (16 lanes per row group, as K1)
+// and parks the raw tile in LDS; phase 2 walks columns of the LDS tile (two
+// channels per thread, a quarter of the tokens each) as K2 does.  Both
+// outputs are bit-identical to the two separate quantisers.
+// ---------------------------------------------------------------------------
+template <typename T>
+struct DualTile;
+template <>
+struct DualTile<uint16_t> {
+  static constexpr int kLd = 128 + 8;  // bf16 elements per LDS row (16-byte aligned rows)
+};
+template <>
+struct DualTile<float> {
+  static constexpr int kLd = 128 + 4;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_dual_kernel(
+    const T* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+    float* __restrict__ s, uint8_t* __restrict__ qt, int64_t ldqt, float* __restrict__ st,
+    int64_t n_ch_blocks, int64_t n_tok_blocks) {
+  constexpr int kLd = DualTile<T>::kLd;
+  __shared__ __attribute__((aligned(16))) T tile[128 * kLd];
+  __shared__ float part[4][128];
+  const int tid = threadIdx.x;
+  const int64_t cb = blockIdx.x, tb = blockIdx.y;
+  const int64_t m0 = tb * 128, c0 = cb * 128;
+
+  // ---- phase 1: row groups (one per token row of the tile) -------------
+  const int lane16 = tid & 15, rsub = tid >> 4;
+  float v[8][8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int r = rsub + 16 * u;
+    Load8<T>::run(x + (m0 + r) * ldx + c0 + lane16 * 8, v[u], 8);
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int r = rsub + 16 * u;
+    const float amax = row16_max(absmax8(v[u]));
+    float sc, inv;
+    group_scale(amax, sc, inv);
+    *reinterpret_cast<uint2*>(q + (m0 + r) * ldq + c0 + lane16 * 8) = encode8(v[u], inv);
+    if (lane16 == 0) s[(m0 + r) * n_ch_blocks + cb] = sc;
+    T* dst = tile + r * kLd + lane16 * 8;
+    if (sizeof(T) == 2) {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = (__float_as_uint(v[u][2 * i]) >> 16) | (__float_as_uint(v[u][2 * i + 1]) & 0xFFFF0000u);
+      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      reinterpret_cast<float4*>(dst)[0] = make_float4(v[u][0], v[u][1], v[u][2], v[u][3]);
+      reinterpret_cast<float4*>(dst)[1] = make_float4(v[u][4], v[u][5], v[u][6], v[u][7]);
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2: token groups (one per channel), written transposed -----
+  const int cp = tid & 63, p = tid >> 6;  // channels 2cp, 2cp+1; tokens 32p..32p+31
+  float a[32], b[32];
+  float ma = 0.0f, mb = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const T* src = tile + (32 * p + i) * kLd + 2 * cp;
+    if (sizeof(T) == 2) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(src);
+      a[i] = bf16_bits_to_f32(w & 0xFFFFu);
+      b[i] = bf16_bits_to_f32(w >> 16);
+    } else {
+      const float2 w = *reinterpret_cast<const float2*>(src);
+      a[i] = w.x;
+      b[i] = w.y;
+    }
+    ma = fmaxf(ma, fabsf(a[i]));
+    mb = fmaxf(mb, fabsf(b[i]));
+  }
+  part[p][2 * cp] = ma;
+  part[p][2 * cp + 1] = mb;
+  __syncthreads();
+  const float amax_a = fmaxf(fmaxf(part[0][2 * cp], part[1][2 * cp]),
+                             fmaxf(part[2][2 * cp], part[3][2 * cp]));
+  const float amax_b = fmaxf(fmaxf(part[0][2 * cp + 1], part[1][2 * cp + 1]),
+                             fmaxf(part[2][2 * cp + 1], part[3][2 * cp + 1]));
+  float sa, inva, sb, invb;
+  group_scale(amax_a, sa, inva);
+  group_scale(amax_b, sb, invb);
+  uint32_t wa[8], wb[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    wa[i] = encode4(a[4 * i] * inva, a[4 * i + 1] * inva, a[4 * i + 2] * inva, a[4 * i + 3] * inva);
+    wb[i] = encode4(b[4 * i] * invb, b[4 * i + 1] * invb, b[4 * i + 2] * invb, b[4 * i + 3] * invb);
+  }
+  uint4* da = reinterpret_cast<uint4*>(qt + (c0 + 2 * cp) * ldqt + m0 + 32 * p);
+  uint4* db = reinterpret_cast<uint4*>(qt + (c0 + 2 * cp + 1) * ldqt + m0 + 32 * p);
+  da[0] = make_uint4(wa[0], wa[1], wa[2], wa[3]);
+  da[1] = make_uint4(wa[4], wa[5], wa[6], wa[7]);
+  db[0] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+  db[1] = make_uint4(wb[4], wb[5], wb[6], wb[7]);
+  if (p == 0) {
+    st[(c0 + 2 * cp) * n_tok_blocks + tb] = sa;
+    st[(c0 + 2 * cp + 1) * n_tok_blocks + tb] = sb;
+  }
+}
+
 inline bfp8_status last_launch_status() {
   return hipPeekAtLastError() == hipSuccess ? BFP8_OK : BFP8_ERR_HIP;
 }
@@ -270,6 +379,21 @@ bfp8_status launch_quantize_act_transposed(const void* x, bfp8_in_dtype dt, int6
   else
     quantize_act_t_kernel<float><<<grid, dim3(256), 0, stream>>>(
         static_cast<const float*>(x), ldx, cols, qt, ldqt, st, tok_blocks);
+  return last_launch_status();
+}
+
+bfp8_status launch_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
+                                     int64_t ldx, uint8_t* q, int64_t ldq, float* s, uint8_t* qt,
+                                     int64_t ldqt, float* st, hipStream_t stream) {
+  if (rows == 0 || cols == 0) return BFP8_OK;
+  const int64_t ch_blocks = cols / kGroup, tok_blocks = rows / kGroup;
+  dim3 grid(static_cast<unsigned>(ch_blocks), static_cast<unsigned>(tok_blocks));
+  if (dt == BFP8_IN_BF16)
+    quantize_dual_kernel<uint16_t><<<grid, dim3(256), 0, stream>>>(
+        static_cast<const uint16_t*>(x), ldx, q, ldq, s, qt, ldqt, st, ch_blocks, tok_blocks);
+  else
+    quantize_dual_kernel<float><<<grid, dim3(256), 0, stream>>>(
+        static_cast<const float*>(x), ldx, q, ldq, s, qt, ldqt, st, ch_blocks, tok_blocks);
   return last_launch_status();
 }
 

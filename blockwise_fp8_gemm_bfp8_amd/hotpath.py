@@ -6,6 +6,7 @@ the Puro-2B paper translation (papers.lianghsun.dev), section 3.2:
   dgrad:  quantize_act(dy), gemm NN with W's codes as stored -> dx [M][in]
   wgrad:  quantize_act_transposed(dy), quantize_act_transposed(x),
           gemm NT on the two token-grouped operands          -> dW [out][in]
+where a tensor needed in both layouts is read once (quantize_act_dual).
 All buffers (codes, scales, outputs, split-K workspaces) are allocated once, so a
 pass only enqueues kernels on the current stream.  This module only calls
 the binding; every step runs in libbfp8's kernels.
@@ -16,7 +17,8 @@ from typing import Dict, List, Optional
 
 import torch
 
-from . import gemm, gemm_workspace_bytes, quantize_act, quantize_act_transposed, quantize_weight
+from . import (gemm, gemm_workspace_bytes, quantize_act, quantize_act_dual,
+               quantize_act_transposed, quantize_weight)
 
 
 @dataclass
@@ -78,21 +80,36 @@ class HotPath:
         return gemm(*args, **kw)
 
     def run(self):
-        """Enqueue one full pass (every quantiser and GEMM) on the current stream."""
+        """Enqueue one full pass (every quantiser and GEMM) on the current stream.
+
+        When a pass has both fprop and wgrad, X is quantised once into both
+        layouts (the token-grouped codes are kept for wgrad, FP8 being the
+        activation storage format); likewise dY serves dgrad and wgrad from
+        one read."""
+        both_x = "fprop" in self.roles and "wgrad" in self.roles
+        both_dy = "dgrad" in self.roles and "wgrad" in self.roles
         for L in self.layers:
             b = L.buf
             quantize_weight(L.w, b["wq"], b["ws"])
             if "fprop" in self.roles:
-                quantize_act(L.x, b["xq"], b["xs"])
+                if both_x:
+                    quantize_act_dual(L.x, b["xq"], b["xs"], b["xqt"], b["xst"])
+                else:
+                    quantize_act(L.x, b["xq"], b["xs"])
                 self._gemm("NT", b["xq"], b["xs"], b["wq"], b["ws"], "act", "block", out=b["y"])
         for L in self.layers:
             b = L.buf
-            if "dgrad" in self.roles:
+            if both_dy:
+                quantize_act_dual(L.dy, b["dyq"], b["dys"], b["dyqt"], b["dyst"])
+            elif "dgrad" in self.roles:
                 quantize_act(L.dy, b["dyq"], b["dys"])
+            elif "wgrad" in self.roles:
+                quantize_act_transposed(L.dy, b["dyqt"], b["dyst"])
+            if "dgrad" in self.roles:
                 self._gemm("NN", b["dyq"], b["dys"], b["wq"], b["ws"], "act", "block",
                            out=b["dx"])
             if "wgrad" in self.roles:
-                quantize_act_transposed(L.dy, b["dyqt"], b["dyst"])
-                quantize_act_transposed(L.x, b["xqt"], b["xst"])
+                if not both_x:
+                    quantize_act_transposed(L.x, b["xqt"], b["xst"])
                 self._gemm("NT", b["dyqt"], b["dyst"], b["xqt"], b["xst"], "act", "act",
                            out=b["dw"], workspace=b["ws_wgrad"])

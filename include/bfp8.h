@@ -121,6 +121,22 @@ bfp8_status bfp8_quantize_act_transposed(const void* x, bfp8_in_dtype dt, int64_
                                          int64_t ldqt, float* st, hipStream_t stream);
 
 /*
+ * Both activation layouts from one read: the row-grouped codes of
+ * bfp8_quantize_act AND the token-grouped transposed codes of
+ * bfp8_quantize_act_transposed, bit-identical to calling the two.
+ * (Puro-2B translation, section 3.2: FP8 is the online compute and
+ * activation-storage format -- the fprop quantisation of X keeps the codes
+ * the wgrad GEMM needs, and one pass over dY serves both dgrad and wgrad.)
+ *
+ *   x   [rows][ldx] (rows = tokens, cols = channels; both % 128 == 0)
+ *   q   [rows][ldq] uint8,  s  [rows][cols/128] float32   (as quantize_act)
+ *   qt  [cols][ldqt] uint8, st [cols][rows/128] float32   (as quantize_act_transposed)
+ */
+bfp8_status bfp8_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
+                                   int64_t ldx, uint8_t* q, int64_t ldq, float* s, uint8_t* qt,
+                                   int64_t ldqt, float* st, hipStream_t stream);
+
+/*
  * Weight quantiser: one scale per 128x128 block.
  * (Puro-2B translation, section 3.2; Puro-2B tutorial, FP8/MuonH section:
  * weights are cut into 128x128 2-D blocks that share one scale.)

@@ -34,6 +34,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["bfp8_quantize_act", "bfp8_quantize_act_transposed",
+                            "bfp8_quantize_act_dual",
                             "bfp8_quantize_weight", "bfp8_gemm", "bfp8_gemm_workspace_bytes",
                             "bfp8_status_str", "bfp8_abi_version"])
 
@@ -82,6 +83,22 @@ def test_quantize_transposed_errors(L):
     assert f(dt=1, ldx=385) == ALIGN
     assert f(rows=0, x=None, q=None, s=None) == OK
     assert f(cols=0, x=None, q=None, s=None) == OK
+
+
+def test_quantize_dual_errors(L):
+    f = lambda **k: L.bfp8_quantize_act_dual(
+        k.get("x", P), k.get("dt", 0), k.get("rows", 256), k.get("cols", 384), k.get("ldx", 384),
+        k.get("q", P), k.get("ldq", 384), k.get("s", P), k.get("qt", P), k.get("ldqt", 256),
+        k.get("st", P), None)
+    assert f(rows=200) == SHAPE                   # both axes are grouped
+    assert f(cols=200, ldx=208, ldq=208) == SHAPE
+    assert f(qt=None) == NULL
+    assert f(st=None) == NULL
+    assert f(qt=P + 8) == ALIGN
+    assert f(ldqt=200) == SHAPE
+    assert f(ldqt=264) == ALIGN
+    assert f(dt=3) == DTYPE
+    assert f(rows=0, x=None, q=None, s=None, qt=None, st=None) == OK
 
 
 def test_quantize_weight_errors(L):

@@ -156,6 +156,34 @@ def test_transposed_equals_act_of_transpose_on_gpu():
     assert torch.equal(qt, q2) and torch.equal(st.view(torch.int32), s2.view(torch.int32))
 
 
+# ---------------------------------------------------------------- dual
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("rows,cols", [(128, 128), (384, 256), (1024, 2048), (8192, 384)])
+def test_quantize_act_dual_equals_both_quantisers(dtype, rows, cols):
+    g = torch.Generator().manual_seed(rows * 3 + cols)
+    x = (torch.randn((rows, cols), generator=g) * 2).to(dtype)
+    x[:, cols // 3] = 0
+    x[rows // 2, :] = 0
+    q, s_, qt, st = bfp8.quantize_act_dual(dev(x))
+    eq, es = oracle.quantize_act(to_numpy_input(x))
+    assert_same_codes(q, s_, eq, es, f"dual rows {rows}x{cols} {dtype}")
+    eqt, est = oracle.quantize_act_transposed(to_numpy_input(x))
+    assert_same_codes(qt, st, eqt, est, f"dual cols {rows}x{cols} {dtype}")
+
+
+def test_quantize_act_dual_adversarial():
+    base = adversarial_groups()  # 12 x 128 rows of corner cases
+    x = np.concatenate([base] * 11)[:128]
+    x = np.concatenate([x, x.T.copy()], axis=1)  # corner cases along both axes
+    q, s_, qt, st = bfp8.quantize_act_dual(torch.from_numpy(np.ascontiguousarray(x)).cuda())
+    eq, es = oracle.quantize_act(x)
+    eqt, est = oracle.quantize_act_transposed(x)
+    assert_same_codes(q, s_, eq, es, "dual adversarial rows")
+    assert_same_codes(qt, st, eqt, est, "dual adversarial cols")
+
+
 # ---------------------------------------------------------------- weight
 
 
