@@ -152,23 +152,28 @@ struct Operand {
     }
   }
 
-  // Copy 1 KiB piece j (0..3) of this wave's share of K block kb into the
-  // LDS tile at `dst`.
-  __device__ __forceinline__ void load_piece(int64_t kb, uint8_t* dst, int wave, int j) const {
-    i32x4 r;
+  // Buffer descriptor of K block kb: its first byte and the extent the
+  // copies of that block may touch.  Computed once per K block; the four
+  // copies of a wave then only differ in their LDS destination.
+  __device__ __forceinline__ i32x4 block_rsrc(int64_t kb) const {
     if (!KMAJOR) {
       // bytes from (row 0, k = kb*128) to the end of the last valid row
       const int64_t ext = (rows_left > 256 ? 256 : rows_left) * ld - (ld - K) - kb * BK;
-      r = make_rsrc(base + kb * BK, ext);
+      return make_rsrc(base + kb * BK, ext);
     } else {
       // whole 16-byte chunks: a ragged last column chunk is read up to the
       // next 16-byte boundary, which the padded leading dimension covers
       const int64_t cols = rows_left > 256 ? 256 : ((rows_left + 15) & ~int64_t(15));
       const int64_t ext = (BK - 1) * ld + cols;
-      r = make_rsrc(base + kb * BK * ld, ext);
+      return make_rsrc(base + kb * BK * ld, ext);
     }
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(dst) + wave * 4 * 1024);
-    copy16_to_lds(base + j * 1024, voff[j], r);
+  }
+
+  // Copy 1 KiB piece j (0..3) of this wave's share of the K block described
+  // by `r` into the LDS tile at `dst`.
+  __device__ __forceinline__ void load_piece(const i32x4& r, uint8_t* dst, int wave, int j) const {
+    const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_addr(dst) + wave * 4 * 1024);
+    copy16_to_lds(lbase + j * 1024, voff[j], r);
   }
 
   // Fragment of 16 rows starting at tile row `r0` (multiple of 16): 32 bytes
@@ -228,6 +233,20 @@ __device__ __forceinline__ void load_act_scales(const float* s, int64_t r0, int6
                make_rsrc(base, ext));
 }
 
+// Block-mode scale staging: the scales of the two 128-blocks a 256-row
+// (A) or 256-column (B) tile spans, for one K block, copied to LDS words 0
+// and 1 (the other lanes repeat block 0).  Blocks past the end are clamped.
+template <bool KMAJOR>
+__device__ __forceinline__ void load_block_scales(const float* s, int64_t r0, int64_t nblk,
+                                                  int64_t KB, int64_t kb, uint8_t* dst, int lane) {
+  int64_t blk = r0 / 128 + (lane < 2 ? lane : 0);
+  if (blk > nblk - 1) blk = nblk - 1;
+  // K-contig operand: scales [nblk][KB]; K-major: [KB][nblk]
+  const int64_t idx = KMAJOR ? kb * nblk + blk : blk * KB + kb;
+  copy4_to_lds(__builtin_amdgcn_readfirstlane(lds_addr(dst)), static_cast<uint32_t>(idx * 4),
+               make_rsrc(s, nblk * KB * 4));
+}
+
 template <bool A_KM, bool B_KM, int MODE_A, int MODE_B>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(2, 2))) void
@@ -268,41 +287,41 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
   // A, 4 x 1 KiB of B, one dword per lane of act-mode scales) so the pieces
   // can be spread over the MFMA issue slots of the block before.
   constexpr int kLoadPieces = 9;
+  i32x4 rsrc_a, rsrc_b;  // descriptors of the K block being copied
   auto issue_piece = [&](int64_t kb, uint8_t* st, int piece) {
     if (piece < 4) {
-      opa.load_piece(kb, st, wave, piece);
+      opa.load_piece(rsrc_a, st, wave, piece);
     } else if (piece < 8) {
-      opb.load_piece(kb, st + kTileABytes, wave, piece - 4);
+      opb.load_piece(rsrc_b, st + kTileABytes, wave, piece - 4);
     } else {
       uint8_t* sdst = st + kTileABytes + kTileBBytes;
-      if (MODE_A == 0 && wave < 4) load_act_scales<A_KM>(sA, m0, M, KB, kb, sdst, wave, lane);
-      if (MODE_B == 0 && wave >= 4)
-        load_act_scales<B_KM>(sB, n0, N, KB, kb, sdst + 1024, wave - 4, lane);
+      if (wave < 4) {
+        if (MODE_A == 0) load_act_scales<A_KM>(sA, m0, M, KB, kb, sdst, wave, lane);
+        else if (wave == 0) load_block_scales<A_KM>(sA, m0, MBk, KB, kb, sdst, lane);
+      } else {
+        if (MODE_B == 0) load_act_scales<B_KM>(sB, n0, N, KB, kb, sdst + 1024, wave - 4, lane);
+        else if (wave == 4) load_block_scales<B_KM>(sB, n0, NBk, KB, kb, sdst + 1024, lane);
+      }
     }
   };
   auto issue_loads = [&](int64_t kb, uint8_t* st) {
+    rsrc_a = opa.block_rsrc(kb);
+    rsrc_b = opb.block_rsrc(kb);
 #pragma unroll
     for (int p = 0; p < kLoadPieces; ++p) issue_piece(kb, st, p);
   };
 
-  // block-mode scale rows (a wave's 64 rows / 128 columns sit in one block)
-  int64_t a_blk = (m0 + wm * WM) / 128, b_blk = (n0 + wn * WN) / 128;
-  if (a_blk > MBk - 1) a_blk = MBk - 1;
-  if (b_blk > NBk - 1) b_blk = NBk - 1;
-  auto block_scale_a = [&](int64_t kb) { return A_KM ? sA[kb * MBk + a_blk] : sA[a_blk * KB + kb]; };
-  auto block_scale_b = [&](int64_t kb) { return B_KM ? sB[kb * NBk + b_blk] : sB[b_blk * KB + kb]; };
-
   // per-row multipliers of one K block: sA (act) or sA_blk, times sB_blk
-  // when B is block-scaled
-  auto row_mults = [&](const uint8_t* st, int64_t kb, float (&ra)[TM]) {
+  // (a wave's 64 rows / 128 columns sit in one 128-block); every scale
+  // comes from the K block's LDS stage, copied with its codes
+  auto row_mults = [&](const uint8_t* st, float (&ra)[TM]) {
     const float* s_lds = reinterpret_cast<const float*>(st + kTileABytes + kTileBBytes);
-    float sb = 1.0f;
-    if (MODE_B == 1) sb = block_scale_b(kb);
+    const float sb = MODE_B == 1 ? s_lds[BM + wn] : 1.0f;
     if (MODE_A == 0) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) ra[i] = s_lds[wm * WM + 16 * i + r16] * sb;
     } else {
-      const float sa = block_scale_a(kb) * sb;
+      const float sa = s_lds[(wm * WM) / 128] * sb;
 #pragma unroll
       for (int i = 0; i < TM; ++i) ra[i] = sa;
     }
@@ -349,7 +368,7 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
 #pragma unroll
   for (int i = 0; i < TM; ++i) af[i] = opa.frag(stage0, wm * WM + 16 * i, lane);
   bq = opb.frag(stage0 + kTileABytes, wn * WN, lane);
-  row_mults(stage0, kb_begin, ra);
+  row_mults(stage0, ra);
 
   // Partials are promoted kLag MFMAs behind their issue (subtile order
   // t = j*TM + i), so the VALU never waits on a result still in the matrix
@@ -367,6 +386,17 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
   // block kb+1 are read from `nxt`.
   auto kblock = [&](int64_t kb, const uint8_t* cur, uint8_t* nxt) {
     const bool more = kb + 1 < kb_end;
+    // The copies are issued unconditionally (no branch per piece): after the
+    // last block they read nothing (an empty descriptor makes every access
+    // out of range, which lands zeros in the idle stage) and the scale copies
+    // repeat this block's scales.
+    const int64_t kn = more ? kb + 1 : kb;
+    rsrc_a = opa.block_rsrc(kn);
+    rsrc_b = opb.block_rsrc(kn);
+    if (!more) {
+      rsrc_a.z = 0;
+      rsrc_b.z = 0;
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       v8i bn = bq;
@@ -384,7 +414,7 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
           promote(acc[i2][j2], pend[t % kLag], ra[i2], j2 == j ? cm_cur : cm_prev);
         }
         pend[t % kLag] = pc;
-        if (t >= 1 && t <= kLoadPieces && more) issue_piece(kb + 1, nxt, t - 1);
+        if (t >= 1 && t <= kLoadPieces) issue_piece(kn, nxt, t - 1);
         // one MFMA and the promotion of the partial kLag issues back per
         // scheduling region: the machine scheduler would otherwise pull each
         // promotion up against the MFMA that produces it and stall on it
@@ -402,7 +432,7 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
 #pragma unroll
       for (int i = 0; i < TM; ++i) af[i] = opa.frag(nxt, wm * WM + 16 * i, lane);
       bq = opb.frag(nxt + kTileABytes, wn * WN, lane);
-      row_mults(nxt, kb + 1, ra);
+      row_mults(nxt, ra);
     }
 #pragma unroll
     for (int q = 0; q < kLag; ++q) {
@@ -416,6 +446,9 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
     if (kb + 1 < kb_end) kblock(kb + 1, stage1, stage0);
   }
 
+  // the copies issued during the last block must land before the stages
+  // are reused for the output
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   if (part != nullptr) {
     // split-K partial: 4 consecutive fp32 columns per lane, 16-byte stores
     float* pbase = part + static_cast<int64_t>(split) * M * ldp;
