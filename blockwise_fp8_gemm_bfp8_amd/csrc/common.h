@@ -20,11 +20,12 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
   return __uint_as_float(b16 << 16);
 }
 
-// float32 -> bfloat16 bits, round to nearest even (inputs are finite here).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two float32 -> packed bfloat16 pair (low half = a), round to nearest
+// even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float f2_ __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf2_ __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_{a, b}), bf2_));
 }
 
 // Group scale and its reciprocal multiplier.  s = fl32(amax / 448) and

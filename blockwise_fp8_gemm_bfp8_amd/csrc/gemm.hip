@@ -55,6 +55,8 @@ constexpr int kXcds = 8;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
 typedef __attribute__((address_space(3))) v2i lds_v2i;
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 // Map the hardware block id to a (tile_m, tile_n) pair: first undo the
 // round-robin XCD dealing so each XCD owns a contiguous range of logical
@@ -472,18 +474,18 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
   // ---- epilogue: bf16 RNE, staged through LDS so that global stores write
   // whole 128-byte lines: each wave parks its 64 x 128 bf16 tile in its own
   // LDS slot (rows padded to 264 B), then 16 lanes store one 256-byte row.
+  // The stores are non-temporal: the output is not read again by this
+  // kernel, and keeping it out of L2 leaves the operand tiles other
+  // workgroups still stream there.
   __syncthreads();  // every wave is done reading both stages
   uint8_t* slot = (wave < 4 ? stage0 : stage1) + (wave & 3) * kEpiSlotBytes;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const uint32_t h0 = f32_to_bf16_bits(acc[i][j][0]);
-      const uint32_t h1 = f32_to_bf16_bits(acc[i][j][1]);
-      const uint32_t h2 = f32_to_bf16_bits(acc[i][j][2]);
-      const uint32_t h3 = f32_to_bf16_bits(acc[i][j][3]);
       *reinterpret_cast<uint2*>(slot + (16 * i + r16) * kEpiRowBytes + (16 * j + 4 * g) * 2) =
-          make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+          make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]),
+                     pack_bf16x2(acc[i][j][2], acc[i][j][3]));
     }
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's slot is written
@@ -498,7 +500,7 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
     if (m >= M) continue;
     uint16_t* dst = C + m * ldc + n;
     if (n + 7 < N) {
-      *reinterpret_cast<uint4*>(dst) = v;
+      __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(dst));
     } else if (n < N) {
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
       for (int e = 0; e < 8 && n + e < N; ++e)
@@ -530,13 +532,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     const v4f v = *reinterpret_cast<const v4f*>(p + s * M * ldp);
     acc[0] += v[0]; acc[1] += v[1]; acc[2] += v[2]; acc[3] += v[3];
   }
-  const uint32_t h0 = f32_to_bf16_bits(acc[0]), h1 = f32_to_bf16_bits(acc[1]);
-  const uint32_t h2 = f32_to_bf16_bits(acc[2]), h3 = f32_to_bf16_bits(acc[3]);
+  const uint32_t w0 = pack_bf16x2(acc[0], acc[1]), w1 = pack_bf16x2(acc[2], acc[3]);
   uint16_t* dst = C + m * ldc + n;
   if (n + 3 < N) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+    __builtin_nontemporal_store(v2u{w0, w1}, reinterpret_cast<v2u*>(dst));
   } else {
-    const uint32_t h[4] = {h0, h1, h2, h3};
+    const uint32_t h[4] = {w0 & 0xFFFFu, w0 >> 16, w1 & 0xFFFFu, w1 >> 16};
     for (int e = 0; e < 4 && n + e < N; ++e) dst[e] = static_cast<uint16_t>(h[e]);
   }
 }
