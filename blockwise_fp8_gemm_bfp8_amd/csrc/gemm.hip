@@ -454,6 +454,15 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
   if (part != nullptr) {
     // split-K partial: 4 consecutive fp32 columns per lane, 16-byte stores
     float* pbase = part + static_cast<int64_t>(split) * M * ldp;
+    if (m0 + wm * WM + WM <= M && n0 + wn * WN + WN <= N) {
+      float* dst = pbase + (m0 + wm * WM + r16) * ldp + n0 + wn * WN + 4 * g;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          *reinterpret_cast<v4f*>(dst + 16 * i * ldp + 16 * j) = acc[i][j];
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int64_t m = m0 + wm * WM + 16 * i + r16;
@@ -491,10 +500,24 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's slot is written
   __builtin_amdgcn_wave_barrier();
   const int64_t mw = m0 + wm * WM, nw = n0 + wn * WN;
+  const int chunk = lane & 15;  // 8 bf16 columns
+  if (mw + WM <= M && nw + WN <= N) {
+    // whole wave tile inside C: all row reads first, then the stores, with
+    // no per-row tests (a read-then-test loop waits out the LDS latency
+    // once per row)
+    v4u v[WM / 4];
+#pragma unroll
+    for (int u = 0; u < WM / 4; ++u)
+      v[u] = *reinterpret_cast<const v4u*>(slot + (4 * u + (lane >> 4)) * kEpiRowBytes + chunk * 16);
+    uint16_t* dst = C + (mw + (lane >> 4)) * ldc + nw + chunk * 8;
+#pragma unroll
+    for (int u = 0; u < WM / 4; ++u)
+      __builtin_nontemporal_store(v[u], reinterpret_cast<v4u*>(dst + 4 * u * ldc));
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < WM / 4; ++u) {
     const int row = 4 * u + (lane >> 4);
-    const int chunk = lane & 15;  // 8 bf16 columns
     const uint4 v = *reinterpret_cast<const uint4*>(slot + row * kEpiRowBytes + chunk * 16);
     const int64_t m = mw + row, n = nw + chunk * 8;
     if (m >= M) continue;
