@@ -19,6 +19,11 @@ What it computes follows these passages:
   translation's reference list), E4M3 definition: bias 7, no infinities,
   S.1111.111 is NaN, largest finite 448.
 
+* Puro-2B translation, section 3.2, again: on SM120 every logical block
+  scale was a power of two on the native MXFP8 path (``mx.py``: E8M0 scales,
+  1x128 / 128x128 groups and the MXFP8 1x32 groups of the tutorial's MXFP
+  figure).
+
 Readings where the pages are silent (each also listed in the design doc):
 scale = fl32(amax / 448); element map fl32(x * fl32(448 / amax)); saturating
 round-to-nearest-even; an all-zero group gets scale 1.0; signed zeros are
@@ -39,6 +44,17 @@ from .quant import (
     GROUP,
 )
 from .gemm import dequantize_operand, gemm_ref, normwise_error, rel_error
+from .mx import (
+    E8M0_BIAS,
+    dequantize_mx_operand,
+    e8m0_decode,
+    gemm_mx_ref,
+    pow2_exponent,
+    quantize_mx_act,
+    quantize_mx_act_transposed,
+    quantize_mx_group,
+    quantize_mx_weight,
+)
 
 __all__ = [
     "e4m3_decode",
@@ -53,4 +69,13 @@ __all__ = [
     "gemm_ref",
     "rel_error",
     "normwise_error",
+    "E8M0_BIAS",
+    "pow2_exponent",
+    "e8m0_decode",
+    "quantize_mx_group",
+    "quantize_mx_act",
+    "quantize_mx_act_transposed",
+    "quantize_mx_weight",
+    "dequantize_mx_operand",
+    "gemm_mx_ref",
 ]

@@ -138,3 +138,92 @@ def test_gemm_wrong_operand_orientation_is_caught():
     # reading the NN operand as if it were NT (B stored [N][K]) is a transpose bug
     wrong = gemm_ref("NT", qa, sa, "act", qb, np.ascontiguousarray(sb.T), "block")
     assert not (wrong == E).all()
+
+
+# ---- power-of-two (E8M0) mutants -------------------------------------------
+
+import pins_mx  # noqa: E402
+from oracle import pow2_exponent, quantize_group, quantize_mx_act  # noqa: E402
+
+
+def exp_floor(a):
+    """floor(log2(amax/448)) instead of rounding up: the OCP MX default."""
+    a = np.asarray(a, np.float64)
+    e = np.where(a == 0, 0, np.floor(np.log2(np.where(a == 0, 1, a) / 448.0)))
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def exp_no_clamp_high(a):
+    """Rounds to the nearest power instead of up (log2 rounded half-up)."""
+    a = np.asarray(a, np.float64)
+    e = np.where(a == 0, 0, np.round(np.log2(np.where(a == 0, 1, a) / 448.0)))
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+@pytest.mark.parametrize("mutant", [exp_floor, exp_no_clamp_high])
+def test_pow2_exponent_mutants_are_caught(mutant):
+    assert _fails(pins_mx.check_pow2_exponent, mutant, np.random.default_rng(0))
+
+
+def _mx_group(x, exp_fn=pow2_exponent, bias=127, saturate_ok=True):
+    x = np.asarray(x, np.float32)
+    amax = np.float32(np.max(np.abs(x)))
+    e = int(exp_fn(np.array([amax], np.float32))[0])
+    y = (x.astype(np.float64) * 2.0 ** -e).astype(np.float32)
+    return e4m3_encode(y), np.uint8(e + bias)
+
+
+def mxq_floor_exponent(x):
+    return _mx_group(x, exp_fn=exp_floor)
+
+
+def mxq_bias_128(x):
+    return _mx_group(x, bias=128)
+
+
+def mxq_fp32_rule(x):
+    """Uses the fp32 amax/448 scale but reports its rounded-up exponent."""
+    q, s = quantize_group(x)
+    e = int(pow2_exponent(np.array([np.max(np.abs(np.asarray(x, np.float32)))], np.float32))[0])
+    return q, np.uint8(e + 127)
+
+
+@pytest.mark.parametrize("mutant", [mxq_floor_exponent, mxq_bias_128, mxq_fp32_rule])
+def test_mx_quantiser_mutants_are_caught(mutant):
+    r = np.random.default_rng(1)
+    caught = (_fails(pins_mx.check_mx_fill, mutant, r, 32)
+              or _fails(pins_mx.check_mx_exact_representability, mutant, r, 32)
+              or _fails(pins_mx.check_mx_codes_are_library_cast, mutant, r, 32)
+              or _fails(pins_mx.check_mx_roundtrip_bound, mutant, r, 32))
+    assert caught
+
+
+def mx_act_groups_misaligned(x, group):
+    """Groups of `group` starting at column 16 (a wrong group origin)."""
+    x = np.asarray(x, np.float32)
+    rolled = np.roll(x, -16, axis=1)
+    q, s = quantize_mx_act(rolled, group)
+    return np.roll(q, 16, axis=1), s
+
+
+def test_mx_group_origin_mutant_is_caught():
+    assert _fails(pins_mx.check_mx_group_locality, mx_act_groups_misaligned,
+                  np.random.default_rng(2), 32)
+
+
+def gemm_mx32_scales_on_wrong_axis(layout, qa, sa, ma, qb, sb, mb):
+    """A's 1x32 scales applied to permuted K positions (a group/position mix-up)."""
+    from oracle import dequantize_mx_operand, e8m0_decode
+    full = np.repeat(e8m0_decode(sa), 32, axis=1)
+    perm = np.random.default_rng(9).permutation(full.shape[1])
+    a = e4m3_decode(qa) * full[:, perm]
+    return a @ dequantize_mx_operand(qb, sb, "B", layout[1], mb)
+
+
+def test_mx_gemm_scale_axis_mutant_is_caught():
+    M, N, K = 4, 3, 128
+    qa, sa, qb, sb = pins_mx.random_mx_operands(np.random.default_rng(3), "NT", "mx32", "mx32",
+                                                M, N, K)
+    want = pins_mx.fraction_gemm_mx("NT", qa, sa, "mx32", qb, sb, "mx32")
+    got = gemm_mx32_scales_on_wrong_axis("NT", qa, sa, "mx32", qb, sb, "mx32")
+    assert not np.allclose(got, want, rtol=0, atol=1e-12 * np.max(np.abs(want)))
