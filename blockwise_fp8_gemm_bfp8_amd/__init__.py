@@ -11,6 +11,13 @@ Functions (same names as the C ABI in include/bfp8.h, without the prefix):
   quantize_act_dual(x)          -> (q, s, qt, st): both of the above from one read
   quantize_weight(w)            -> (q uint8 [R][C], s f32 [ceil(R/128)][ceil(C/128)])
   gemm(layout, qa, sa, qb, sb, mode_a, mode_b) -> bf16 [M][N]
+Power-of-two (E8M0) scales, group 32 or 128 (scales are uint8 tensors):
+  quantize_mx_act(x, group)            -> (q, s u8 [R][C/group])
+  quantize_mx_act_transposed(x, group) -> (qt, st u8 [C][M/group])
+  quantize_mx_act_dual(x, group)       -> (q, s, qt, st)
+  quantize_mx_weight(w)                -> (q, s u8 [ceil(R/128)][ceil(C/128)])
+  gemm_mx(layout, qa, sa, qb, sb, mode_a, mode_b) -> bf16 [M][N]
+    (modes 'act' = 1x128, 'block' = 128x128, 'mx32' = 1x32)
 """
 
 import ctypes
@@ -27,6 +34,11 @@ __all__ = [
     "quantize_weight",
     "gemm",
     "gemm_workspace_bytes",
+    "quantize_mx_act",
+    "quantize_mx_act_transposed",
+    "quantize_mx_act_dual",
+    "quantize_mx_weight",
+    "gemm_mx",
     "lib",
     "BFP8Error",
     "STATUS",
@@ -46,7 +58,7 @@ STATUS = {
     8: "BFP8_ERR_HIP",
 }
 LAYOUTS = {"NN": 0, "NT": 1, "TN": 2}
-MODES = {"act": 0, "block": 1}
+MODES = {"act": 0, "block": 1, "mx32": 2}
 DTYPES = {torch.bfloat16: 0, torch.float32: 1}
 
 _i64 = ctypes.c_int64
@@ -61,6 +73,13 @@ _SIGNATURES = {
     "bfp8_gemm": [_int, _i64, _i64, _i64, _vp, _i64, _vp, _int, _vp, _i64, _vp, _int, _vp,
                   _i64, _vp, ctypes.c_size_t, _vp],
     "bfp8_gemm_workspace_bytes": [_int, _int, _int, _i64, _i64, _i64],
+    "bfp8_quantize_mx_act": [_vp, _int, _i64, _i64, _i64, _int, _vp, _i64, _vp, _vp],
+    "bfp8_quantize_mx_act_transposed": [_vp, _int, _i64, _i64, _i64, _int, _vp, _i64, _vp, _vp],
+    "bfp8_quantize_mx_act_dual": [_vp, _int, _i64, _i64, _i64, _int, _vp, _i64, _vp, _vp, _i64,
+                                  _vp, _vp],
+    "bfp8_quantize_mx_weight": [_vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _vp],
+    "bfp8_gemm_mx": [_int, _i64, _i64, _i64, _vp, _i64, _vp, _int, _vp, _i64, _vp, _int, _vp,
+                     _i64, _vp, ctypes.c_size_t, _vp],
     "bfp8_status_str": [_int],
     "bfp8_abi_version": [],
 }
@@ -225,6 +244,97 @@ def gemm(layout: str, qa, sa, qb, sb, mode_a: str = "act", mode_b: str = "block"
     if ws_bytes and (workspace is None or workspace.numel() < ws_bytes):
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=qa.device)
     _check("bfp8_gemm", lib().bfp8_gemm(
+        LAYOUTS[layout], M, N, K, qa.data_ptr(), qa.stride(0), sa.data_ptr(), MODES[mode_a],
+        qb.data_ptr(), qb.stride(0), sb.data_ptr(), MODES[mode_b], out.data_ptr(),
+        out.stride(0), workspace.data_ptr() if ws_bytes else None, ws_bytes, _stream(qa)))
+    return out
+
+
+# ---- power-of-two (E8M0) scales --------------------------------------------
+
+def _scale_bytes(rows: int, cols: int, device):
+    """Dense uint8 [rows][cols] scale tensor with 4 readable bytes of slack
+    past its end (the GEMM fetches scales as aligned 32-bit words)."""
+    n = rows * cols
+    return torch.empty((n + 4,), dtype=torch.uint8, device=device)[:n].view(rows, cols)
+
+
+def quantize_mx_act(x: torch.Tensor, group: int = 128, q=None, s=None):
+    """Power-of-two scales, groups of `group` along rows; see bfp8_quantize_mx_act."""
+    _check_input(x, "x")
+    R, C = x.shape
+    if q is None:
+        q = _padded_empty(R, C, torch.uint8, x.device, 16)
+    if s is None:
+        s = _scale_bytes(R, max(C // group, 0), x.device)
+    _check("bfp8_quantize_mx_act", lib().bfp8_quantize_mx_act(
+        x.data_ptr(), DTYPES[x.dtype], R, C, x.stride(0), group, q.data_ptr(), q.stride(0),
+        s.data_ptr(), _stream(x)))
+    return q, s
+
+
+def quantize_mx_act_transposed(x: torch.Tensor, group: int = 128, qt=None, st=None):
+    """Power-of-two scales, token groups written transposed; see
+    bfp8_quantize_mx_act_transposed."""
+    _check_input(x, "x")
+    M, C = x.shape
+    if qt is None:
+        qt = _padded_empty(C, M, torch.uint8, x.device, 16)
+    if st is None:
+        st = _scale_bytes(C, max(M // group, 0), x.device)
+    _check("bfp8_quantize_mx_act_transposed", lib().bfp8_quantize_mx_act_transposed(
+        x.data_ptr(), DTYPES[x.dtype], M, C, x.stride(0), group, qt.data_ptr(), qt.stride(0),
+        st.data_ptr(), _stream(x)))
+    return qt, st
+
+
+def quantize_mx_act_dual(x: torch.Tensor, group: int = 128, q=None, s=None, qt=None, st=None):
+    """Both power-of-two layouts from one read; returns (q, s, qt, st)."""
+    _check_input(x, "x")
+    M, C = x.shape
+    if q is None:
+        q = _padded_empty(M, C, torch.uint8, x.device, 16)
+    if s is None:
+        s = _scale_bytes(M, max(C // group, 0), x.device)
+    if qt is None:
+        qt = _padded_empty(C, M, torch.uint8, x.device, 16)
+    if st is None:
+        st = _scale_bytes(C, max(M // group, 0), x.device)
+    _check("bfp8_quantize_mx_act_dual", lib().bfp8_quantize_mx_act_dual(
+        x.data_ptr(), DTYPES[x.dtype], M, C, x.stride(0), group, q.data_ptr(), q.stride(0),
+        s.data_ptr(), qt.data_ptr(), qt.stride(0), st.data_ptr(), _stream(x)))
+    return q, s, qt, st
+
+
+def quantize_mx_weight(w: torch.Tensor, q=None, s=None):
+    """128x128 blocks with power-of-two scales; see bfp8_quantize_mx_weight."""
+    _check_input(w, "w")
+    R, C = w.shape
+    if q is None:
+        q = _padded_empty(R, C, torch.uint8, w.device, 16)
+    if s is None:
+        s = _scale_bytes((R + 127) // 128, (C + 127) // 128, w.device)
+    _check("bfp8_quantize_mx_weight", lib().bfp8_quantize_mx_weight(
+        w.data_ptr(), DTYPES[w.dtype], R, C, w.stride(0), q.data_ptr(), q.stride(0),
+        s.data_ptr(), _stream(w)))
+    return q, s
+
+
+def gemm_mx(layout: str, qa, sa, qb, sb, mode_a: str = "act", mode_b: str = "block",
+            out: torch.Tensor = None, workspace: torch.Tensor = None, split_k: bool = True):
+    """GEMM on E8M0-scaled operands -> bf16 [M][N]; see bfp8_gemm_mx."""
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    M, N, K = gemm_dims(layout, qa, qb)
+    for name, sc in (("sa", sa), ("sb", sb)):
+        if not sc.is_contiguous() or sc.dtype != torch.uint8:
+            raise ValueError(f"{name} must be a dense uint8 (E8M0) tensor")
+    if out is None:
+        out = _padded_empty(M, N, torch.bfloat16, qa.device, 8)
+    ws_bytes = gemm_workspace_bytes(layout, mode_a, mode_b, M, N, K) if split_k else 0
+    if ws_bytes and (workspace is None or workspace.numel() < ws_bytes):
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=qa.device)
+    _check("bfp8_gemm_mx", lib().bfp8_gemm_mx(
         LAYOUTS[layout], M, N, K, qa.data_ptr(), qa.stride(0), sa.data_ptr(), MODES[mode_a],
         qb.data_ptr(), qb.stride(0), sb.data_ptr(), MODES[mode_b], out.data_ptr(),
         out.stride(0), workspace.data_ptr() if ws_bytes else None, ws_bytes, _stream(qa)))

@@ -47,6 +47,56 @@ inline bfp8_status check_quant_common(const void* x, bfp8_in_dtype dt, int64_t r
   return BFP8_OK;
 }
 
+inline int mode_index(bfp8_scale_mode m) {
+  return m == BFP8_SCALE_1x128 ? 0 : (m == BFP8_SCALE_128x128 ? 1 : 2);
+}
+
+// Shape, pointer and alignment checks shared by the two GEMM entry points
+// (layout and scale modes are checked by the callers), then the launch.
+bfp8_status gemm_common(bfp8_layout layout, int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                        int64_t lda, const void* sA, bfp8_scale_mode modeA, const uint8_t* B,
+                        int64_t ldb, const void* sB, bfp8_scale_mode modeB, void* C, int64_t ldc,
+                        void* workspace, size_t workspace_bytes, bool mx, hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return BFP8_ERR_SHAPE;
+  if (M == 0 || N == 0) return BFP8_OK;
+  if (C == nullptr) return BFP8_ERR_NULL;
+  if (!aligned16(C)) return BFP8_ERR_ALIGN;
+  if (ldc < N) return BFP8_ERR_SHAPE;
+  if (ldc % 8 != 0) return BFP8_ERR_ALIGN;
+  if (cdiv(M, 256) * cdiv(N, 256) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+  if (K == 0) return launch_fill_bf16_zero(static_cast<uint16_t*>(C), M, N, ldc, stream);
+
+  if (A == nullptr || B == nullptr || sA == nullptr || sB == nullptr) return BFP8_ERR_NULL;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(sA) || !aligned16(sB)) return BFP8_ERR_ALIGN;
+  const bool a_kmajor = layout == BFP8_TN;   // A 'T' stored [K][M]
+  const bool b_kmajor = layout != BFP8_NT;   // B 'N' stored [K][N]
+  const int64_t a_row = a_kmajor ? M : K;    // stored row length
+  const int64_t b_row = b_kmajor ? N : K;
+  if (lda < a_row || ldb < b_row) return BFP8_ERR_SHAPE;
+  if (lda % 16 != 0 || ldb % 16 != 0) return BFP8_ERR_ALIGN;
+  if (lda > kMaxGemmLd || ldb > kMaxGemmLd) return BFP8_ERR_SHAPE;
+  if (workspace != nullptr && !aligned16(workspace)) return BFP8_ERR_ALIGN;
+
+  GemmArgs g;
+  g.A = A;
+  g.lda = lda;
+  g.sA = sA;
+  g.modeA = mode_index(modeA);
+  g.a_kmajor = a_kmajor;
+  g.B = B;
+  g.ldb = ldb;
+  g.sB = sB;
+  g.modeB = mode_index(modeB);
+  g.b_kmajor = b_kmajor;
+  g.C = static_cast<uint16_t*>(C);
+  g.ldc = ldc;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.mx = mx;
+  return launch_gemm(g, workspace, workspace_bytes, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -77,7 +127,7 @@ bfp8_status bfp8_quantize_act(const void* x, bfp8_in_dtype dt, int64_t rows, int
   if (st != BFP8_OK || rows == 0 || cols == 0) return st;
   if (ldq < cols) return BFP8_ERR_SHAPE;
   if (rows * (cols / 128) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
-  return launch_quantize_act(x, dt, rows, cols, ldx, q, ldq, s, stream);
+  return launch_quantize_act(x, dt, rows, cols, ldx, 0, 128, q, ldq, s, stream);
 }
 
 bfp8_status bfp8_quantize_act_transposed(const void* x, bfp8_in_dtype dt, int64_t rows,
@@ -88,7 +138,7 @@ bfp8_status bfp8_quantize_act_transposed(const void* x, bfp8_in_dtype dt, int64_
   if (st != BFP8_OK || rows == 0 || cols == 0) return st;
   if (ldqt < rows) return BFP8_ERR_SHAPE;
   if (rows / 128 > kMaxGridY || cdiv(cols, 64) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
-  return launch_quantize_act_transposed(x, dt, rows, cols, ldx, qt, ldqt, st_, stream);
+  return launch_quantize_act_transposed(x, dt, rows, cols, ldx, 0, 128, qt, ldqt, st_, stream);
 }
 
 bfp8_status bfp8_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
@@ -103,7 +153,8 @@ bfp8_status bfp8_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t rows
   if (ldq < cols || ldqt < rows) return BFP8_ERR_SHAPE;
   if (ldqt % 16 != 0) return BFP8_ERR_ALIGN;
   if (rows / 128 > kMaxGridY || cols / 128 >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
-  return launch_quantize_act_dual(x, dt, rows, cols, ldx, q, ldq, s, qt, ldqt, st_, stream);
+  return launch_quantize_act_dual(x, dt, rows, cols, ldx, 0, 128, q, ldq, s, qt, ldqt, st_,
+                                  stream);
 }
 
 bfp8_status bfp8_quantize_weight(const void* w, bfp8_in_dtype dt, int64_t rows, int64_t cols,
@@ -113,14 +164,68 @@ bfp8_status bfp8_quantize_weight(const void* w, bfp8_in_dtype dt, int64_t rows, 
   if (st != BFP8_OK || rows == 0 || cols == 0) return st;
   if (ldq < cols) return BFP8_ERR_SHAPE;
   if (cdiv(rows, 128) > kMaxGridY || cdiv(cols, 128) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
-  return launch_quantize_weight(w, dt, rows, cols, ldw, q, ldq, s, stream);
+  return launch_quantize_weight(w, dt, rows, cols, ldw, 0, q, ldq, s, stream);
+}
+
+// ---- power-of-two (E8M0) scale rule ----------------------------------------
+
+bfp8_status bfp8_quantize_mx_act(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
+                                 int64_t ldx, int group, uint8_t* q, int64_t ldq, uint8_t* s,
+                                 hipStream_t stream) {
+  if (group != 32 && group != 128) return BFP8_ERR_SCALE_MODE;
+  if (cols % 128 != 0 && cols > 0) return valid_dtype(dt) ? BFP8_ERR_SHAPE : BFP8_ERR_DTYPE;
+  bfp8_status st = check_quant_common(x, dt, rows, cols, ldx, q, ldq, s);
+  if (st != BFP8_OK || rows == 0 || cols == 0) return st;
+  if (ldq < cols) return BFP8_ERR_SHAPE;
+  if (rows * (cols / 128) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+  return launch_quantize_act(x, dt, rows, cols, ldx, 1, group, q, ldq, s, stream);
+}
+
+bfp8_status bfp8_quantize_mx_act_transposed(const void* x, bfp8_in_dtype dt, int64_t rows,
+                                            int64_t cols, int64_t ldx, int group, uint8_t* qt,
+                                            int64_t ldqt, uint8_t* st_, hipStream_t stream) {
+  if (group != 32 && group != 128) return BFP8_ERR_SCALE_MODE;
+  if (rows % 128 != 0 && rows > 0) return valid_dtype(dt) ? BFP8_ERR_SHAPE : BFP8_ERR_DTYPE;
+  bfp8_status st = check_quant_common(x, dt, rows, cols, ldx, qt, ldqt, st_);
+  if (st != BFP8_OK || rows == 0 || cols == 0) return st;
+  if (ldqt < rows) return BFP8_ERR_SHAPE;
+  if (rows / 128 > kMaxGridY || cdiv(cols, 64) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+  return launch_quantize_act_transposed(x, dt, rows, cols, ldx, 1, group, qt, ldqt, st_, stream);
+}
+
+bfp8_status bfp8_quantize_mx_act_dual(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
+                                      int64_t ldx, int group, uint8_t* q, int64_t ldq, uint8_t* s,
+                                      uint8_t* qt, int64_t ldqt, uint8_t* st_,
+                                      hipStream_t stream) {
+  if (group != 32 && group != 128) return BFP8_ERR_SCALE_MODE;
+  if (((rows % 128 != 0 && rows > 0) || (cols % 128 != 0 && cols > 0)))
+    return valid_dtype(dt) ? BFP8_ERR_SHAPE : BFP8_ERR_DTYPE;
+  bfp8_status st = check_quant_common(x, dt, rows, cols, ldx, q, ldq, s);
+  if (st != BFP8_OK || rows == 0 || cols == 0) return st;
+  if (qt == nullptr || st_ == nullptr) return BFP8_ERR_NULL;
+  if (!aligned16(qt) || !aligned16(st_)) return BFP8_ERR_ALIGN;
+  if (ldq < cols || ldqt < rows) return BFP8_ERR_SHAPE;
+  if (ldqt % 16 != 0) return BFP8_ERR_ALIGN;
+  if (rows / 128 > kMaxGridY || cols / 128 >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+  return launch_quantize_act_dual(x, dt, rows, cols, ldx, 1, group, q, ldq, s, qt, ldqt, st_,
+                                  stream);
+}
+
+bfp8_status bfp8_quantize_mx_weight(const void* w, bfp8_in_dtype dt, int64_t rows, int64_t cols,
+                                    int64_t ldw, uint8_t* q, int64_t ldq, uint8_t* s,
+                                    hipStream_t stream) {
+  bfp8_status st = check_quant_common(w, dt, rows, cols, ldw, q, ldq, s);
+  if (st != BFP8_OK || rows == 0 || cols == 0) return st;
+  if (ldq < cols) return BFP8_ERR_SHAPE;
+  if (cdiv(rows, 128) > kMaxGridY || cdiv(cols, 128) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+  return launch_quantize_weight(w, dt, rows, cols, ldw, 1, q, ldq, s, stream);
 }
 
 size_t bfp8_gemm_workspace_bytes(bfp8_layout layout, bfp8_scale_mode modeA,
                                  bfp8_scale_mode modeB, int64_t M, int64_t N, int64_t K) {
   if (layout != BFP8_NN && layout != BFP8_NT && layout != BFP8_TN) return static_cast<size_t>(-1);
-  if ((modeA != BFP8_SCALE_1x128 && modeA != BFP8_SCALE_128x128) ||
-      (modeB != BFP8_SCALE_1x128 && modeB != BFP8_SCALE_128x128))
+  if ((modeA != BFP8_SCALE_1x128 && modeA != BFP8_SCALE_128x128 && modeA != BFP8_SCALE_1x32) ||
+      (modeB != BFP8_SCALE_1x128 && modeB != BFP8_SCALE_128x128 && modeB != BFP8_SCALE_1x32))
     return static_cast<size_t>(-1);
   if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return static_cast<size_t>(-1);
   return gemm_workspace(layout, modeA, modeB, M, N, K);
@@ -135,43 +240,26 @@ bfp8_status bfp8_gemm(bfp8_layout layout, int64_t M, int64_t N, int64_t K, const
   if ((modeA != BFP8_SCALE_1x128 && modeA != BFP8_SCALE_128x128) ||
       (modeB != BFP8_SCALE_1x128 && modeB != BFP8_SCALE_128x128))
     return BFP8_ERR_SCALE_MODE;
-  if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return BFP8_ERR_SHAPE;
-  if (M == 0 || N == 0) return BFP8_OK;
-  if (C == nullptr) return BFP8_ERR_NULL;
-  if (!aligned16(C)) return BFP8_ERR_ALIGN;
-  if (ldc < N) return BFP8_ERR_SHAPE;
-  if (ldc % 8 != 0) return BFP8_ERR_ALIGN;
-  if (cdiv(M, 256) * cdiv(N, 256) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
-  if (K == 0) return launch_fill_bf16_zero(static_cast<uint16_t*>(C), M, N, ldc, stream);
+  return gemm_common(layout, M, N, K, A, lda, sA, modeA, B, ldb, sB, modeB, C, ldc, workspace,
+                     workspace_bytes, false, stream);
+}
 
-  if (A == nullptr || B == nullptr || sA == nullptr || sB == nullptr) return BFP8_ERR_NULL;
-  if (!aligned16(A) || !aligned16(B) || !aligned16(sA) || !aligned16(sB)) return BFP8_ERR_ALIGN;
-  const bool a_kmajor = layout == BFP8_TN;   // A 'T' stored [K][M]
-  const bool b_kmajor = layout != BFP8_NT;   // B 'N' stored [K][N]
-  const int64_t a_row = a_kmajor ? M : K;    // stored row length
-  const int64_t b_row = b_kmajor ? N : K;
-  if (lda < a_row || ldb < b_row) return BFP8_ERR_SHAPE;
-  if (lda % 16 != 0 || ldb % 16 != 0) return BFP8_ERR_ALIGN;
-  if (lda > kMaxGemmLd || ldb > kMaxGemmLd) return BFP8_ERR_SHAPE;
-  if (workspace != nullptr && !aligned16(workspace)) return BFP8_ERR_ALIGN;
-
-  GemmArgs g;
-  g.A = A;
-  g.lda = lda;
-  g.sA = sA;
-  g.modeA = modeA == BFP8_SCALE_1x128 ? 0 : 1;
-  g.a_kmajor = a_kmajor;
-  g.B = B;
-  g.ldb = ldb;
-  g.sB = sB;
-  g.modeB = modeB == BFP8_SCALE_1x128 ? 0 : 1;
-  g.b_kmajor = b_kmajor;
-  g.C = static_cast<uint16_t*>(C);
-  g.ldc = ldc;
-  g.M = M;
-  g.N = N;
-  g.K = K;
-  return launch_gemm(g, workspace, workspace_bytes, stream);
+bfp8_status bfp8_gemm_mx(bfp8_layout layout, int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                         int64_t lda, const uint8_t* sA, bfp8_scale_mode modeA, const uint8_t* B,
+                         int64_t ldb, const uint8_t* sB, bfp8_scale_mode modeB, void* C,
+                         int64_t ldc, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  if (layout != BFP8_NN && layout != BFP8_NT && layout != BFP8_TN) return BFP8_ERR_LAYOUT;
+  auto valid = [](bfp8_scale_mode m) {
+    return m == BFP8_SCALE_1x128 || m == BFP8_SCALE_128x128 || m == BFP8_SCALE_1x32;
+  };
+  if (!valid(modeA) || !valid(modeB)) return BFP8_ERR_SCALE_MODE;
+  // 1x32 scales only for K-contiguous operands (A of NN/NT, B of NT)
+  if ((modeA == BFP8_SCALE_1x32 && layout == BFP8_TN) ||
+      (modeB == BFP8_SCALE_1x32 && layout != BFP8_NT))
+    return BFP8_ERR_SCALE_MODE;
+  return gemm_common(layout, M, N, K, A, lda, sA, modeA, B, ldb, sB, modeB, C, ldc, workspace,
+                     workspace_bytes, true, stream);
 }
 
 }  // extern "C"

@@ -41,6 +41,49 @@ __device__ __forceinline__ void group_scale(float amax, float& s, float& inv) {
   }
 }
 
+// Power-of-two group scale (E8M0): e = the least integer with
+// 448 * 2^e >= amax, clamped to [-127, 127], found from amax's float32 bit
+// fields (448 = 1.75 * 2^8: a mantissa above 1.75 needs one more binade);
+// an all-zero group gets e = 0.  Returns the scale byte e + 127 and sets
+// inv = 2^-e exactly.  (A float32-subnormal amax is outside the contract;
+// it gets the clamped e = -127.)
+__device__ __forceinline__ uint8_t group_scale_pow2(float amax, float& inv) {
+  const uint32_t bits = __float_as_uint(amax);
+  const int biased = static_cast<int>((bits >> 23) & 0xFFu);
+  int e;
+  if (amax == 0.0f) {
+    e = 0;
+  } else if (biased == 0) {
+    e = -127;
+  } else {
+    e = biased - 127 - 8 + ((bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  }
+  inv = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
+  return static_cast<uint8_t>(e + 127);
+}
+
+// The two scale rules behind one interface: RULE 0 = float32 amax / 448
+// (scale type float), RULE 1 = power of two stored as an E8M0 byte.
+template <int RULE>
+struct ScaleRule;
+template <>
+struct ScaleRule<0> {
+  typedef float type;
+  static __device__ __forceinline__ float make(float amax, float& inv) {
+    float s;
+    group_scale(amax, s, inv);
+    return s;
+  }
+};
+template <>
+struct ScaleRule<1> {
+  typedef uint8_t type;
+  static __device__ __forceinline__ uint8_t make(float amax, float& inv) {
+    return group_scale_pow2(amax, inv);
+  }
+};
+
 // Four float32 -> four E4M3 codes packed little-endian in one dword.
 // Saturation is done by the clamp (the conversion instruction's own
 // overflow result is NaN); the conversion rounds to nearest even and keeps
@@ -80,18 +123,23 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Host-side launch helpers (defined in the .hip files).
+// Host-side launch helpers (defined in the .hip files).  `rule` selects the
+// scale rule (0: float32 amax/448, 1: power-of-two E8M0 byte) and `s` points
+// to float or uint8_t scales accordingly; `group` is the group length along
+// the grouped axis (128, or 32 for the power-of-two rule).
 bfp8_status launch_quantize_act(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
-                                int64_t ldx, uint8_t* q, int64_t ldq, float* s,
-                                hipStream_t stream);
+                                int64_t ldx, int rule, int group, uint8_t* q, int64_t ldq,
+                                void* s, hipStream_t stream);
 bfp8_status launch_quantize_act_transposed(const void* x, bfp8_in_dtype dt, int64_t rows,
-                                           int64_t cols, int64_t ldx, uint8_t* qt,
-                                           int64_t ldqt, float* st, hipStream_t stream);
+                                           int64_t cols, int64_t ldx, int rule, int group,
+                                           uint8_t* qt, int64_t ldqt, void* st,
+                                           hipStream_t stream);
 bfp8_status launch_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
-                                     int64_t ldx, uint8_t* q, int64_t ldq, float* s, uint8_t* qt,
-                                     int64_t ldqt, float* st, hipStream_t stream);
+                                     int64_t ldx, int rule, int group, uint8_t* q, int64_t ldq,
+                                     void* s, uint8_t* qt, int64_t ldqt, void* st,
+                                     hipStream_t stream);
 bfp8_status launch_quantize_weight(const void* w, bfp8_in_dtype dt, int64_t rows, int64_t cols,
-                                   int64_t ldw, uint8_t* q, int64_t ldq, float* s,
+                                   int64_t ldw, int rule, uint8_t* q, int64_t ldq, void* s,
                                    hipStream_t stream);
 
 struct GemmArgs {
@@ -100,17 +148,18 @@ struct GemmArgs {
   // stored orientation (see include/bfp8.h).
   const uint8_t* A;
   int64_t lda;
-  const float* sA;
-  int modeA;  // 0 = 1x128 act groups, 1 = 128x128 blocks
+  const void* sA;  // float32 scales, or E8M0 bytes when mx
+  int modeA;  // 0 = 1x128 act groups, 1 = 128x128 blocks, 2 = 1x32 groups (mx only)
   bool a_kmajor;
   const uint8_t* B;
   int64_t ldb;
-  const float* sB;
+  const void* sB;
   int modeB;
   bool b_kmajor;
   uint16_t* C;  // bf16 bits
   int64_t ldc;
   int64_t M, N, K;
+  bool mx;  // power-of-two (E8M0) scales applied by the MFMA
 };
 
 bfp8_status launch_gemm(const GemmArgs& a, void* workspace, size_t workspace_bytes,

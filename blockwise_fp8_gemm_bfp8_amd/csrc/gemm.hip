@@ -30,6 +30,18 @@
 //     hardware deals workgroups to the 8 XCDs round robin) and tiles are
 //     grouped along M so concurrent tiles on an XCD share A rows and B
 //     columns in that XCD's L2.
+//
+// The same kernel, instantiated with MX = true, multiplies operands whose
+// scales are powers of two stored as E8M0 bytes (Puro-2B translation,
+// section 3.2: the SM120 runs used power-of-two block scales on the MXFP8
+// path).  There the scales ride in the matrix-core instruction
+// (v_mfma_scale_f32_16x16x128_f8f6f4), the accumulators are the MFMA's C
+// operand, and no VALU promotion is needed.  The instruction takes one
+// scale byte per row and 32-deep K chunk: the register of lane group j
+// (lane 16j + r) scales row r's K values [32j, 32j + 32) -- which the
+// fragment layout below spreads over lane groups 2j mod 4 and 2j + 1 mod 4
+// (measured on gfx950) -- so the lane's byte is always its row's scale of
+// chunk j = lane / 16.
 
 #include "common.h"
 
@@ -180,11 +192,12 @@ struct Operand {
 
   // Fragment of 16 rows starting at tile row `r0` (multiple of 16): 32 bytes
   // per lane; lane group g = lane/16 holds K bytes [16g, 16g+16) followed by
-  // [64+16g, 64+16g+16) for both operands (any K order works as long as A
-  // and B agree).  With this split the four lane groups of one ds_read_b128
-  // touch four adjacent 16-byte chunks of their rows, which the LDS serves
-  // without bank conflicts; reading chunks 2g and 2g+1 instead halves the
-  // read rate.
+  // [64+16g, 64+16g+16) for both operands.  This is also the K order the
+  // scaled MFMA assumes when it applies one scale per 32-deep K chunk (see
+  // the file comment).  With this split the four lane groups of one
+  // ds_read_b128 touch four adjacent 16-byte chunks of their rows, which the
+  // LDS serves without bank conflicts; reading chunks 2g and 2g+1 instead
+  // halves the read rate.
   __device__ __forceinline__ v8i frag(const uint8_t* tile, int r0, int lane) const {
     const int g = lane >> 4, q = lane & 15;
     if (!KMAJOR) {
@@ -249,13 +262,49 @@ __device__ __forceinline__ void load_block_scales(const float* s, int64_t r0, in
                make_rsrc(s, nblk * KB * 4));
 }
 
-template <bool A_KM, bool B_KM, int MODE_A, int MODE_B>
+// E8M0 scale staging: for each of 256 consecutive rows (A) or columns (B),
+// the aligned 32-bit word holding its scale byte(s) for K block kb goes to
+// one LDS word (the reader picks the byte: `mx_byte_index`).  MODE 0: 1x128
+// groups, one byte per row; MODE 2: 1x32 groups ([rows][K/32], K-contiguous
+// only), the word holds the 4 bytes of the block's 32-groups; MODE 1:
+// 128x128 blocks, lanes 0 and 1 fetch the two blocks the tile spans.  The
+// scale tensor is read up to its size rounded up to 4 bytes.
+template <bool KMAJOR, int MODE>
+__device__ __forceinline__ int64_t mx_scale_index(int64_t r, int64_t rows, int64_t nblk,
+                                                  int64_t KB, int64_t kb) {
+  if (MODE == 1) return KMAJOR ? kb * nblk + r : r * KB + kb;  // r: block index
+  if (MODE == 2) return r * KB * 4 + kb * 4;
+  return KMAJOR ? kb * rows + r : r * KB + kb;
+}
+template <bool KMAJOR, int MODE>
+__device__ __forceinline__ void load_mx_scales(const uint8_t* s, int64_t r0, int64_t rows,
+                                               int64_t nblk, int64_t KB, int64_t kb, uint8_t* dst,
+                                               int sub, int lane) {
+  int64_t r;
+  if (MODE == 1) {
+    r = r0 / 128 + (lane < 2 ? lane : 0);
+    if (r > nblk - 1) r = nblk - 1;
+  } else {
+    r = r0 + sub * 64 + lane;
+    if (r > rows - 1) r = rows - 1;
+  }
+  const int64_t idx = mx_scale_index<KMAJOR, MODE>(r, rows, nblk, KB, kb);
+  const int64_t bytes = MODE == 1 ? nblk * KB : (MODE == 2 ? rows * KB * 4 : rows * KB);
+  copy4_to_lds(__builtin_amdgcn_readfirstlane(lds_addr(dst) + sub * 256),
+               static_cast<uint32_t>(idx & ~int64_t(3)), make_rsrc(s, (bytes + 3) & ~int64_t(3)));
+}
+
+template <bool A_KM, bool B_KM, int MODE_A, int MODE_B, bool MX>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(2, 2))) void
-gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ sA,
-            const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ sB,
+gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__ sA_,
+            const uint8_t* __restrict__ B, int64_t ldb, const void* __restrict__ sB_,
             uint16_t* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K, int tiles_m,
             int tiles_n, float* __restrict__ part, int64_t ldp) {
+  const float* __restrict__ sA = static_cast<const float*>(sA_);  // float32 scales (!MX)
+  const float* __restrict__ sB = static_cast<const float*>(sB_);
+  const uint8_t* __restrict__ eA = static_cast<const uint8_t*>(sA_);  // E8M0 scales (MX)
+  const uint8_t* __restrict__ eB = static_cast<const uint8_t*>(sB_);
   // Two pipeline stages; block kb lives in stage kb % 2.
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
@@ -297,12 +346,22 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
       opb.load_piece(rsrc_b, st + kTileABytes, wave, piece - 4);
     } else {
       uint8_t* sdst = st + kTileABytes + kTileBBytes;
-      if (wave < 4) {
-        if (MODE_A == 0) load_act_scales<A_KM>(sA, m0, M, KB, kb, sdst, wave, lane);
-        else if (wave == 0) load_block_scales<A_KM>(sA, m0, MBk, KB, kb, sdst, lane);
+      if constexpr (MX) {
+        if (wave < 4) {
+          if (MODE_A != 1 || wave == 0)
+            load_mx_scales<A_KM, MODE_A>(eA, m0, M, MBk, KB, kb, sdst, wave, lane);
+        } else {
+          if (MODE_B != 1 || wave == 4)
+            load_mx_scales<B_KM, MODE_B>(eB, n0, N, NBk, KB, kb, sdst + 1024, wave - 4, lane);
+        }
       } else {
-        if (MODE_B == 0) load_act_scales<B_KM>(sB, n0, N, KB, kb, sdst + 1024, wave - 4, lane);
-        else if (wave == 4) load_block_scales<B_KM>(sB, n0, NBk, KB, kb, sdst + 1024, lane);
+        if (wave < 4) {
+          if (MODE_A == 0) load_act_scales<A_KM>(sA, m0, M, KB, kb, sdst, wave, lane);
+          else if (wave == 0) load_block_scales<A_KM>(sA, m0, MBk, KB, kb, sdst, lane);
+        } else {
+          if (MODE_B == 0) load_act_scales<B_KM>(sB, n0, N, KB, kb, sdst + 1024, wave - 4, lane);
+          else if (wave == 4) load_block_scales<B_KM>(sB, n0, NBk, KB, kb, sdst + 1024, lane);
+        }
       }
     }
   };
@@ -334,6 +393,61 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
       const float4 v = *reinterpret_cast<const float4*>(s_lds + BM + wn * WN + 16 * j + 4 * g);
       cb[0] = v.x; cb[1] = v.y; cb[2] = v.z; cb[3] = v.w;
     }
+  };
+
+  // E8M0 scales of this lane's fragments (MX): for each A row subtile i and
+  // B column subtile j, the byte of the staged LDS word that covers this
+  // lane's row / column and 32 K values.  The byte index within the word is
+  // (scale index) & 3; its per-lane part is fixed for the tile and packed 2
+  // bits per subtile into one register per operand, the K-block part is
+  // added per block.
+  auto byte_base = [&](bool b_side, int rt) -> uint32_t {
+    const int mode = b_side ? MODE_B : MODE_A;
+    const bool km = b_side ? B_KM : A_KM;
+    const int64_t r0 = b_side ? n0 : m0, rows = b_side ? N : M, nblk = b_side ? NBk : MBk;
+    if (mode == 2) return 0;
+    if (mode == 1) {
+      int64_t blk = (r0 + rt) / 128;
+      if (blk > nblk - 1) blk = nblk - 1;
+      return static_cast<uint32_t>(km ? blk : blk * KB) & 3u;
+    }
+    int64_t r = r0 + rt;
+    if (r > rows - 1) r = rows - 1;
+    return static_cast<uint32_t>(km ? r : r * KB) & 3u;
+  };
+  uint32_t pack_a = 0, pack_b = 0;
+  if constexpr (MX) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) pack_a |= byte_base(false, wm * WM + 16 * i + r16) << (2 * i);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) pack_b |= byte_base(true, wn * WN + 16 * j + r16) << (2 * j);
+  }
+  int mxa[TM];
+  // K-block part of the byte index: kb (K-contiguous act / block scales),
+  // kb * rows or kb * nblk (K-major), 0 for 1x32 (byte = lane group)
+  auto kterm = [&](int mode, bool km, int64_t rows, int64_t nblk, int64_t kb) -> uint32_t {
+    if (mode == 2) return 0;
+    return static_cast<uint32_t>(km ? kb * (mode == 1 ? nblk : rows) : kb) & 3u;
+  };
+  auto mx_scales_a = [&](const uint8_t* st, int64_t kb) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(st + kTileABytes + kTileBBytes);
+    const uint32_t ka = kterm(MODE_A, A_KM, M, MBk, kb);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int rt = wm * WM + 16 * i + r16;
+      // block scales: word 0 / 1 = the tile's first / second 128 rows
+      const uint32_t word = MODE_A == 1 ? w[wm >> 1] : w[rt];
+      const uint32_t sh = MODE_A == 2 ? 8u * g : 8u * (((pack_a >> (2 * i)) + ka) & 3u);
+      mxa[i] = static_cast<int>((word >> sh) & 0xFFu);
+    }
+  };
+  // B scale of column subtile j, read while the MFMAs of subtile j - 1 run
+  auto mx_scale_b = [&](const uint8_t* st, int64_t kb, int j) -> int {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(st + kTileABytes + kTileBBytes) + BM;
+    const uint32_t word = MODE_B == 1 ? w[wn] : w[wn * WN + 16 * j + r16];
+    const uint32_t kbb = kterm(MODE_B, B_KM, N, NBk, kb);
+    const uint32_t sh = MODE_B == 2 ? 8u * g : 8u * (((pack_b >> (2 * j)) + kbb) & 3u);
+    return static_cast<int>((word >> sh) & 0xFFu);
   };
 
   v4f acc[TM][TN];
@@ -370,7 +484,13 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
 #pragma unroll
   for (int i = 0; i < TM; ++i) af[i] = opa.frag(stage0, wm * WM + 16 * i, lane);
   bq = opb.frag(stage0 + kTileABytes, wn * WN, lane);
-  row_mults(stage0, ra);
+  int mxb = 0;  // B scale of the current column subtile (MX)
+  if constexpr (MX) {
+    mx_scales_a(stage0, kb_begin);
+    mxb = mx_scale_b(stage0, kb_begin, 0);
+  } else {
+    row_mults(stage0, ra);
+  }
 
   // Partials are promoted kLag MFMAs behind their issue (subtile order
   // t = j*TM + i), so the VALU never waits on a result still in the matrix
@@ -405,17 +525,32 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
       if (j + 1 < TN) bn = opb.frag(cur + kTileABytes, wn * WN + 16 * (j + 1), lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) cm_prev[r] = cm_cur[r];
-      col_mults(cur, j, cm_cur);
+      if constexpr (!MX) col_mults(cur, j, cm_cur);
+      int mxb_next = 0;
+      if constexpr (MX) {
+        if (j + 1 < TN) mxb_next = mx_scale_b(cur, kb, j + 1);
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int t = j * TM + i;
-        const v4f pc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            bq, af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-        if (t >= kLag) {
-          const int i2 = (t - kLag) % TM, j2 = (t - kLag) / TM;
-          promote(acc[i2][j2], pend[t % kLag], ra[i2], j2 == j ? cm_cur : cm_prev);
+        if constexpr (MX) {
+          // scale operand 0 (src0 = the B fragment) and 1 (src1 = A), byte 0
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              bq, af[i], acc[i][j], 0, 0, 0, mxb, 0, mxa[i]);
+          // pin the accumulator of the MFMA three issues back here (its
+          // result is ready by now): without an anchor the compiler moves
+          // the MFMAs away from the copies and fragment reads they are
+          // meant to hide, and runs out of registers
+          if (t >= 3) asm volatile("" : "+v"(acc[(t - 3) % TM][(t - 3) / TM]));
+        } else {
+          const v4f pc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              bq, af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+          if (t >= kLag) {
+            const int i2 = (t - kLag) % TM, j2 = (t - kLag) / TM;
+            promote(acc[i2][j2], pend[t % kLag], ra[i2], j2 == j ? cm_cur : cm_prev);
+          }
+          pend[t % kLag] = pc;
         }
-        pend[t % kLag] = pc;
         if (t >= 1 && t <= kLoadPieces) issue_piece(kn, nxt, t - 1);
         // one MFMA and the promotion of the partial kLag issues back per
         // scheduling region: the machine scheduler would otherwise pull each
@@ -423,6 +558,7 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
         __builtin_amdgcn_sched_barrier(0);
       }
       bq = bn;
+      if constexpr (MX) mxb = mxb_next;
     }
     // all MFMAs of this K block are issued; the last kLag subtiles (all in
     // column TN-1) are pending with this block's multipliers
@@ -434,18 +570,39 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const float* __restrict_
 #pragma unroll
       for (int i = 0; i < TM; ++i) af[i] = opa.frag(nxt, wm * WM + 16 * i, lane);
       bq = opb.frag(nxt + kTileABytes, wn * WN, lane);
-      row_mults(nxt, ra);
+      if constexpr (MX) {
+        mx_scales_a(nxt, kb + 1);
+        mxb = mx_scale_b(nxt, kb + 1, 0);
+      } else {
+        row_mults(nxt, ra);
+      }
     }
+    if constexpr (MX) {
 #pragma unroll
-    for (int q = 0; q < kLag; ++q) {
-      const int t = TM * TN - kLag + q;
-      promote(acc[t % TM][TN - 1], pend[t % kLag], ra_last[t % TM], cm_cur);
+      for (int q = 0; q < 3; ++q) asm volatile("" : "+v"(acc[(TM * TN - 3 + q) % TM][TN - 1]));
+    }
+    if constexpr (!MX) {
+#pragma unroll
+      for (int q = 0; q < kLag; ++q) {
+        const int t = TM * TN - kLag + q;
+        promote(acc[t % TM][TN - 1], pend[t % kLag], ra_last[t % TM], cm_cur);
+      }
     }
   };
 
-  for (int kb = kb_begin; kb < kb_end; kb += 2) {
-    kblock(kb, stage0, stage1);
-    if (kb + 1 < kb_end) kblock(kb + 1, stage1, stage0);
+  if constexpr (MX) {
+    // one copy of the block body with the stages picked at run time (two
+    // unrolled copies make the register allocator split the in-place MFMA
+    // accumulators and spill)
+    for (int kb = kb_begin; kb < kb_end; ++kb) {
+      const bool odd = ((kb - kb_begin) & 1) != 0;
+      kblock(kb, odd ? stage1 : stage0, odd ? stage0 : stage1);
+    }
+  } else {
+    for (int kb = kb_begin; kb < kb_end; kb += 2) {
+      kblock(kb, stage0, stage1);
+      if (kb + 1 < kb_end) kblock(kb + 1, stage1, stage0);
+    }
   }
 
   // the copies issued during the last block must land before the stages
@@ -571,16 +728,29 @@ inline bfp8_status last_launch_status() {
 
 }  // namespace
 
-template <bool A_KM, bool B_KM>
+template <bool A_KM, bool B_KM, bool MX>
 static void launch_layout(const GemmArgs& a, dim3 grid, int tm, int tn, float* part,
                           int64_t ldp, hipStream_t stream) {
 #define BFP8_LAUNCH(MA, MB)                                                              \
-  gemm_kernel<A_KM, B_KM, MA, MB><<<grid, dim3(kThreads), 0, stream>>>(                  \
+  gemm_kernel<A_KM, B_KM, MA, MB, MX><<<grid, dim3(kThreads), 0, stream>>>(              \
       a.A, a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K, tm, tn, part, ldp)
   if (a.modeA == 0 && a.modeB == 1) BFP8_LAUNCH(0, 1);
   else if (a.modeA == 0 && a.modeB == 0) BFP8_LAUNCH(0, 0);
   else if (a.modeA == 1 && a.modeB == 0) BFP8_LAUNCH(1, 0);
-  else BFP8_LAUNCH(1, 1);
+  else if (a.modeA == 1 && a.modeB == 1) BFP8_LAUNCH(1, 1);
+  else if constexpr (MX) {
+    // 1x32 groups (mode 2) exist only with E8M0 scales and K-contiguous storage
+    if constexpr (!A_KM && !B_KM) {
+      if (a.modeA == 2 && a.modeB == 2) BFP8_LAUNCH(2, 2);
+      else if (a.modeA == 2 && a.modeB == 0) BFP8_LAUNCH(2, 0);
+      else if (a.modeA == 2 && a.modeB == 1) BFP8_LAUNCH(2, 1);
+      else if (a.modeA == 0 && a.modeB == 2) BFP8_LAUNCH(0, 2);
+      else if (a.modeA == 1 && a.modeB == 2) BFP8_LAUNCH(1, 2);
+    } else if constexpr (!A_KM) {
+      if (a.modeA == 2 && a.modeB == 0) BFP8_LAUNCH(2, 0);
+      else if (a.modeA == 2 && a.modeB == 1) BFP8_LAUNCH(2, 1);
+    }
+  }
 #undef BFP8_LAUNCH
 }
 
@@ -635,10 +805,17 @@ bfp8_status launch_gemm(const GemmArgs& a, void* workspace, size_t workspace_byt
   const int64_t ldp = split_ldp(a.N);
   const dim3 grid(static_cast<unsigned>(nblk), static_cast<unsigned>(S));
   const int tm = static_cast<int>(tiles_m), tn = static_cast<int>(tiles_n);
-  if (!a.a_kmajor && !a.b_kmajor) launch_layout<false, false>(a, grid, tm, tn, part, ldp, stream);
-  else if (!a.a_kmajor && a.b_kmajor) launch_layout<false, true>(a, grid, tm, tn, part, ldp, stream);
-  else if (a.a_kmajor && a.b_kmajor) launch_layout<true, true>(a, grid, tm, tn, part, ldp, stream);
-  else return BFP8_ERR_LAYOUT;
+  if (a.mx) {
+    if (!a.a_kmajor && !a.b_kmajor) launch_layout<false, false, true>(a, grid, tm, tn, part, ldp, stream);
+    else if (!a.a_kmajor && a.b_kmajor) launch_layout<false, true, true>(a, grid, tm, tn, part, ldp, stream);
+    else if (a.a_kmajor && a.b_kmajor) launch_layout<true, true, true>(a, grid, tm, tn, part, ldp, stream);
+    else return BFP8_ERR_LAYOUT;
+  } else {
+    if (!a.a_kmajor && !a.b_kmajor) launch_layout<false, false, false>(a, grid, tm, tn, part, ldp, stream);
+    else if (!a.a_kmajor && a.b_kmajor) launch_layout<false, true, false>(a, grid, tm, tn, part, ldp, stream);
+    else if (a.a_kmajor && a.b_kmajor) launch_layout<true, true, false>(a, grid, tm, tn, part, ldp, stream);
+    else return BFP8_ERR_LAYOUT;
+  }
   if (S > 1) {
     const int64_t n = a.M * ((a.N + 3) / 4);
     splitk_reduce_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream>>>(

@@ -5,7 +5,10 @@
 // activation gradients use 1-D groups of 128 consecutive values along the
 // GEMM reduction dimension, weights 128x128 2-D blocks.  Scale = amax/448 and
 // the saturating round-to-nearest-even E4M3 cast are the readings stated in
-// include/bfp8.h.
+// include/bfp8.h.  The same section says the scales ran as powers of two on
+// the MXFP8 path; every kernel also takes that rule (RULE 1: the least power
+// of two covering amax/448, stored as an E8M0 byte), and the row / token
+// kernels the MXFP8 group length of 32 (Puro-2B tutorial, MXFP figure).
 //
 // All three kernels are HBM-bound (about 3 bytes moved per bf16 element and
 // a handful of VALU operations), so the design goal is wide coalesced loads,
@@ -69,18 +72,26 @@ __device__ __forceinline__ uint2 encode8(const float (&v)[8], float inv) {
   return r;
 }
 
+// Max over the lanes of one group: 16 lanes per 128-group, 4 per 32-group.
+template <int GROUP>
+__device__ __forceinline__ float group_lanes_max(float v) {
+  return GROUP == 128 ? row16_max(v) : quad_max(v);
+}
+
 // ---------------------------------------------------------------------------
-// K1: 1x128 groups along rows.  16 lanes own one group (8 elements each, one
-// 16-byte load for bf16); a 256-thread block covers 16 groups per unrolled
-// step and issues all UNROLL steps' loads before any reduction.
+// K1: groups along rows.  16 lanes own one 128-element chunk (8 elements
+// each, one 16-byte load for bf16) -- one group, or four 32-groups of four
+// lanes each; a 256-thread block covers 16 chunks per unrolled step and
+// issues all UNROLL steps' loads before any reduction.
 // ---------------------------------------------------------------------------
 constexpr int kActUnroll = 4;
 
-template <typename T>
-__global__ __launch_bounds__(256) void quantize_act_kernel(const T* __restrict__ x, int64_t ldx,
-                                                           uint8_t* __restrict__ q, int64_t ldq,
-                                                           float* __restrict__ s, uint32_t gpr,
-                                                           uint32_t n_groups) {
+template <typename T, int RULE, int GROUP>
+__global__ __launch_bounds__(256) void quantize_act_kernel(
+    const T* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+    typename ScaleRule<RULE>::type* __restrict__ s, uint32_t gpr, uint32_t n_groups) {
+  // gpr / n_groups count 128-element chunks; s holds gpr * (128 / GROUP)
+  // scales per row.
   const uint32_t lane16 = threadIdx.x & 15u;
   const uint32_t slot = threadIdx.x >> 4;  // 0..15: group within a step
   const uint32_t per_block = 16u * kActUnroll;
@@ -99,14 +110,17 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const T* __restrict__
 #pragma unroll
     for (int u = 0; u < kActUnroll; ++u) {
       const uint32_t g = base + u * 16u + slot;
-      const float amax = row16_max(absmax8(v[u]));
-      float sc, inv;
-      group_scale(amax, sc, inv);
+      const float amax = group_lanes_max<GROUP>(absmax8(v[u]));
+      float inv;
+      const auto sc = ScaleRule<RULE>::make(amax, inv);
       if (g < n_groups) {
         uint2 codes = encode8(v[u], inv);
         *reinterpret_cast<uint2*>(q + static_cast<int64_t>(row[u]) * ldq + gc[u] * kGroup +
                                   lane16 * 8u) = codes;
-        if (lane16 == 0) s[static_cast<int64_t>(row[u]) * gpr + gc[u]] = sc;
+        constexpr uint32_t kLanes = GROUP / 8;  // lanes per group
+        constexpr uint32_t kSub = kGroup / GROUP;
+        if (lane16 % kLanes == 0)
+          s[static_cast<int64_t>(row[u]) * gpr * kSub + gc[u] * kSub + lane16 / kLanes] = sc;
       }
     }
   }
@@ -115,19 +129,21 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const T* __restrict__
 // ---------------------------------------------------------------------------
 // K2: token-axis groups, transposed output.  A block owns 128 tokens x 64
 // channels: coalesced row loads into an fp32 LDS tile, then thread
-// (channel c, quarter p) walks 32 tokens of its channel, the four quarters
-// combine their amax through LDS, and each thread writes its 32 codes as two
-// 16-byte stores into row c of qt.
+// (channel c, quarter p) walks 32 tokens of its channel; for 128-token
+// groups the four quarters combine their amax through LDS (a 32-token group
+// is one quarter), and each thread writes its 32 codes as two 16-byte
+// stores into row c of qt.
 // ---------------------------------------------------------------------------
 constexpr int kTrTok = 128;
 constexpr int kTrCh = 64;
 constexpr int kTrLd = kTrCh + 4;  // padded fp32 row stride (16-byte aligned)
 
-template <typename T>
-__global__ __launch_bounds__(256) void quantize_act_t_kernel(const T* __restrict__ x, int64_t ldx,
-                                                             int64_t cols, uint8_t* __restrict__ qt,
-                                                             int64_t ldqt, float* __restrict__ st,
-                                                             int64_t n_tok_blocks) {
+template <typename T, int RULE, int GROUP>
+__global__ __launch_bounds__(256) void quantize_act_t_kernel(
+    const T* __restrict__ x, int64_t ldx, int64_t cols, uint8_t* __restrict__ qt, int64_t ldqt,
+    typename ScaleRule<RULE>::type* __restrict__ st, int64_t n_tok_blocks) {
+  // n_tok_blocks counts 128-token blocks; st rows hold n_tok_blocks *
+  // (128 / GROUP) scales.
   __shared__ __attribute__((aligned(16))) float tile[kTrTok * kTrLd];
   __shared__ float part[4][kTrCh];
   const int tid = threadIdx.x;
@@ -161,11 +177,14 @@ __global__ __launch_bounds__(256) void quantize_act_t_kernel(const T* __restrict
     v[i] = tile[(32 * p + i) * kTrLd + c];
     m = fmaxf(m, fabsf(v[i]));
   }
-  part[p][c] = m;
-  __syncthreads();
-  const float amax = fmaxf(fmaxf(part[0][c], part[1][c]), fmaxf(part[2][c], part[3][c]));
-  float sc, inv;
-  group_scale(amax, sc, inv);
+  float amax = m;
+  if (GROUP == 128) {
+    part[p][c] = m;
+    __syncthreads();
+    amax = fmaxf(fmaxf(part[0][c], part[1][c]), fmaxf(part[2][c], part[3][c]));
+  }
+  float inv;
+  const auto sc = ScaleRule<RULE>::make(amax, inv);
   if (c0 + c < cols) {
     uint32_t w[8];
 #pragma unroll
@@ -174,7 +193,11 @@ __global__ __launch_bounds__(256) void quantize_act_t_kernel(const T* __restrict
     uint4* dst = reinterpret_cast<uint4*>(qt + (c0 + c) * ldqt + m0 + 32 * p);
     dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
     dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    if (p == 0) st[(c0 + c) * n_tok_blocks + tb] = sc;
+    if (GROUP == 128) {
+      if (p == 0) st[(c0 + c) * n_tok_blocks + tb] = sc;
+    } else {
+      st[(c0 + c) * n_tok_blocks * 4 + tb * 4 + p] = sc;
+    }
   }
 }
 
@@ -183,12 +206,10 @@ __global__ __launch_bounds__(256) void quantize_act_t_kernel(const T* __restrict
 // elements in registers between the block-wide amax and the encode; partial
 // edge blocks mask their missing elements to zero and store byte-wise.
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void quantize_weight_kernel(const T* __restrict__ w, int64_t ldw,
-                                                              int64_t rows, int64_t cols,
-                                                              uint8_t* __restrict__ q, int64_t ldq,
-                                                              float* __restrict__ s,
-                                                              int64_t n_col_blocks) {
+template <typename T, int RULE>
+__global__ __launch_bounds__(256) void quantize_weight_kernel(
+    const T* __restrict__ w, int64_t ldw, int64_t rows, int64_t cols, uint8_t* __restrict__ q,
+    int64_t ldq, typename ScaleRule<RULE>::type* __restrict__ s, int64_t n_col_blocks) {
   __shared__ float red[4];
   const int tid = threadIdx.x;
   const int64_t bm = blockIdx.y, bk = blockIdx.x;
@@ -212,8 +233,8 @@ __global__ __launch_bounds__(256) void quantize_weight_kernel(const T* __restric
   if ((tid & 63) == 0) red[tid >> 6] = m;
   __syncthreads();
   const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float sc, inv;
-  group_scale(amax, sc, inv);
+  float inv;
+  const auto sc = ScaleRule<RULE>::make(amax, inv);
   if (tid == 0) s[bm * n_col_blocks + bk] = sc;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -234,8 +255,8 @@ __global__ __launch_bounds__(256) void quantize_weight_kernel(const T* __restric
 
 // ---------------------------------------------------------------------------
 // K1+K2 fused: one read of a 128-token x 128-channel tile emits both the
-// row-grouped codes (1x128 along channels: the fprop / dgrad operand) and
-// the token-grouped codes written transposed (1x128 along tokens: the wgrad
+// row-grouped codes (groups along channels: the fprop / dgrad operand) and
+// the token-grouped codes written transposed (groups along tokens: the wgrad
 // operand).  Phase 1 works from registers (16 lanes per row group, as K1)
 // and parks the raw tile in LDS; phase 2 walks columns of the LDS tile (two
 // channels per thread, a quarter of the tokens each) as K2 does.  Both
@@ -252,11 +273,12 @@ struct DualTile<float> {
   static constexpr int kLd = 128 + 4;
 };
 
-template <typename T>
+template <typename T, int RULE, int GROUP>
 __global__ __launch_bounds__(256) void quantize_dual_kernel(
     const T* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
-    float* __restrict__ s, uint8_t* __restrict__ qt, int64_t ldqt, float* __restrict__ st,
-    int64_t n_ch_blocks, int64_t n_tok_blocks) {
+    typename ScaleRule<RULE>::type* __restrict__ s, uint8_t* __restrict__ qt, int64_t ldqt,
+    typename ScaleRule<RULE>::type* __restrict__ st, int64_t n_ch_blocks, int64_t n_tok_blocks) {
+  constexpr int kSub = kGroup / GROUP;  // groups per 128 along either axis
   constexpr int kLd = DualTile<T>::kLd;
   __shared__ __attribute__((aligned(16))) T tile[128 * kLd];
   __shared__ float part[4][128];
@@ -275,11 +297,12 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int r = rsub + 16 * u;
-    const float amax = row16_max(absmax8(v[u]));
-    float sc, inv;
-    group_scale(amax, sc, inv);
+    const float amax = group_lanes_max<GROUP>(absmax8(v[u]));
+    float inv;
+    const auto sc = ScaleRule<RULE>::make(amax, inv);
     *reinterpret_cast<uint2*>(q + (m0 + r) * ldq + c0 + lane16 * 8) = encode8(v[u], inv);
-    if (lane16 == 0) s[(m0 + r) * n_ch_blocks + cb] = sc;
+    if (lane16 % (GROUP / 8) == 0)
+      s[(m0 + r) * n_ch_blocks * kSub + cb * kSub + lane16 / (GROUP / 8)] = sc;
     T* dst = tile + r * kLd + lane16 * 8;
     if (sizeof(T) == 2) {
       uint32_t w[4];
@@ -313,16 +336,18 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(
     ma = fmaxf(ma, fabsf(a[i]));
     mb = fmaxf(mb, fabsf(b[i]));
   }
-  part[p][2 * cp] = ma;
-  part[p][2 * cp + 1] = mb;
-  __syncthreads();
-  const float amax_a = fmaxf(fmaxf(part[0][2 * cp], part[1][2 * cp]),
-                             fmaxf(part[2][2 * cp], part[3][2 * cp]));
-  const float amax_b = fmaxf(fmaxf(part[0][2 * cp + 1], part[1][2 * cp + 1]),
-                             fmaxf(part[2][2 * cp + 1], part[3][2 * cp + 1]));
-  float sa, inva, sb, invb;
-  group_scale(amax_a, sa, inva);
-  group_scale(amax_b, sb, invb);
+  float amax_a = ma, amax_b = mb;
+  if (GROUP == 128) {
+    part[p][2 * cp] = ma;
+    part[p][2 * cp + 1] = mb;
+    __syncthreads();
+    amax_a = fmaxf(fmaxf(part[0][2 * cp], part[1][2 * cp]), fmaxf(part[2][2 * cp], part[3][2 * cp]));
+    amax_b = fmaxf(fmaxf(part[0][2 * cp + 1], part[1][2 * cp + 1]),
+                   fmaxf(part[2][2 * cp + 1], part[3][2 * cp + 1]));
+  }
+  float inva, invb;
+  const auto sa = ScaleRule<RULE>::make(amax_a, inva);
+  const auto sb = ScaleRule<RULE>::make(amax_b, invb);
   uint32_t wa[8], wb[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -335,9 +360,14 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(
   da[1] = make_uint4(wa[4], wa[5], wa[6], wa[7]);
   db[0] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
   db[1] = make_uint4(wb[4], wb[5], wb[6], wb[7]);
-  if (p == 0) {
-    st[(c0 + 2 * cp) * n_tok_blocks + tb] = sa;
-    st[(c0 + 2 * cp + 1) * n_tok_blocks + tb] = sb;
+  if (GROUP == 128) {
+    if (p == 0) {
+      st[(c0 + 2 * cp) * n_tok_blocks + tb] = sa;
+      st[(c0 + 2 * cp + 1) * n_tok_blocks + tb] = sb;
+    }
+  } else {
+    st[(c0 + 2 * cp) * n_tok_blocks * kSub + tb * kSub + p] = sa;
+    st[(c0 + 2 * cp + 1) * n_tok_blocks * kSub + tb * kSub + p] = sb;
   }
 }
 
@@ -347,70 +377,81 @@ inline bfp8_status last_launch_status() {
 
 }  // namespace
 
+// Instantiate a kernel for the (input type, rule, group) triple chosen at
+// run time.  Valid triples: rule 0 with group 128; rule 1 with 32 or 128.
+#define BFP8_DISPATCH(KERNEL_CALL)                                           \
+  do {                                                                       \
+    if (dt == BFP8_IN_BF16) {                                                \
+      typedef uint16_t T;                                                    \
+      if (rule == 0) { constexpr int R = 0, G = 128; KERNEL_CALL; }          \
+      else if (group == 128) { constexpr int R = 1, G = 128; KERNEL_CALL; }  \
+      else { constexpr int R = 1, G = 32; KERNEL_CALL; }                     \
+    } else {                                                                 \
+      typedef float T;                                                       \
+      if (rule == 0) { constexpr int R = 0, G = 128; KERNEL_CALL; }          \
+      else if (group == 128) { constexpr int R = 1, G = 128; KERNEL_CALL; }  \
+      else { constexpr int R = 1, G = 32; KERNEL_CALL; }                     \
+    }                                                                        \
+  } while (0)
+
 bfp8_status launch_quantize_act(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
-                                int64_t ldx, uint8_t* q, int64_t ldq, float* s,
-                                hipStream_t stream) {
+                                int64_t ldx, int rule, int group, uint8_t* q, int64_t ldq,
+                                void* s, hipStream_t stream) {
   const int64_t gpr = cols / kGroup;
   const int64_t n_groups = rows * gpr;
   if (n_groups == 0) return BFP8_OK;
   const int64_t per_block = 16 * kActUnroll;
   int64_t blocks = (n_groups + per_block - 1) / per_block;
   if (blocks > 16384) blocks = 16384;
-  if (dt == BFP8_IN_BF16)
-    quantize_act_kernel<uint16_t><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(
-        static_cast<const uint16_t*>(x), ldx, q, ldq, s, static_cast<uint32_t>(gpr),
-        static_cast<uint32_t>(n_groups));
-  else
-    quantize_act_kernel<float><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(
-        static_cast<const float*>(x), ldx, q, ldq, s, static_cast<uint32_t>(gpr),
-        static_cast<uint32_t>(n_groups));
+  BFP8_DISPATCH((quantize_act_kernel<T, R, G>
+                 <<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(
+                     static_cast<const T*>(x), ldx, q, ldq,
+                     static_cast<typename ScaleRule<R>::type*>(s), static_cast<uint32_t>(gpr),
+                     static_cast<uint32_t>(n_groups))));
   return last_launch_status();
 }
 
 bfp8_status launch_quantize_act_transposed(const void* x, bfp8_in_dtype dt, int64_t rows,
-                                           int64_t cols, int64_t ldx, uint8_t* qt,
-                                           int64_t ldqt, float* st, hipStream_t stream) {
+                                           int64_t cols, int64_t ldx, int rule, int group,
+                                           uint8_t* qt, int64_t ldqt, void* st,
+                                           hipStream_t stream) {
   if (rows == 0 || cols == 0) return BFP8_OK;
   const int64_t tok_blocks = rows / kTrTok;
   dim3 grid(static_cast<unsigned>((cols + kTrCh - 1) / kTrCh), static_cast<unsigned>(tok_blocks));
-  if (dt == BFP8_IN_BF16)
-    quantize_act_t_kernel<uint16_t><<<grid, dim3(256), 0, stream>>>(
-        static_cast<const uint16_t*>(x), ldx, cols, qt, ldqt, st, tok_blocks);
-  else
-    quantize_act_t_kernel<float><<<grid, dim3(256), 0, stream>>>(
-        static_cast<const float*>(x), ldx, cols, qt, ldqt, st, tok_blocks);
+  BFP8_DISPATCH((quantize_act_t_kernel<T, R, G><<<grid, dim3(256), 0, stream>>>(
+      static_cast<const T*>(x), ldx, cols, qt, ldqt,
+      static_cast<typename ScaleRule<R>::type*>(st), tok_blocks)));
   return last_launch_status();
 }
 
 bfp8_status launch_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
-                                     int64_t ldx, uint8_t* q, int64_t ldq, float* s, uint8_t* qt,
-                                     int64_t ldqt, float* st, hipStream_t stream) {
+                                     int64_t ldx, int rule, int group, uint8_t* q, int64_t ldq,
+                                     void* s, uint8_t* qt, int64_t ldqt, void* st,
+                                     hipStream_t stream) {
   if (rows == 0 || cols == 0) return BFP8_OK;
   const int64_t ch_blocks = cols / kGroup, tok_blocks = rows / kGroup;
   dim3 grid(static_cast<unsigned>(ch_blocks), static_cast<unsigned>(tok_blocks));
-  if (dt == BFP8_IN_BF16)
-    quantize_dual_kernel<uint16_t><<<grid, dim3(256), 0, stream>>>(
-        static_cast<const uint16_t*>(x), ldx, q, ldq, s, qt, ldqt, st, ch_blocks, tok_blocks);
-  else
-    quantize_dual_kernel<float><<<grid, dim3(256), 0, stream>>>(
-        static_cast<const float*>(x), ldx, q, ldq, s, qt, ldqt, st, ch_blocks, tok_blocks);
+  BFP8_DISPATCH((quantize_dual_kernel<T, R, G><<<grid, dim3(256), 0, stream>>>(
+      static_cast<const T*>(x), ldx, q, ldq, static_cast<typename ScaleRule<R>::type*>(s), qt,
+      ldqt, static_cast<typename ScaleRule<R>::type*>(st), ch_blocks, tok_blocks)));
   return last_launch_status();
 }
 
 bfp8_status launch_quantize_weight(const void* w, bfp8_in_dtype dt, int64_t rows, int64_t cols,
-                                   int64_t ldw, uint8_t* q, int64_t ldq, float* s,
+                                   int64_t ldw, int rule, uint8_t* q, int64_t ldq, void* s,
                                    hipStream_t stream) {
   if (rows == 0 || cols == 0) return BFP8_OK;
   const int64_t rb = (rows + kGroup - 1) / kGroup;
   const int64_t cb = (cols + kGroup - 1) / kGroup;
   dim3 grid(static_cast<unsigned>(cb), static_cast<unsigned>(rb));
-  if (dt == BFP8_IN_BF16)
-    quantize_weight_kernel<uint16_t><<<grid, dim3(256), 0, stream>>>(
-        static_cast<const uint16_t*>(w), ldw, rows, cols, q, ldq, s, cb);
-  else
-    quantize_weight_kernel<float><<<grid, dim3(256), 0, stream>>>(
-        static_cast<const float*>(w), ldw, rows, cols, q, ldq, s, cb);
+  const int group = 128;
+  BFP8_DISPATCH((quantize_weight_kernel<T, R><<<grid, dim3(256), 0, stream>>>(
+      static_cast<const T*>(w), ldw, rows, cols, q, ldq,
+      static_cast<typename ScaleRule<R>::type*>(s), cb)));
+  (void)group;
   return last_launch_status();
 }
+
+#undef BFP8_DISPATCH
 
 }  // namespace bfp8

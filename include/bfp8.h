@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define BFP8_ABI_VERSION 1
+#define BFP8_ABI_VERSION 2
 
 typedef enum {
   BFP8_OK = 0,
@@ -89,7 +89,11 @@ typedef enum {
 
 typedef enum { BFP8_IN_BF16 = 0, BFP8_IN_F32 = 1 } bfp8_in_dtype;
 typedef enum { BFP8_NN = 0, BFP8_NT = 1, BFP8_TN = 2 } bfp8_layout;
-typedef enum { BFP8_SCALE_1x128 = 0, BFP8_SCALE_128x128 = 1 } bfp8_scale_mode;
+typedef enum {
+  BFP8_SCALE_1x128 = 0,   /* 1 x 128 groups along K                          */
+  BFP8_SCALE_128x128 = 1, /* 128 x 128 blocks                                */
+  BFP8_SCALE_1x32 = 2     /* 1 x 32 groups along K (E8M0 scales only: MXFP8) */
+} bfp8_scale_mode;
 
 /*
  * Activation / activation-gradient quantiser: 1x128 groups along each row.
@@ -175,9 +179,67 @@ bfp8_status bfp8_gemm(bfp8_layout layout, int64_t M, int64_t N, int64_t K, const
                       int64_t ldc, void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
-/* Workspace bytes that let bfp8_gemm use its split-K plan for this problem
- * (0 when the problem runs unsplit).  Returns (size_t)-1 for an invalid
- * layout, scale mode or size. */
+/*
+ * ---- Power-of-two (E8M0) scales: the MXFP8 form of the same recipe --------
+ * (Puro-2B translation, section 3.2: on SM120 every logical block scale was
+ * constrained to a power of two and ran on the native MXFP8 path; Puro-2B
+ * tutorial, MXFP figure: MXFP8 shares one scale per 32 elements.)
+ *
+ * Scale rule (a reading): e = the least integer with 448 * 2^e >= amax of the
+ * group, clamped to [-127, 127] (0 for an all-zero group); the scale is the
+ * E8M0 byte e + 127 (value 2^(byte - 127)); codes are the round-to-nearest-
+ * even E4M3 cast of x * 2^-e (no element saturates).  Groups whose amax is
+ * below 2^-126 and non-finite inputs are outside the contract.
+ * Scale tensors are dense row-major uint8 arrays with the same shapes as the
+ * float32 scale tensors above, the grouped axis divided by the group length
+ * (32 or 128).  Errors and ownership as above; `group` other than 32 or 128
+ * returns BFP8_ERR_SCALE_MODE.
+ */
+
+/* Rows quantised in groups of `group` (32 or 128) consecutive values:
+ * q [rows][ldq], s [rows][cols/group].  cols % 128 == 0. */
+bfp8_status bfp8_quantize_mx_act(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
+                                 int64_t ldx, int group, uint8_t* q, int64_t ldq, uint8_t* s,
+                                 hipStream_t stream);
+
+/* Token-axis groups of `group` tokens, written transposed:
+ * qt [cols][ldqt], st [cols][rows/group].  rows % 128 == 0. */
+bfp8_status bfp8_quantize_mx_act_transposed(const void* x, bfp8_in_dtype dt, int64_t rows,
+                                            int64_t cols, int64_t ldx, int group, uint8_t* qt,
+                                            int64_t ldqt, uint8_t* st, hipStream_t stream);
+
+/* Both of the above from one read (rows and cols % 128 == 0). */
+bfp8_status bfp8_quantize_mx_act_dual(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
+                                      int64_t ldx, int group, uint8_t* q, int64_t ldq, uint8_t* s,
+                                      uint8_t* qt, int64_t ldqt, uint8_t* st, hipStream_t stream);
+
+/* 128x128 weight blocks: q [rows][ldq], s [ceil(rows/128)][ceil(cols/128)]. */
+bfp8_status bfp8_quantize_mx_weight(const void* w, bfp8_in_dtype dt, int64_t rows, int64_t cols,
+                                    int64_t ldw, uint8_t* q, int64_t ldq, uint8_t* s,
+                                    hipStream_t stream);
+
+/*
+ * GEMM on E8M0-scaled operands: C[m][n] = sum over K of dec(A) * dec(B) with
+ * each product scaled by its two groups' powers of two, accumulated in fp32,
+ * rounded to bf16 (RNE).  On gfx950 the scales ride in the matrix-core
+ * instruction itself (v_mfma_scale_f32_16x16x128_f8f6f4), so the exact
+ * power-of-two scaling replaces the per-128-K promotion of bfp8_gemm.
+ * Same layouts, shapes, leading-dimension and workspace rules as bfp8_gemm;
+ * scale tensors are uint8 E8M0 in the layouts of the table at the top of
+ * this file, with BFP8_SCALE_1x32 as [rows][K/32] (K-contiguous operands
+ * only: A of NN/NT, B of NT; otherwise BFP8_ERR_SCALE_MODE).  Each scale
+ * tensor must be readable up to the next multiple of 4 bytes past its end
+ * (scales are fetched as aligned 32-bit words).
+ */
+bfp8_status bfp8_gemm_mx(bfp8_layout layout, int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                         int64_t lda, const uint8_t* sA, bfp8_scale_mode modeA, const uint8_t* B,
+                         int64_t ldb, const uint8_t* sB, bfp8_scale_mode modeB, void* C,
+                         int64_t ldc, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/* Workspace bytes that let bfp8_gemm (or bfp8_gemm_mx) use its split-K plan
+ * for this problem (0 when the problem runs unsplit).  Returns (size_t)-1 for
+ * an invalid layout, scale mode or size. */
 size_t bfp8_gemm_workspace_bytes(bfp8_layout layout, bfp8_scale_mode modeA,
                                  bfp8_scale_mode modeB, int64_t M, int64_t N, int64_t K);
 

@@ -36,7 +36,9 @@ def test_header_declares_the_boundary():
     assert names == sorted(["bfp8_quantize_act", "bfp8_quantize_act_transposed",
                             "bfp8_quantize_act_dual",
                             "bfp8_quantize_weight", "bfp8_gemm", "bfp8_gemm_workspace_bytes",
-                            "bfp8_status_str", "bfp8_abi_version"])
+                            "bfp8_quantize_mx_act", "bfp8_quantize_mx_act_transposed",
+                            "bfp8_quantize_mx_act_dual", "bfp8_quantize_mx_weight",
+                            "bfp8_gemm_mx", "bfp8_status_str", "bfp8_abi_version"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -45,7 +47,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.bfp8_abi_version() == 1
+    assert L.bfp8_abi_version() == 2
     for code in range(9):
         assert len(L.bfp8_status_str(code)) > 0
     assert L.bfp8_status_str(99) == b"unknown status"
@@ -119,7 +121,8 @@ def gemm(L, layout=1, M=256, N=384, K=512, A=P, lda=512, sA=P, ma=0, B=P, ldb=51
 
 def test_gemm_errors(L):
     assert gemm(L, layout=3) == LAYOUT
-    assert gemm(L, ma=2) == SMODE
+    assert gemm(L, ma=2) == SMODE                 # 1x32 needs E8M0 scales (bfp8_gemm_mx)
+    assert gemm(L, ma=3) == SMODE
     assert gemm(L, mb=-1) == SMODE
     assert gemm(L, K=500) == SHAPE
     assert gemm(L, M=-1) == SHAPE
@@ -160,3 +163,48 @@ def test_gemm_rejects_misaligned_workspace(L):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         bfp8.lib(str(tmp_path / "missing.so"))
+
+
+# ---- power-of-two (E8M0) entry points ---------------------------------------
+
+def test_quantize_mx_errors(L):
+    f = lambda **k: L.bfp8_quantize_mx_act(
+        k.get("x", P), k.get("dt", 0), k.get("rows", 256), k.get("cols", 512),
+        k.get("ldx", 512), k.get("group", 32), k.get("q", P), k.get("ldq", 512), k.get("s", P), None)
+    assert f(group=64) == SMODE
+    assert f(group=0) == SMODE
+    assert f(cols=500, ldx=512) == SHAPE
+    assert f(s=None) == NULL
+    assert f(x=P + 8) == ALIGN
+    assert f(dt=5) == DTYPE
+    assert f(rows=0, x=None, q=None, s=None) == OK
+    t = lambda **k: L.bfp8_quantize_mx_act_transposed(
+        k.get("x", P), 0, k.get("rows", 256), 384, 384, k.get("group", 128), P, 256, P, None)
+    assert t(group=16) == SMODE
+    assert t(rows=100) == SHAPE
+    d = lambda **k: L.bfp8_quantize_mx_act_dual(
+        P, 0, k.get("rows", 256), 384, 384, k.get("group", 32), P, 384, P, k.get("qt", P), 256,
+        P, None)
+    assert d(group=256) == SMODE
+    assert d(qt=None) == NULL
+    w = lambda **k: L.bfp8_quantize_mx_weight(P, k.get("dt", 0), 300, 200, 208, P, 208,
+                                              k.get("s", P), None)
+    assert w(s=None) == NULL
+    assert w(dt=9) == DTYPE
+
+
+def gemm_mx(L, layout=1, M=256, N=384, K=512, A=P, lda=512, sA=P, ma=0, B=P, ldb=512, sB=P,
+            mb=1, C=P, ldc=384, ws=None, wsb=0):
+    return L.bfp8_gemm_mx(layout, M, N, K, A, lda, sA, ma, B, ldb, sB, mb, C, ldc, ws, wsb, None)
+
+
+def test_gemm_mx_errors(L):
+    assert gemm_mx(L, layout=4) == LAYOUT
+    assert gemm_mx(L, ma=3) == SMODE
+    assert gemm_mx(L, layout=2, ma=2, lda=256) == SMODE   # 1x32 A must be K-contiguous
+    assert gemm_mx(L, layout=0, mb=2, ldb=384) == SMODE   # 1x32 B must be K-contiguous
+    assert gemm_mx(L, K=200) == SHAPE
+    assert gemm_mx(L, sA=None) == NULL
+    assert gemm_mx(L, sB=P + 1) == ALIGN
+    assert gemm_mx(L, M=0, A=None, B=None, C=None) == OK
+    assert L.bfp8_gemm_workspace_bytes(1, 2, 2, 8192, 4096, 2048) == 0

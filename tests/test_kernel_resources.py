@@ -1,8 +1,9 @@
 """Compile the GEMM for gfx950 and check the hot kernels' register use.
 
 A VGPR spill in the GEMM main loop costs ~8x (scratch traffic per MFMA); the
-kernels the training pass launches (fprop NT act x block, dgrad NN act x
-block, wgrad NT act x act) must compile without spills.  CPU only (hipcc
+kernels the training passes launch (fprop NT act x block, dgrad NN act x
+block, wgrad NT act x act, with float32 or power-of-two scales, and the
+1x32 MXFP8 NT kernel) must compile without spills.  CPU only (hipcc
 cross-compiles)."""
 import os
 import re
@@ -14,9 +15,14 @@ import pytest
 from blockwise_fp8_gemm_bfp8_amd import build as bfp8_build
 
 HOT = {
-    "fprop NT act x block": r"gemm_kernelILb0ELb0ELi0ELi1E",
-    "dgrad NN act x block": r"gemm_kernelILb0ELb1ELi0ELi1E",
-    "wgrad NT act x act": r"gemm_kernelILb0ELb0ELi0ELi0E",
+    "fprop NT act x block": r"gemm_kernelILb0ELb0ELi0ELi1ELb0E",
+    "dgrad NN act x block": r"gemm_kernelILb0ELb1ELi0ELi1ELb0E",
+    "wgrad NT act x act": r"gemm_kernelILb0ELb0ELi0ELi0ELb0E",
+    # power-of-two (E8M0) scales, hardware-scaled MFMA
+    "mx fprop NT act x block": r"gemm_kernelILb0ELb0ELi0ELi1ELb1E",
+    "mx dgrad NN act x block": r"gemm_kernelILb0ELb1ELi0ELi1ELb1E",
+    "mx wgrad NT act x act": r"gemm_kernelILb0ELb0ELi0ELi0ELb1E",
+    "mx32 NT 1x32 x 1x32": r"gemm_kernelILb0ELb0ELi2ELi2ELb1E",
 }
 
 

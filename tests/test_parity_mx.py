@@ -1,0 +1,255 @@
+"""GPU parity of the power-of-two (E8M0) path against the CPU oracle (oracle/mx.py).
+
+Quantisers: bit-exact codes and bit-exact scale bytes, groups of 32 and 128.
+GEMM: rel_error <= 1e-2 against the float64 product of the dequantised
+operands (same reading of the tolerance as tests/test_parity_gemm.py), and
+bit-exact bf16 where every fp32 step is exact (integer-valued codes).
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pins_mx
+from workloads import make_inputs, to_numpy_input
+
+pytestmark = pytest.mark.gpu
+
+import blockwise_fp8_gemm_bfp8_amd as bfp8  # noqa: E402
+
+TOL = 1e-2
+
+
+def dev(t):
+    """Device copy whose rows start 16-byte aligned (padded leading dim)."""
+    if isinstance(t, np.ndarray):
+        t = torch.from_numpy(np.ascontiguousarray(t))
+    R, C = t.shape
+    per = 16 // t.element_size()
+    ld = max(-(-C // per) * per, per)
+    buf = torch.zeros((R, ld), dtype=t.dtype, device="cuda")
+    buf[:, :C] = t.to("cuda")
+    return buf[:, :C]
+
+
+def scales_dev(s):
+    """Dense uint8 scale tensor with 4 readable bytes past its end."""
+    s = np.ascontiguousarray(s, dtype=np.uint8)
+    buf = torch.zeros((s.size + 4,), dtype=torch.uint8, device="cuda")
+    buf[:s.size] = torch.from_numpy(s.reshape(-1)).cuda()
+    return buf[:s.size].view(*s.shape)
+
+
+def same(got_q, got_s, exp_q, exp_s, what=""):
+    gq, gs = got_q.cpu().numpy(), got_s.cpu().numpy()
+    bad = np.argwhere(gq != exp_q)
+    assert bad.size == 0, f"{what}: {len(bad)} byte mismatches, first {bad[:5].tolist()}"
+    assert gs.shape == exp_s.shape, (gs.shape, exp_s.shape)
+    bad = np.argwhere(gs != exp_s)
+    assert bad.size == 0, f"{what}: {len(bad)} scale mismatches, first {bad[:5].tolist()}"
+
+
+def rand(shape, seed, dtype, std=1.0, heavy=False):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(shape, generator=g) * std
+    if heavy:
+        x = x * torch.exp(torch.randn(shape, generator=g) * 2)
+    return x.to(dtype)
+
+
+def boundary_groups(group):
+    """Groups whose amax sits on / next to 448 * 2**k (where the exponent
+    steps), plus zero, signed-zero, tiny and huge groups."""
+    rows = []
+    rng = np.random.default_rng(group)
+    for k in (-100, -20, -7, -1, 0, 1, 9, 60, 110):
+        base = np.float32(448.0 * 2.0 ** k)
+        for amax in (base, np.nextafter(base, np.float32(np.inf)), np.nextafter(base, np.float32(0)),
+                     np.float32(base * 0.5), np.float32(base * 0.75)):
+            r = (rng.uniform(-1, 1, group) * amax).astype(np.float32)
+            r[int(rng.integers(group))] = -amax
+            rows.append(r)
+    rows.append(np.zeros(group, np.float32))
+    z = np.zeros(group, np.float32); z[::2] = -0.0; rows.append(z)
+    rows.append((np.linspace(-1, 1, group) * 3e38).astype(np.float32))
+    return np.concatenate(rows).reshape(-1, 128).astype(np.float32)
+
+
+# ---------------------------------------------------------------- quantisers
+
+
+@pytest.mark.parametrize("group", [32, 128])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("rows,cols", [(1, 128), (3, 384), (777, 2048), (256, 6144)])
+def test_mx_act(group, dtype, rows, cols):
+    x = rand((rows, cols), rows * 3 + cols + group, dtype, 2.0, heavy=True)
+    q, s = bfp8.quantize_mx_act(dev(x), group)
+    eq, es = oracle.quantize_mx_act(to_numpy_input(x), group)
+    same(q, s, eq, es, f"mx act {group} {rows}x{cols} {dtype}")
+
+
+@pytest.mark.parametrize("group", [32, 128])
+def test_mx_act_exponent_boundaries(group):
+    x = boundary_groups(group)
+    q, s = bfp8.quantize_mx_act(torch.from_numpy(x).cuda(), group)
+    eq, es = oracle.quantize_mx_act(x, group)
+    same(q, s, eq, es, f"boundaries {group}")
+
+
+@pytest.mark.parametrize("group", [32, 128])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("rows,cols", [(128, 1), (128, 100), (384, 384), (1024, 2100)])
+def test_mx_act_transposed(group, dtype, rows, cols):
+    x = rand((rows, cols), rows + cols * 5 + group, dtype, 0.5, heavy=True)
+    qt, st = bfp8.quantize_mx_act_transposed(dev(x), group)
+    eq, es = oracle.quantize_mx_act_transposed(to_numpy_input(x), group)
+    same(qt, st, eq, es, f"mx transposed {group} {rows}x{cols}")
+
+
+@pytest.mark.parametrize("group", [32, 128])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("rows,cols", [(128, 128), (384, 256), (1024, 2048)])
+def test_mx_act_dual(group, dtype, rows, cols):
+    x = rand((rows, cols), rows * 11 + cols + group, dtype, 1.0, heavy=True)
+    q, s, qt, st = bfp8.quantize_mx_act_dual(dev(x), group)
+    xn = to_numpy_input(x)
+    eq, es = oracle.quantize_mx_act(xn, group)
+    eqt, est = oracle.quantize_mx_act_transposed(xn, group)
+    same(q, s, eq, es, "dual rows")
+    same(qt, st, eqt, est, "dual tokens")
+
+
+def test_mx_dual_boundaries():
+    b = boundary_groups(32)                       # [n][128] rows of boundary groups
+    x = np.ascontiguousarray(np.tile(b, (-(-128 // b.shape[0]), 2))[:128])  # [128][256]
+    x[:, 128:] = x[::-1, 128:].copy()             # different token groups in the right half
+    for group in (32, 128):
+        q, s, qt, st = bfp8.quantize_mx_act_dual(torch.from_numpy(x).cuda(), group)
+        eq, es = oracle.quantize_mx_act(x, group)
+        eqt, est = oracle.quantize_mx_act_transposed(x, group)
+        same(q, s, eq, es, f"dual boundary rows {group}")
+        same(qt, st, eqt, est, f"dual boundary tokens {group}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("rows,cols", [(128, 128), (300, 200), (2048, 6144)])
+def test_mx_weight(dtype, rows, cols):
+    w = rand((rows, cols), rows + cols, dtype, 0.02, heavy=True)
+    q, s = bfp8.quantize_mx_weight(dev(w))
+    eq, es = oracle.quantize_mx_weight(to_numpy_input(w))
+    same(q, s, eq, es, f"mx weight {rows}x{cols}")
+
+
+# ---------------------------------------------------------------- GEMM
+
+
+def run_mx(layout, qa, sa, ma, qb, sb, mb, **kw):
+    C = bfp8.gemm_mx(layout, dev(qa), scales_dev(sa), dev(qb), scales_dev(sb), ma, mb, **kw)
+    torch.cuda.synchronize()
+    return C
+
+
+def ref_mx(layout, qa, sa, ma, qb, sb, mb):
+    return oracle.gemm_mx_ref(layout, qa, sa, ma, qb, sb, mb)
+
+
+MX_CASES = [("NT", "act", "block"), ("NT", "act", "act"), ("NT", "mx32", "mx32"),
+            ("NT", "mx32", "block"), ("NT", "block", "mx32"), ("NT", "block", "block"),
+            ("NN", "act", "block"), ("NN", "mx32", "block"), ("NN", "act", "act"),
+            ("TN", "act", "act"), ("TN", "block", "block")]
+
+
+@pytest.mark.parametrize("layout,ma,mb", MX_CASES)
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (300, 520, 640), (513, 129, 384)])
+def test_gemm_mx_random(layout, ma, mb, M, N, K):
+    rng = np.random.default_rng(M + 3 * N + 7 * K + len(ma) * 13 + len(mb))
+    qa, sa, qb, sb = pins_mx.random_mx_operands(rng, layout, ma, mb, M, N, K)
+    R = ref_mx(layout, qa, sa, ma, qb, sb, mb)
+    C = run_mx(layout, qa, sa, ma, qb, sb, mb)
+    err = oracle.rel_error(C.float().cpu().numpy(), R)
+    assert err <= TOL, (layout, ma, mb, M, N, K, err)
+
+
+def integer_mx_operands(rng, layout, ma, mb, M, N, K):
+    """Codes decoding to integers in [-8, 8] and E8M0 scales in 2**[-2, 2]."""
+    qa, sa, qb, sb = pins_mx.random_mx_operands(rng, layout, ma, mb, M, N, K)
+    dec = oracle.e4m3_decode(np.arange(256, dtype=np.uint8))
+    ints = np.array([c for c in range(256) if np.isfinite(dec[c]) and float(dec[c]).is_integer()
+                     and abs(dec[c]) <= 8], np.uint8)
+    qa = rng.choice(ints, qa.shape).astype(np.uint8)
+    qb = rng.choice(ints, qb.shape).astype(np.uint8)
+    sa = rng.integers(125, 130, sa.shape).astype(np.uint8)
+    sb = rng.integers(125, 130, sb.shape).astype(np.uint8)
+    return qa, sa, qb, sb
+
+
+@pytest.mark.parametrize("layout,ma,mb", MX_CASES)
+def test_gemm_mx_integer_exact_bitwise(layout, ma, mb):
+    rng = np.random.default_rng(21)
+    M, N, K = 512, 384, 512
+    qa, sa, qb, sb = integer_mx_operands(rng, layout, ma, mb, M, N, K)
+    R = ref_mx(layout, qa, sa, ma, qb, sb, mb)
+    exp = torch.from_numpy(R).float().to(torch.bfloat16)
+    got = run_mx(layout, qa, sa, ma, qb, sb, mb).cpu()
+    bad = (got.view(torch.int16) != exp.view(torch.int16)).nonzero()
+    assert bad.numel() == 0, (layout, ma, mb, bad[:5].tolist())
+
+
+@pytest.mark.parametrize("M,N,K,ma,mb", [(512, 256, 16384, "act", "act"),
+                                         (2048, 2048, 16384, "mx32", "mx32")])
+def test_gemm_mx_split_k(M, N, K, ma, mb):
+    rng = np.random.default_rng(M + N)
+    qa, sa, qb, sb = pins_mx.random_mx_operands(rng, "NT", ma, mb, M, N, K)
+    assert bfp8.gemm_workspace_bytes("NT", ma, mb, M, N, K) > 0
+    R = ref_mx("NT", qa, sa, ma, qb, sb, mb)
+    split = run_mx("NT", qa, sa, ma, qb, sb, mb)
+    unsplit = run_mx("NT", qa, sa, ma, qb, sb, mb, split_k=False)
+    assert oracle.rel_error(split.float().cpu().numpy(), R) <= TOL
+    assert oracle.rel_error(unsplit.float().cpu().numpy(), R) <= TOL
+
+
+@pytest.mark.parametrize("group", [32, 128])
+def test_mx_linear_layer_end_to_end(group):
+    """fprop / dgrad / wgrad of one linear with power-of-two scales, from
+    bf16 inputs through the MX quantisers and gemm_mx, against the oracle
+    run on the same inputs (sampled rows of a 2048-token batch)."""
+    t = make_inputs("qkv_fprop_m8192")
+    x = t["x.qkv"][:2048]
+    w = t["w.qkv"][:1024]
+    dy = rand((2048, 1024), 99, torch.bfloat16, 1e-3)
+    xn, wn, dyn = to_numpy_input(x), to_numpy_input(w), to_numpy_input(dy)
+    mode = "mx32" if group == 32 else "act"
+    # GPU
+    xq, xs, xqt, xst = bfp8.quantize_mx_act_dual(dev(x), group)
+    dq, ds, dqt, dst = bfp8.quantize_mx_act_dual(dev(dy), group)
+    if group == 32:
+        wq, ws, wqt, wst = bfp8.quantize_mx_act_dual(dev(w), 32)
+        y = bfp8.gemm_mx("NT", xq, xs, wq, ws, mode, mode)
+        dx = bfp8.gemm_mx("NT", dq, ds, wqt, wst, mode, mode)
+    else:
+        wq, ws = bfp8.quantize_mx_weight(dev(w))
+        y = bfp8.gemm_mx("NT", xq, xs, wq, ws, mode, "block")
+        dx = bfp8.gemm_mx("NN", dq, ds, wq, ws, mode, "block")
+    dw = bfp8.gemm_mx("NT", dqt, dst, xqt, xst, mode, mode)
+    torch.cuda.synchronize()
+    # oracle, on sampled rows / all of dW
+    rows = np.arange(0, 2048, 97)
+    eq, es = oracle.quantize_mx_act(xn[rows], group)
+    dqo, dso = oracle.quantize_mx_act(dyn[rows], group)
+    if group == 32:
+        wqo, wso = oracle.quantize_mx_act(wn, 32)
+        wqto, wsto = oracle.quantize_mx_act_transposed(wn, 32)
+        Ry = oracle.gemm_mx_ref("NT", eq, es, mode, wqo, wso, mode)
+        Rdx = oracle.gemm_mx_ref("NT", dqo, dso, mode, wqto, wsto, mode)
+    else:
+        wqo, wso = oracle.quantize_mx_weight(wn)
+        Ry = oracle.gemm_mx_ref("NT", eq, es, mode, wqo, wso, "block")
+        Rdx = oracle.gemm_mx_ref("NN", dqo, dso, mode, wqo, wso, "block")
+    xqto, xsto = oracle.quantize_mx_act_transposed(xn, group)
+    dqto, dsto = oracle.quantize_mx_act_transposed(dyn, group)
+    Rdw = oracle.gemm_mx_ref("NT", dqto, dsto, mode, xqto, xsto, mode)
+    assert oracle.rel_error(y.float().cpu().numpy()[rows], Ry) <= TOL
+    assert oracle.rel_error(dx.float().cpu().numpy()[rows], Rdx) <= TOL
+    assert oracle.rel_error(dw.float().cpu().numpy(), Rdw) <= TOL
