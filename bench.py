@@ -9,7 +9,15 @@ wgrad GEMM -- 12 GEMMs, 4.95 TFLOP.  Inputs are resident in HBM before the
 timed region.  Prints ONE JSON line on stdout; details go to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--no-cpu-baseline] [--copy-calibration]
+                  [--scales fp32|mx128|mx32] [--no-cpu-baseline] [--no-bf16-baseline]
+                  [--copy-calibration]
+
+--scales picks the scale format of the pass: fp32 (float32 amax/448 scales,
+promotion on the VALU; the default and the headline), mx128 (the same groups
+with power-of-two E8M0 scales applied by the scaled MFMA) or mx32 (MXFP8,
+1x32 power-of-two groups).  The line also carries `bf16_baseline`: the same
+12 GEMMs on the unquantised bf16 tensors through torch.matmul (hipBLASLt),
+timed the same way, for the FP8-over-BF16 ratio.
 """
 
 import argparse
@@ -52,7 +60,7 @@ def load_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(workload_name, tokens_sample):
+def cpu_baseline(workload_name, tokens_sample, scales="fp32"):
     """The oracle (numpy, float64 GEMM) on the same workload with M cut to
     `tokens_sample` tokens: every quantiser and all GEMMs of the step."""
     import numpy as np
@@ -71,7 +79,29 @@ def cpu_baseline(workload_name, tokens_sample):
     M = min(tokens_sample, wl.tokens)
     flops = 0
     t0 = time.perf_counter()
-    for L in wl.linears:
+    if scales != "fp32":
+        grp = 32 if scales == "mx32" else 128
+        mode = "mx32" if grp == 32 else "act"
+        for L in wl.linears:
+            x = to_numpy_input(t["x." + L.name])[:M]
+            w = to_numpy_input(t["w." + L.name])
+            dy = to_numpy_input(t["dy." + L.name])[:M]
+            xq, xs = oracle.quantize_mx_act(x, grp)
+            dq, ds = oracle.quantize_mx_act(dy, grp)
+            if grp == 32:
+                wq, ws = oracle.quantize_mx_act(w, 32)
+                wqt, wst = oracle.quantize_mx_act_transposed(w, 32)
+                oracle.gemm_mx_ref("NT", xq, xs, mode, wq, ws, mode)
+                oracle.gemm_mx_ref("NT", dq, ds, mode, wqt, wst, mode)
+            else:
+                wq, ws = oracle.quantize_mx_weight(w)
+                oracle.gemm_mx_ref("NT", xq, xs, mode, wq, ws, "block")
+                oracle.gemm_mx_ref("NN", dq, ds, mode, wq, ws, "block")
+            aq, as_ = oracle.quantize_mx_act_transposed(dy, grp)
+            bq, bs = oracle.quantize_mx_act_transposed(x, grp)
+            oracle.gemm_mx_ref("NT", aq, as_, mode, bq, bs, mode)
+            flops += 3 * 2 * M * L.out_features * L.in_features
+    for L in (wl.linears if scales == "fp32" else []):
         x = to_numpy_input(t["x." + L.name])[:M]
         w = to_numpy_input(t["w." + L.name])
         wq, ws = oracle.quantize_weight(w)
@@ -97,8 +127,43 @@ def cpu_baseline(workload_name, tokens_sample):
         "cores": int(threads),
         "kind": "oracle",
         "sample": f"{workload_name} with M cut to {M} tokens (all quantisers and GEMMs of "
-                  f"one step, {flops / 1e9:.1f} GFLOP, {dt:.1f} s)",
+                  f"one step, {scales} scales, {flops / 1e9:.1f} GFLOP, {dt:.1f} s)",
     }
+
+
+def bf16_baseline(tensors, wl, steps, fp8_value):
+    """The step's 12 GEMMs on the unquantised bf16 tensors via torch.matmul
+    (hipBLASLt), no quantisation: fprop X W^T, dgrad dY W, wgrad dY^T X."""
+    import torch
+
+    # every operand contiguous: the transposes W^T and dY^T are materialised
+    # once, outside the timed steps, so each product is a plain row-major
+    # matmul (transposed-view bf16 products are avoided altogether: their
+    # batched form has faulted on this software stack)
+    lin = [(tensors["x." + L.name], tensors["w." + L.name], tensors["dy." + L.name],
+            tensors["w." + L.name].t().contiguous(), tensors["dy." + L.name].t().contiguous())
+           for L in wl.linears]
+
+    def step():
+        for x, _, _, wt, _ in lin:
+            torch.matmul(x, wt)
+        for x, w, dy, _, dyt in lin:
+            torch.matmul(dy, w)
+            torch.matmul(dyt, x)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    value = wl.flops / dt / 1e12
+    log(f"[bench] bf16 baseline (torch.matmul): {dt * 1e3:.3f} ms per step, {value:.1f} TFLOP/s")
+    return {"value": round(value, 2), "unit": "TFLOP/s", "ms_per_step": round(dt * 1e3, 4),
+            "kind": "the same 12 GEMMs in bf16 via torch.matmul (hipBLASLt), unquantised",
+            "fp8_over_bf16": round(fp8_value / value, 3)}
 
 
 def main():
@@ -109,6 +174,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--scales", default="fp32", choices=["fp32", "mx128", "mx32"])
+    ap.add_argument("--no-bf16-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
@@ -131,7 +198,7 @@ def main():
     wl = WORKLOADS[args.workload]
     log(f"[bench] workload {wl.name}: generating inputs")
     tensors = {k: v.cuda() for k, v in make_inputs(wl.name).items()}
-    hp = HotPath(tensors, [L.name for L in wl.linears], wl.roles)
+    hp = HotPath(tensors, [L.name for L in wl.linears], wl.roles, scales=args.scales)
     flops_step = wl.flops
     # HotPath.run launches the GEMMs in this order:
     order = [g for g in wl.gemms if g.role == "fprop"]
@@ -174,7 +241,10 @@ def main():
     achieved = avg_flops / (avg_launch_ms * 1e-3) / 1e12
     traffic = load_traffic()
     roofline = {
-        "kernel": "gemm_kernel (blockwise FP8 GEMM; mean over the step's GEMM launches)",
+        "kernel": ("gemm_kernel (blockwise FP8 GEMM; mean over the step's GEMM launches)"
+                   if args.scales == "fp32" else
+                   f"gemm_kernel, E8M0 instantiation ({args.scales}; mean over the step's GEMM "
+                   "launches)"),
         "bound": "mfma",
         "achieved": round(achieved, 1),
         "peak": FP8_DENSE_PEAK_TFLOPS,
@@ -189,10 +259,14 @@ def main():
             f"{d * 1e3:8.1f} us  {g.flops / (d * 1e-3) / 1e12:7.1f} TFLOP/s")
     log(f"[bench] GEMM time {total_gemm_ms / args.steps:.3f} ms of {ms_per_step:.3f} ms per step")
 
+    bf16 = None
+    if not args.no_bf16_baseline and set(wl.roles) == {"fprop", "dgrad", "wgrad"}:
+        bf16 = bf16_baseline(tensors, wl, max(args.steps // 3, 3), value)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
-        cpu = cpu_baseline(wl.name, args.cpu_tokens)
+        cpu = cpu_baseline(wl.name, args.cpu_tokens, args.scales)
 
     line = {
         "metric": METRIC,
@@ -205,7 +279,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
+        "dtype": ("fp8_e4m3 (fp32 accumulate, bf16 out)" if args.scales == "fp32" else
+                  f"fp8_e4m3 with E8M0 scales, {args.scales} (fp32 accumulate, bf16 out)"),
         "data": "synthetic",
         "pct_fp8_peak": round(100 * value / FP8_DENSE_PEAK_TFLOPS, 2),
         "config": {
@@ -218,6 +293,7 @@ def main():
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "bf16_baseline": bf16,
     }
     print(json.dumps(line), flush=True)
 

@@ -10,6 +10,16 @@ where a tensor needed in both layouts is read once (quantize_act_dual).
 All buffers (codes, scales, outputs, split-K workspaces) are allocated once, so a
 pass only enqueues kernels on the current stream.  This module only calls
 the binding; every step runs in libbfp8's kernels.
+
+`scales` selects the scale format:
+  "fp32"  float32 amax/448 scales, per-128-K promotion on the VALU (the above);
+  "mx128" the same groups with power-of-two E8M0 scales (the translation,
+          section 3.2: the SM120 runs constrained block scales to powers of
+          two), applied by the scaled MFMA;
+  "mx32"  MXFP8: 1x32 power-of-two groups along K for every operand (the
+          tutorial's MXFP figure); the weight is quantised along both axes
+          (its in-features groups feed fprop, its out-features groups dgrad),
+          so all three GEMMs are NT.
 """
 
 from dataclasses import dataclass, field
@@ -17,8 +27,11 @@ from typing import Dict, List, Optional
 
 import torch
 
-from . import (gemm, gemm_workspace_bytes, quantize_act, quantize_act_dual,
-               quantize_act_transposed, quantize_weight)
+from . import (_scale_bytes, gemm, gemm_mx, gemm_workspace_bytes, quantize_act,
+               quantize_act_dual, quantize_act_transposed, quantize_mx_act_dual,
+               quantize_mx_weight, quantize_weight)
+
+SCALE_FORMATS = ("fp32", "mx128", "mx32")
 
 
 @dataclass
@@ -33,8 +46,14 @@ class LinearState:
 class HotPath:
     """Preallocated fprop/dgrad/wgrad pass over a list of linear layers."""
 
-    def __init__(self, tensors: Dict[str, torch.Tensor], names: List[str], roles: List[str]):
+    def __init__(self, tensors: Dict[str, torch.Tensor], names: List[str], roles: List[str],
+                 scales: str = "fp32"):
+        if scales not in SCALE_FORMATS:
+            raise ValueError(f"scales must be one of {SCALE_FORMATS}")
+        self.scales = scales
         self.roles = list(roles)
+        if scales != "fp32" and set(self.roles) != {"fprop", "dgrad", "wgrad"}:
+            raise ValueError("the power-of-two passes run the full fprop + dgrad + wgrad step")
         self.layers: List[LinearState] = []
         for n in names:
             L = LinearState(n, tensors["x." + n], tensors["w." + n], tensors.get("dy." + n))
@@ -43,6 +62,8 @@ class HotPath:
         self.gemm_events = None
 
     def _alloc(self, L: LinearState):
+        if self.scales != "fp32":
+            return self._alloc_mx(L)
         dev = L.x.device
         M, din = L.x.shape
         dout = L.w.shape[0]
@@ -67,17 +88,48 @@ class HotPath:
             nb = gemm_workspace_bytes("NT", "act", "act", dout, din, M)
             b["ws_wgrad"] = torch.empty((max(nb, 16),), dtype=u8, device=dev)
 
+    def _alloc_mx(self, L: LinearState):
+        """Buffers of the power-of-two passes (E8M0 scale bytes)."""
+        dev = L.x.device
+        M, din = L.x.shape
+        dout = L.w.shape[0]
+        u8, bf = torch.uint8, torch.bfloat16
+        grp = 32 if self.scales == "mx32" else 128
+        b = L.buf
+        b["wq"] = torch.empty((dout, din), dtype=u8, device=dev)
+        if grp == 32:
+            b["ws"] = _scale_bytes(dout, din // 32, dev)
+            b["wqt"] = torch.empty((din, dout), dtype=u8, device=dev)
+            b["wst"] = _scale_bytes(din, dout // 32, dev)
+        else:
+            b["ws"] = _scale_bytes((dout + 127) // 128, (din + 127) // 128, dev)
+        b["xq"] = torch.empty((M, din), dtype=u8, device=dev)
+        b["xs"] = _scale_bytes(M, din // grp, dev)
+        b["xqt"] = torch.empty((din, M), dtype=u8, device=dev)
+        b["xst"] = _scale_bytes(din, M // grp, dev)
+        b["y"] = torch.empty((M, dout), dtype=bf, device=dev)
+        b["dyq"] = torch.empty((M, dout), dtype=u8, device=dev)
+        b["dys"] = _scale_bytes(M, dout // grp, dev)
+        b["dyqt"] = torch.empty((dout, M), dtype=u8, device=dev)
+        b["dyst"] = _scale_bytes(dout, M // grp, dev)
+        b["dx"] = torch.empty((M, din), dtype=bf, device=dev)
+        b["dw"] = torch.empty((dout, din), dtype=bf, device=dev)
+        mode = "mx32" if grp == 32 else "act"
+        nb = gemm_workspace_bytes("NT", mode, mode, dout, din, M)
+        b["ws_wgrad"] = torch.empty((max(nb, 16),), dtype=u8, device=dev)
+
     def _gemm(self, *args, **kw):
+        fn = gemm if self.scales == "fp32" else gemm_mx
         ev = self.gemm_events
         if ev is not None:
             s = torch.cuda.Event(enable_timing=True)
             e = torch.cuda.Event(enable_timing=True)
             s.record()
-            out = gemm(*args, **kw)
+            out = fn(*args, **kw)
             e.record()
             ev.append((s, e))
             return out
-        return gemm(*args, **kw)
+        return fn(*args, **kw)
 
     def run(self):
         """Enqueue one full pass (every quantiser and GEMM) on the current stream.
@@ -86,6 +138,8 @@ class HotPath:
         layouts (the token-grouped codes are kept for wgrad, FP8 being the
         activation storage format); likewise dY serves dgrad and wgrad from
         one read."""
+        if self.scales != "fp32":
+            return self._run_mx()
         both_x = "fprop" in self.roles and "wgrad" in self.roles
         both_dy = "dgrad" in self.roles and "wgrad" in self.roles
         for L in self.layers:
@@ -113,3 +167,30 @@ class HotPath:
                     quantize_act_transposed(L.x, b["xqt"], b["xst"])
                 self._gemm("NT", b["dyqt"], b["dyst"], b["xqt"], b["xst"], "act", "act",
                            out=b["dw"], workspace=b["ws_wgrad"])
+
+    def _run_mx(self):
+        """One fprop + dgrad + wgrad pass with power-of-two scales.  Every
+        activation / gradient is quantised once into both layouts; with 1x32
+        groups the weight is too (in-features groups for fprop, out-features
+        groups for dgrad), otherwise its 128x128 blocks serve both GEMMs."""
+        grp = 32 if self.scales == "mx32" else 128
+        mode = "mx32" if grp == 32 else "act"
+        for L in self.layers:
+            b = L.buf
+            if grp == 32:
+                quantize_mx_act_dual(L.w, 32, b["wq"], b["ws"], b["wqt"], b["wst"])
+                wmode = "mx32"
+            else:
+                quantize_mx_weight(L.w, b["wq"], b["ws"])
+                wmode = "block"
+            quantize_mx_act_dual(L.x, grp, b["xq"], b["xs"], b["xqt"], b["xst"])
+            self._gemm("NT", b["xq"], b["xs"], b["wq"], b["ws"], mode, wmode, out=b["y"])
+        for L in self.layers:
+            b = L.buf
+            quantize_mx_act_dual(L.dy, grp, b["dyq"], b["dys"], b["dyqt"], b["dyst"])
+            if grp == 32:
+                self._gemm("NT", b["dyq"], b["dys"], b["wqt"], b["wst"], mode, "mx32", out=b["dx"])
+            else:
+                self._gemm("NN", b["dyq"], b["dys"], b["wq"], b["ws"], mode, "block", out=b["dx"])
+            self._gemm("NT", b["dyqt"], b["dyst"], b["xqt"], b["xst"], mode, mode, out=b["dw"],
+                       workspace=b["ws_wgrad"])
