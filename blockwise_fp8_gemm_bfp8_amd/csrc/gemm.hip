@@ -103,18 +103,34 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
   return r;
 }
 
+// Descriptor of base + kb * stride with a precomputed (wave-uniform) extent.
+__device__ __forceinline__ i32x4 advanced_rsrc(uint64_t base, int64_t kb, int64_t stride, int ext) {
+  const uint64_t a = base + static_cast<uint64_t>(kb) * static_cast<uint64_t>(stride);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xFFFFFFFFu));
+  r.y = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xFFFFu));
+  r.z = ext;
+  r.w = kRsrcWord3;
+  return r;
+}
+
 // Asynchronous buffer -> LDS copies (16 or 4 bytes per lane, the 64 lanes
-// landing contiguously at LDS byte address `lds`).  They are issued from
-// inline asm so the compiler does not treat them as stores that may alias
-// every later LDS read: it would otherwise wait for the copy into one stage
-// before reading fragments of the other.  Completion is awaited explicitly
-// (s_waitcnt vmcnt(0) before the barrier that publishes a stage).  The asm
-// has no result registers; its inputs are read when it issues.  The s_nop
-// covers the wait state an LDS-DMA load needs after an SALU write of M0.
+// landing contiguously at LDS byte address `lds` + OFF).  They are issued
+// from inline asm so the compiler does not treat them as stores that may
+// alias every later LDS read: it would otherwise wait for the copy into one
+// stage before reading fragments of the other.  Completion is awaited
+// explicitly (s_waitcnt vmcnt(0) before the barrier that publishes a stage).
+// The asm has no result registers; its inputs are read when it issues.  The
+// s_nop covers the wait state an LDS-DMA load needs after an SALU write of
+// M0.  The instruction's immediate offset OFF moves both the LDS
+// destination and the memory address (so the caller passes voff - OFF); it
+// lets the four 1 KiB copies of a wave share one M0 value instead of an
+// SALU add each.
+template <int OFF>
 __device__ __forceinline__ void copy16_to_lds(uint32_t lds, uint32_t voff, i32x4 rsrc) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen offset:%3 lds"
                :
-               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "s"(lds), "v"(voff), "s"(rsrc), "i"(OFF)
                : "memory", "m0");
 }
 __device__ __forceinline__ void copy4_to_lds(uint32_t lds, uint32_t voff, i32x4 rsrc) {
@@ -138,18 +154,31 @@ __device__ __forceinline__ int kmajor_swizzle(int k) { return (k & 7) | (((k >> 
 // contiguous); KMAJOR == true: stored [K][rows].  `rows` is M for A, N for B.
 template <bool KMAJOR>
 struct Operand {
-  const uint8_t* base;  // start of the tile's first row (K-contig) / first column (K-major)
-  int64_t ld;
-  int64_t rows_left;    // valid rows (or columns) from the tile start
-  int64_t K;
+  uint64_t base;        // address of the tile's first row (K-contig) / first column (K-major)
+  int64_t kstride;      // bytes between the starts of consecutive K blocks
+  int ext;              // descriptor extent, the same for every K block
   uint32_t voff[4];     // per-lane byte offsets of the four 1 KiB copies
 
   __device__ __forceinline__ void init(const uint8_t* p, int64_t ld_, int64_t r0, int64_t rows,
                                        int64_t K_, int wave, int lane) {
-    ld = ld_;
-    K = K_;
-    rows_left = rows - r0;
-    base = KMAJOR ? p + r0 : p + r0 * ld_;
+    (void)K_;
+    const int64_t rows_left = rows - r0;  // valid rows (or columns) from the tile start
+    base = reinterpret_cast<uint64_t>(KMAJOR ? p + r0 : p + r0 * ld_);
+    kstride = KMAJOR ? BK * ld_ : BK;
+    // Extent from the start of a K block.  K-contiguous: up to the end of
+    // that block's part of the last valid row, so every copy of a row past
+    // the valid ones (offset >= valid rows * ld) reads zeros.  K-major: the
+    // block's 128 k rows, a ragged last column chunk read up to the next
+    // 16-byte boundary, which the padded leading dimension covers.
+    int64_t e;
+    if (!KMAJOR) {
+      const int64_t rv = rows_left > 256 ? 256 : rows_left;
+      e = (rv - 1) * ld_ + BK;
+    } else {
+      const int64_t cols = rows_left > 256 ? 256 : ((rows_left + 15) & ~int64_t(15));
+      e = (BK - 1) * ld_ + cols;
+    }
+    ext = __builtin_amdgcn_readfirstlane(static_cast<int>(e > 0x7FFFFFFF ? 0x7FFFFFFF : e));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (!KMAJOR) {
@@ -166,28 +195,21 @@ struct Operand {
     }
   }
 
-  // Buffer descriptor of K block kb: its first byte and the extent the
-  // copies of that block may touch.  Computed once per K block; the four
-  // copies of a wave then only differ in their LDS destination.
+  // Buffer descriptor of K block kb: its first byte and the constant
+  // extent.  Computed once per K block (a 64-bit scalar add); the four
+  // copies of a wave then only differ in their offsets.
   __device__ __forceinline__ i32x4 block_rsrc(int64_t kb) const {
-    if (!KMAJOR) {
-      // bytes from (row 0, k = kb*128) to the end of the last valid row
-      const int64_t ext = (rows_left > 256 ? 256 : rows_left) * ld - (ld - K) - kb * BK;
-      return make_rsrc(base + kb * BK, ext);
-    } else {
-      // whole 16-byte chunks: a ragged last column chunk is read up to the
-      // next 16-byte boundary, which the padded leading dimension covers
-      const int64_t cols = rows_left > 256 ? 256 : ((rows_left + 15) & ~int64_t(15));
-      const int64_t ext = (BK - 1) * ld + cols;
-      return make_rsrc(base + kb * BK * ld, ext);
-    }
+    return advanced_rsrc(base, kb, kstride, ext);
   }
 
   // Copy 1 KiB piece j (0..3) of this wave's share of the K block described
   // by `r` into the LDS tile at `dst`.
   __device__ __forceinline__ void load_piece(const i32x4& r, uint8_t* dst, int wave, int j) const {
     const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_addr(dst) + wave * 4 * 1024);
-    copy16_to_lds(lbase + j * 1024, voff[j], r);
+    if (j == 0) copy16_to_lds<0>(lbase, voff[0], r);
+    else if (j == 1) copy16_to_lds<1024>(lbase, voff[1] - 1024u, r);
+    else if (j == 2) copy16_to_lds<2048>(lbase, voff[2] - 2048u, r);
+    else copy16_to_lds<3072>(lbase, voff[3] - 3072u, r);
   }
 
   // Fragment of 16 rows starting at tile row `r0` (multiple of 16): 32 bytes
@@ -230,37 +252,6 @@ struct Operand {
     }
   }
 };
-
-// Act-mode scale staging: 256 consecutive rows (A) or columns (B) of one K
-// block, one dword per lane, four waves per operand.  Rows past the end are
-// clamped to the last valid one (their products are never stored).
-template <bool KMAJOR>
-__device__ __forceinline__ void load_act_scales(const float* s, int64_t r0, int64_t rows,
-                                                int64_t KB, int64_t kb, uint8_t* dst, int sub,
-                                                int lane) {
-  int64_t r = sub * 64 + lane;  // relative to r0
-  if (r > rows - r0 - 1) r = rows - r0 - 1;
-  // K-contig operand: scales [rows][KB]; K-major: [KB][rows]
-  const float* base = KMAJOR ? s + kb * rows + r0 : s + r0 * KB + kb;
-  const int64_t ext = KMAJOR ? (rows - r0) * 4 : ((rows - r0) * KB - kb) * 4;
-  const uint32_t voff = static_cast<uint32_t>(KMAJOR ? r * 4 : r * KB * 4);
-  copy4_to_lds(__builtin_amdgcn_readfirstlane(lds_addr(dst) + sub * 256), voff,
-               make_rsrc(base, ext));
-}
-
-// Block-mode scale staging: the scales of the two 128-blocks a 256-row
-// (A) or 256-column (B) tile spans, for one K block, copied to LDS words 0
-// and 1 (the other lanes repeat block 0).  Blocks past the end are clamped.
-template <bool KMAJOR>
-__device__ __forceinline__ void load_block_scales(const float* s, int64_t r0, int64_t nblk,
-                                                  int64_t KB, int64_t kb, uint8_t* dst, int lane) {
-  int64_t blk = r0 / 128 + (lane < 2 ? lane : 0);
-  if (blk > nblk - 1) blk = nblk - 1;
-  // K-contig operand: scales [nblk][KB]; K-major: [KB][nblk]
-  const int64_t idx = KMAJOR ? kb * nblk + blk : blk * KB + kb;
-  copy4_to_lds(__builtin_amdgcn_readfirstlane(lds_addr(dst)), static_cast<uint32_t>(idx * 4),
-               make_rsrc(s, nblk * KB * 4));
-}
 
 // E8M0 scale staging: for each of 256 consecutive rows (A) or columns (B),
 // the aligned 32-bit word holding its scale byte(s) for K block kb goes to
@@ -339,6 +330,58 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
   // can be spread over the MFMA issue slots of the block before.
   constexpr int kLoadPieces = 9;
   i32x4 rsrc_a, rsrc_b;  // descriptors of the K block being copied
+
+  // float32 scales: the one dword-per-lane copy this wave makes per K block
+  // (waves 0-3 stage A's scales, waves 4-7 B's; for 128x128 block scales
+  // only the first wave of each half copies the two blocks the tile spans),
+  // as a descriptor advanced by a fixed stride per K block.  Rows past the
+  // end are clamped to the last valid one (their products are never stored).
+  bool sc_active = false;
+  uint64_t sc_base = 0;
+  int64_t sc_stride = 0;
+  int sc_ext = 0;
+  uint32_t sc_voff = 0, sc_lds = 0;
+  if constexpr (!MX) {
+    const bool b_side = wave >= 4;
+    const int sub = wave & 3;
+    const int mode = b_side ? MODE_B : MODE_A;
+    const bool km = b_side ? B_KM : A_KM;
+    const float* sp = b_side ? sB : sA;
+    const int64_t r0 = b_side ? n0 : m0, rows = b_side ? N : M, nblk = b_side ? NBk : MBk;
+    sc_lds = (b_side ? 1024u : 0u) + (mode == 0 ? static_cast<uint32_t>(sub) * 256u : 0u);
+    sc_active = mode == 0 || sub == 0;
+    const float* b;
+    int64_t e;
+    if (mode == 0) {
+      int64_t r = sub * 64 + lane;
+      if (r > rows - r0 - 1) r = rows - r0 - 1;
+      if (!km) {  // scales [rows][KB]
+        b = sp + r0 * KB;
+        sc_voff = static_cast<uint32_t>(r * KB * 4);
+        sc_stride = 4;
+        e = ((rows - r0 - 1) * KB + 1) * 4;
+      } else {    // scales [KB][rows]
+        b = sp + r0;
+        sc_voff = static_cast<uint32_t>(r * 4);
+        sc_stride = rows * 4;
+        e = (rows - r0) * 4;
+      }
+    } else {
+      int64_t blk = r0 / 128 + (lane < 2 ? lane : 0);
+      if (blk > nblk - 1) blk = nblk - 1;
+      b = sp;
+      if (!km) {  // scales [nblk][KB]
+        sc_voff = static_cast<uint32_t>(blk * KB * 4);
+        sc_stride = 4;
+      } else {    // scales [KB][nblk]
+        sc_voff = static_cast<uint32_t>(blk * 4);
+        sc_stride = nblk * 4;
+      }
+      e = nblk * KB * 4;
+    }
+    sc_base = reinterpret_cast<uint64_t>(b);
+    sc_ext = __builtin_amdgcn_readfirstlane(static_cast<int>(e > 0x7FFFFFFF ? 0x7FFFFFFF : e));
+  }
   auto issue_piece = [&](int64_t kb, uint8_t* st, int piece) {
     if (piece < 4) {
       opa.load_piece(rsrc_a, st, wave, piece);
@@ -354,14 +397,9 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
           if (MODE_B != 1 || wave == 4)
             load_mx_scales<B_KM, MODE_B>(eB, n0, N, NBk, KB, kb, sdst + 1024, wave - 4, lane);
         }
-      } else {
-        if (wave < 4) {
-          if (MODE_A == 0) load_act_scales<A_KM>(sA, m0, M, KB, kb, sdst, wave, lane);
-          else if (wave == 0) load_block_scales<A_KM>(sA, m0, MBk, KB, kb, sdst, lane);
-        } else {
-          if (MODE_B == 0) load_act_scales<B_KM>(sB, n0, N, KB, kb, sdst + 1024, wave - 4, lane);
-          else if (wave == 4) load_block_scales<B_KM>(sB, n0, NBk, KB, kb, sdst + 1024, lane);
-        }
+      } else if (sc_active) {
+        copy4_to_lds(__builtin_amdgcn_readfirstlane(lds_addr(sdst) + sc_lds), sc_voff,
+                     advanced_rsrc(sc_base, kb, sc_stride, sc_ext));
       }
     }
   };
@@ -567,9 +605,11 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
     if (more) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's copies of block kb+1 landed
       __syncthreads();                     // everyone's did, and `cur` is free
+      // B fragment and A row 0 first: the next block's first MFMA needs
+      // only those two
+      bq = opb.frag(nxt + kTileABytes, wn * WN, lane);
 #pragma unroll
       for (int i = 0; i < TM; ++i) af[i] = opa.frag(nxt, wm * WM + 16 * i, lane);
-      bq = opb.frag(nxt + kTileABytes, wn * WN, lane);
       if constexpr (MX) {
         mx_scales_a(nxt, kb + 1);
         mxb = mx_scale_b(nxt, kb + 1, 0);
