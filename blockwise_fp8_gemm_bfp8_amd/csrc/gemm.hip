@@ -31,12 +31,13 @@
 //     grouped along M so concurrent tiles on an XCD share A rows and B
 //     columns in that XCD's L2.
 //
-// The same kernel, instantiated with MX = true, multiplies operands whose
-// scales are powers of two stored as E8M0 bytes (Puro-2B translation,
-// section 3.2: the SM120 runs used power-of-two block scales on the MXFP8
-// path).  There the scales ride in the matrix-core instruction
+// Operands whose scales are powers of two stored as E8M0 bytes (Puro-2B
+// translation, section 3.2: the SM120 runs used power-of-two block scales on
+// the MXFP8 path) go to gemm_mx4_kernel: the same tile and LDS stages, but
+// the scales ride in the matrix-core instruction
 // (v_mfma_scale_f32_16x16x128_f8f6f4), the accumulators are the MFMA's C
-// operand, and no VALU promotion is needed.  The instruction takes one
+// operand in the AGPR file, and no VALU promotion is needed, which lets 4
+// waves of 128 x 128 replace 8 waves of 64 x 128.  The instruction takes one
 // scale byte per row and 32-deep K chunk: the register of lane group j
 // (lane 16j + r) scales row r's K values [32j, 32j + 32) -- which the
 // fragment layout below spreads over lane groups 2j mod 4 and 2j + 1 mod 4
@@ -152,12 +153,12 @@ __device__ __forceinline__ int kmajor_swizzle(int k) { return (k & 7) | (((k >> 
 
 // Per-operand loader/reader.  KMAJOR == false: stored [rows][K] (K
 // contiguous); KMAJOR == true: stored [K][rows].  `rows` is M for A, N for B.
-template <bool KMAJOR>
+template <bool KMAJOR, int NP = 4>
 struct Operand {
   uint64_t base;        // address of the tile's first row (K-contig) / first column (K-major)
   int64_t kstride;      // bytes between the starts of consecutive K blocks
   int ext;              // descriptor extent, the same for every K block
-  uint32_t voff[4];     // per-lane byte offsets of the four 1 KiB copies
+  uint32_t voff[NP];    // per-lane byte offsets of the wave's NP 1 KiB copies
 
   __device__ __forceinline__ void init(const uint8_t* p, int64_t ld_, int64_t r0, int64_t rows,
                                        int64_t K_, int wave, int lane) {
@@ -180,15 +181,15 @@ struct Operand {
     }
     ext = __builtin_amdgcn_readfirstlane(static_cast<int>(e > 0x7FFFFFFF ? 0x7FFFFFFF : e));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NP; ++j) {
       if (!KMAJOR) {
-        // LDS [256 rows][128 B]; copy (wave*4+j) fills rows 8(wave*4+j)..+7
-        const int row = (wave * 4 + j) * 8 + (lane >> 3);
+        // LDS [256 rows][128 B]; copy (wave*NP+j) fills rows 8(wave*NP+j)..+7
+        const int row = (wave * NP + j) * 8 + (lane >> 3);
         const int c = (lane & 7) ^ (row & 7);
         voff[j] = static_cast<uint32_t>(row * ld_ + c * 16);
       } else {
-        // LDS [128 k][256 B]; copy (wave*4+j) fills k rows 4(wave*4+j)..+3
-        const int k = (wave * 4 + j) * 4 + (lane >> 4);
+        // LDS [128 k][256 B]; copy (wave*NP+j) fills k rows 4(wave*NP+j)..+3
+        const int k = (wave * NP + j) * 4 + (lane >> 4);
         const int c = (lane & 15) ^ kmajor_swizzle(k);
         voff[j] = static_cast<uint32_t>(k * ld_ + c * 16);
       }
@@ -202,14 +203,18 @@ struct Operand {
     return advanced_rsrc(base, kb, kstride, ext);
   }
 
-  // Copy 1 KiB piece j (0..3) of this wave's share of the K block described
-  // by `r` into the LDS tile at `dst`.
+  // Copy 1 KiB piece j (0..NP-1) of this wave's share of the K block
+  // described by `r` into the LDS tile at `dst`.  Copies 4q..4q+3 share the
+  // M0 value lbase + 4 KiB * q (the immediate offset field holds at most
+  // 4095).
   __device__ __forceinline__ void load_piece(const i32x4& r, uint8_t* dst, int wave, int j) const {
-    const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_addr(dst) + wave * 4 * 1024);
-    if (j == 0) copy16_to_lds<0>(lbase, voff[0], r);
-    else if (j == 1) copy16_to_lds<1024>(lbase, voff[1] - 1024u, r);
-    else if (j == 2) copy16_to_lds<2048>(lbase, voff[2] - 2048u, r);
-    else copy16_to_lds<3072>(lbase, voff[3] - 3072u, r);
+    const uint32_t lbase =
+        __builtin_amdgcn_readfirstlane(lds_addr(dst) + wave * NP * 1024 + (j >> 2) * 4096);
+    const int jj = j & 3;
+    if (jj == 0) copy16_to_lds<0>(lbase, voff[j], r);
+    else if (jj == 1) copy16_to_lds<1024>(lbase, voff[j] - 1024u, r);
+    else if (jj == 2) copy16_to_lds<2048>(lbase, voff[j] - 2048u, r);
+    else copy16_to_lds<3072>(lbase, voff[j] - 3072u, r);
   }
 
   // Fragment of 16 rows starting at tile row `r0` (multiple of 16): 32 bytes
@@ -285,17 +290,15 @@ __device__ __forceinline__ void load_mx_scales(const uint8_t* s, int64_t r0, int
                static_cast<uint32_t>(idx & ~int64_t(3)), make_rsrc(s, (bytes + 3) & ~int64_t(3)));
 }
 
-template <bool A_KM, bool B_KM, int MODE_A, int MODE_B, bool MX>
+template <bool A_KM, bool B_KM, int MODE_A, int MODE_B>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(2, 2))) void
 gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__ sA_,
             const uint8_t* __restrict__ B, int64_t ldb, const void* __restrict__ sB_,
             uint16_t* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K, int tiles_m,
             int tiles_n, float* __restrict__ part, int64_t ldp) {
-  const float* __restrict__ sA = static_cast<const float*>(sA_);  // float32 scales (!MX)
+  const float* __restrict__ sA = static_cast<const float*>(sA_);
   const float* __restrict__ sB = static_cast<const float*>(sB_);
-  const uint8_t* __restrict__ eA = static_cast<const uint8_t*>(sA_);  // E8M0 scales (MX)
-  const uint8_t* __restrict__ eB = static_cast<const uint8_t*>(sB_);
   // Two pipeline stages; block kb lives in stage kb % 2.
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
@@ -341,7 +344,7 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
   int64_t sc_stride = 0;
   int sc_ext = 0;
   uint32_t sc_voff = 0, sc_lds = 0;
-  if constexpr (!MX) {
+  {
     const bool b_side = wave >= 4;
     const int sub = wave & 3;
     const int mode = b_side ? MODE_B : MODE_A;
@@ -389,15 +392,7 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
       opb.load_piece(rsrc_b, st + kTileABytes, wave, piece - 4);
     } else {
       uint8_t* sdst = st + kTileABytes + kTileBBytes;
-      if constexpr (MX) {
-        if (wave < 4) {
-          if (MODE_A != 1 || wave == 0)
-            load_mx_scales<A_KM, MODE_A>(eA, m0, M, MBk, KB, kb, sdst, wave, lane);
-        } else {
-          if (MODE_B != 1 || wave == 4)
-            load_mx_scales<B_KM, MODE_B>(eB, n0, N, NBk, KB, kb, sdst + 1024, wave - 4, lane);
-        }
-      } else if (sc_active) {
+      if (sc_active) {
         copy4_to_lds(__builtin_amdgcn_readfirstlane(lds_addr(sdst) + sc_lds), sc_voff,
                      advanced_rsrc(sc_base, kb, sc_stride, sc_ext));
       }
@@ -431,61 +426,6 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
       const float4 v = *reinterpret_cast<const float4*>(s_lds + BM + wn * WN + 16 * j + 4 * g);
       cb[0] = v.x; cb[1] = v.y; cb[2] = v.z; cb[3] = v.w;
     }
-  };
-
-  // E8M0 scales of this lane's fragments (MX): for each A row subtile i and
-  // B column subtile j, the byte of the staged LDS word that covers this
-  // lane's row / column and 32 K values.  The byte index within the word is
-  // (scale index) & 3; its per-lane part is fixed for the tile and packed 2
-  // bits per subtile into one register per operand, the K-block part is
-  // added per block.
-  auto byte_base = [&](bool b_side, int rt) -> uint32_t {
-    const int mode = b_side ? MODE_B : MODE_A;
-    const bool km = b_side ? B_KM : A_KM;
-    const int64_t r0 = b_side ? n0 : m0, rows = b_side ? N : M, nblk = b_side ? NBk : MBk;
-    if (mode == 2) return 0;
-    if (mode == 1) {
-      int64_t blk = (r0 + rt) / 128;
-      if (blk > nblk - 1) blk = nblk - 1;
-      return static_cast<uint32_t>(km ? blk : blk * KB) & 3u;
-    }
-    int64_t r = r0 + rt;
-    if (r > rows - 1) r = rows - 1;
-    return static_cast<uint32_t>(km ? r : r * KB) & 3u;
-  };
-  uint32_t pack_a = 0, pack_b = 0;
-  if constexpr (MX) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i) pack_a |= byte_base(false, wm * WM + 16 * i + r16) << (2 * i);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) pack_b |= byte_base(true, wn * WN + 16 * j + r16) << (2 * j);
-  }
-  int mxa[TM];
-  // K-block part of the byte index: kb (K-contiguous act / block scales),
-  // kb * rows or kb * nblk (K-major), 0 for 1x32 (byte = lane group)
-  auto kterm = [&](int mode, bool km, int64_t rows, int64_t nblk, int64_t kb) -> uint32_t {
-    if (mode == 2) return 0;
-    return static_cast<uint32_t>(km ? kb * (mode == 1 ? nblk : rows) : kb) & 3u;
-  };
-  auto mx_scales_a = [&](const uint8_t* st, int64_t kb) {
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(st + kTileABytes + kTileBBytes);
-    const uint32_t ka = kterm(MODE_A, A_KM, M, MBk, kb);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int rt = wm * WM + 16 * i + r16;
-      // block scales: word 0 / 1 = the tile's first / second 128 rows
-      const uint32_t word = MODE_A == 1 ? w[wm >> 1] : w[rt];
-      const uint32_t sh = MODE_A == 2 ? 8u * g : 8u * (((pack_a >> (2 * i)) + ka) & 3u);
-      mxa[i] = static_cast<int>((word >> sh) & 0xFFu);
-    }
-  };
-  // B scale of column subtile j, read while the MFMAs of subtile j - 1 run
-  auto mx_scale_b = [&](const uint8_t* st, int64_t kb, int j) -> int {
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(st + kTileABytes + kTileBBytes) + BM;
-    const uint32_t word = MODE_B == 1 ? w[wn] : w[wn * WN + 16 * j + r16];
-    const uint32_t kbb = kterm(MODE_B, B_KM, N, NBk, kb);
-    const uint32_t sh = MODE_B == 2 ? 8u * g : 8u * (((pack_b >> (2 * j)) + kbb) & 3u);
-    return static_cast<int>((word >> sh) & 0xFFu);
   };
 
   v4f acc[TM][TN];
@@ -522,13 +462,7 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
 #pragma unroll
   for (int i = 0; i < TM; ++i) af[i] = opa.frag(stage0, wm * WM + 16 * i, lane);
   bq = opb.frag(stage0 + kTileABytes, wn * WN, lane);
-  int mxb = 0;  // B scale of the current column subtile (MX)
-  if constexpr (MX) {
-    mx_scales_a(stage0, kb_begin);
-    mxb = mx_scale_b(stage0, kb_begin, 0);
-  } else {
-    row_mults(stage0, ra);
-  }
+  row_mults(stage0, ra);
 
   // Partials are promoted kLag MFMAs behind their issue (subtile order
   // t = j*TM + i), so the VALU never waits on a result still in the matrix
@@ -563,32 +497,18 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
       if (j + 1 < TN) bn = opb.frag(cur + kTileABytes, wn * WN + 16 * (j + 1), lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) cm_prev[r] = cm_cur[r];
-      if constexpr (!MX) col_mults(cur, j, cm_cur);
-      int mxb_next = 0;
-      if constexpr (MX) {
-        if (j + 1 < TN) mxb_next = mx_scale_b(cur, kb, j + 1);
-      }
+      col_mults(cur, j, cm_cur);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int t = j * TM + i;
-        if constexpr (MX) {
-          // scale operand 0 (src0 = the B fragment) and 1 (src1 = A), byte 0
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              bq, af[i], acc[i][j], 0, 0, 0, mxb, 0, mxa[i]);
-          // pin the accumulator of the MFMA three issues back here (its
-          // result is ready by now): without an anchor the compiler moves
-          // the MFMAs away from the copies and fragment reads they are
-          // meant to hide, and runs out of registers
-          if (t >= 3) asm volatile("" : "+v"(acc[(t - 3) % TM][(t - 3) / TM]));
-        } else {
-          const v4f pc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              bq, af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-          if (t >= kLag) {
-            const int i2 = (t - kLag) % TM, j2 = (t - kLag) / TM;
-            promote(acc[i2][j2], pend[t % kLag], ra[i2], j2 == j ? cm_cur : cm_prev);
-          }
-          pend[t % kLag] = pc;
+        // zero scales (E8M0 bytes 0 are ignored): the unscaled instruction
+        const v4f pc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            bq, af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+        if (t >= kLag) {
+          const int i2 = (t - kLag) % TM, j2 = (t - kLag) / TM;
+          promote(acc[i2][j2], pend[t % kLag], ra[i2], j2 == j ? cm_cur : cm_prev);
         }
+        pend[t % kLag] = pc;
         if (t >= 1 && t <= kLoadPieces) issue_piece(kn, nxt, t - 1);
         // one MFMA and the promotion of the partial kLag issues back per
         // scheduling region: the machine scheduler would otherwise pull each
@@ -596,7 +516,6 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
         __builtin_amdgcn_sched_barrier(0);
       }
       bq = bn;
-      if constexpr (MX) mxb = mxb_next;
     }
     // all MFMAs of this K block are issued; the last kLag subtiles (all in
     // column TN-1) are pending with this block's multipliers
@@ -610,39 +529,18 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
       bq = opb.frag(nxt + kTileABytes, wn * WN, lane);
 #pragma unroll
       for (int i = 0; i < TM; ++i) af[i] = opa.frag(nxt, wm * WM + 16 * i, lane);
-      if constexpr (MX) {
-        mx_scales_a(nxt, kb + 1);
-        mxb = mx_scale_b(nxt, kb + 1, 0);
-      } else {
-        row_mults(nxt, ra);
-      }
+      row_mults(nxt, ra);
     }
-    if constexpr (MX) {
 #pragma unroll
-      for (int q = 0; q < 3; ++q) asm volatile("" : "+v"(acc[(TM * TN - 3 + q) % TM][TN - 1]));
-    }
-    if constexpr (!MX) {
-#pragma unroll
-      for (int q = 0; q < kLag; ++q) {
-        const int t = TM * TN - kLag + q;
-        promote(acc[t % TM][TN - 1], pend[t % kLag], ra_last[t % TM], cm_cur);
-      }
+    for (int q = 0; q < kLag; ++q) {
+      const int t = TM * TN - kLag + q;
+      promote(acc[t % TM][TN - 1], pend[t % kLag], ra_last[t % TM], cm_cur);
     }
   };
 
-  if constexpr (MX) {
-    // one copy of the block body with the stages picked at run time (two
-    // unrolled copies make the register allocator split the in-place MFMA
-    // accumulators and spill)
-    for (int kb = kb_begin; kb < kb_end; ++kb) {
-      const bool odd = ((kb - kb_begin) & 1) != 0;
-      kblock(kb, odd ? stage1 : stage0, odd ? stage0 : stage1);
-    }
-  } else {
-    for (int kb = kb_begin; kb < kb_end; kb += 2) {
-      kblock(kb, stage0, stage1);
-      if (kb + 1 < kb_end) kblock(kb + 1, stage1, stage0);
-    }
+  for (int kb = kb_begin; kb < kb_end; kb += 2) {
+    kblock(kb, stage0, stage1);
+    if (kb + 1 < kb_end) kblock(kb + 1, stage1, stage0);
   }
 
   // the copies issued during the last block must land before the stages
@@ -729,6 +627,282 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
   }
 }
 
+// ---------------------------------------------------------------------------
+// Power-of-two (E8M0) scales, four waves: the same 256x256x128 tile and LDS
+// stages as gemm_kernel, but 4 waves (one per SIMD) with a 128x128 share
+// each (8 x 8 subtiles).  Without the float32 promotion nothing has to run
+// on the VALU per K block, so the 256 accumulators per lane live in the
+// AGPR file as the scaled MFMA's C operand, and the larger wave tile reads
+// 128 KiB of fragments from LDS per K block instead of 192 KiB.  With one
+// wave per SIMD nothing else covers the barrier at the end of a K block:
+// the last column's eight MFMAs are issued after it, from registers, while
+// the next block's fragments are read into the registers they free.
+// ---------------------------------------------------------------------------
+constexpr int k4Threads = 256;
+constexpr int W4M = 128, W4N = 128;  // wave tile, 2 x 2 waves
+constexpr int T4M = W4M / 16, T4N = W4N / 16;
+constexpr int k4EpiRowBytes = W4N * 2 + 8;  // padded bf16 row of a wave tile
+static_assert(2 * W4M * k4EpiRowBytes <= kStageBytes, "two epilogue slots per stage");
+
+template <bool A_KM, bool B_KM, int MODE_A, int MODE_B>
+__global__ __attribute__((amdgpu_flat_work_group_size(k4Threads, k4Threads),
+                          amdgpu_waves_per_eu(1, 1))) void
+gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__ sA_,
+                const uint8_t* __restrict__ B, int64_t ldb, const void* __restrict__ sB_,
+                uint16_t* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K, int tiles_m,
+                int tiles_n, float* __restrict__ part, int64_t ldp) {
+  const uint8_t* __restrict__ eA = static_cast<const uint8_t*>(sA_);
+  const uint8_t* __restrict__ eB = static_cast<const uint8_t*>(sB_);
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int g = lane >> 4, r16 = lane & 15;
+
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = static_cast<int64_t>(tm) * BM;
+  const int64_t n0 = static_cast<int64_t>(tn) * BN;
+  const int64_t KB = K / BK;
+  const int64_t MBk = (M + 127) / 128, NBk = (N + 127) / 128;
+  const int splits = gridDim.y, split = blockIdx.y;
+  const int kb_begin = static_cast<int>((split * static_cast<int>(KB)) / splits);
+  const int kb_end = static_cast<int>(((split + 1) * static_cast<int>(KB)) / splits);
+
+  Operand<A_KM, 8> opa;
+  Operand<B_KM, 8> opb;
+  opa.init(A, lda, m0, M, K, wave, lane);
+  opb.init(B, ldb, n0, N, K, wave, lane);
+
+  // The copy of one K block: 8 x 1 KiB of A, 8 x 1 KiB of B and the scale
+  // words of 64 rows of A and 64 columns of B per wave.
+  constexpr int kPieces = 18;
+  i32x4 rsrc_a, rsrc_b;
+  auto issue_piece = [&](int64_t kb, uint8_t* st, int piece) {
+    if (piece < 8) {
+      opa.load_piece(rsrc_a, st, wave, piece);
+    } else if (piece < 16) {
+      opb.load_piece(rsrc_b, st + kTileABytes, wave, piece - 8);
+    } else {
+      uint8_t* sdst = st + kTileABytes + kTileBBytes;
+      // every wave copies (for 128x128 blocks the copies of waves 1-3 land
+      // beside wave 0's and are never read): no wave-dependent branch
+      if (piece == 16)
+        load_mx_scales<A_KM, MODE_A>(eA, m0, M, MBk, KB, kb, sdst, wave, lane);
+      else
+        load_mx_scales<B_KM, MODE_B>(eB, n0, N, NBk, KB, kb, sdst + 1024, wave, lane);
+    }
+  };
+
+  // E8M0 bytes, as in gemm_kernel: per-lane byte offsets packed 2 bits per
+  // subtile, plus a K-block term
+  auto byte_base = [&](bool b_side, int rt) -> uint32_t {
+    const int mode = b_side ? MODE_B : MODE_A;
+    const bool km = b_side ? B_KM : A_KM;
+    const int64_t r0 = b_side ? n0 : m0, rows = b_side ? N : M, nblk = b_side ? NBk : MBk;
+    if (mode == 2) return 0;
+    if (mode == 1) {
+      int64_t blk = (r0 + rt) / 128;
+      if (blk > nblk - 1) blk = nblk - 1;
+      return static_cast<uint32_t>(km ? blk : blk * KB) & 3u;
+    }
+    int64_t r = r0 + rt;
+    if (r > rows - 1) r = rows - 1;
+    return static_cast<uint32_t>(km ? r : r * KB) & 3u;
+  };
+  uint32_t pack_a = 0, pack_b = 0;
+#pragma unroll
+  for (int i = 0; i < T4M; ++i) pack_a |= byte_base(false, wm * W4M + 16 * i + r16) << (2 * i);
+#pragma unroll
+  for (int j = 0; j < T4N; ++j) pack_b |= byte_base(true, wn * W4N + 16 * j + r16) << (2 * j);
+  auto kterm = [&](int mode, bool km, int64_t rows, int64_t nblk, int64_t kb) -> uint32_t {
+    if (mode == 2) return 0;
+    return static_cast<uint32_t>(km ? kb * (mode == 1 ? nblk : rows) : kb) & 3u;
+  };
+  // E8M0 scale words are read from LDS one column (B) or one block (A)
+  // before the bytes are extracted, so the LDS latency hides under MFMAs
+  auto word_a = [&](const uint8_t* st, int i) -> uint32_t {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(st + kTileABytes + kTileBBytes);
+    return MODE_A == 1 ? w[(wm * W4M) / 128] : w[wm * W4M + 16 * i + r16];
+  };
+  auto byte_a = [&](uint32_t word, int64_t kb, int i) -> int {
+    const uint32_t ka = kterm(MODE_A, A_KM, M, MBk, kb);
+    const uint32_t sh = MODE_A == 2 ? 8u * g : 8u * (((pack_a >> (2 * i)) + ka) & 3u);
+    return static_cast<int>((word >> sh) & 0xFFu);
+  };
+  auto word_b = [&](const uint8_t* st, int j) -> uint32_t {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(st + kTileABytes + kTileBBytes) + BM;
+    return MODE_B == 1 ? w[(wn * W4N) / 128] : w[wn * W4N + 16 * j + r16];
+  };
+  auto byte_b = [&](uint32_t word, int64_t kb, int j) -> int {
+    const uint32_t kbb = kterm(MODE_B, B_KM, N, NBk, kb);
+    const uint32_t sh = MODE_B == 2 ? 8u * g : 8u * (((pack_b >> (2 * j)) + kbb) & 3u);
+    return static_cast<int>((word >> sh) & 0xFFu);
+  };
+
+  v4f acc[T4M][T4N];
+#pragma unroll
+  for (int i = 0; i < T4M; ++i)
+#pragma unroll
+    for (int j = 0; j < T4N; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // ---- prologue -----------------------------------------------------------
+  rsrc_a = opa.block_rsrc(kb_begin);
+  rsrc_b = opb.block_rsrc(kb_begin);
+#pragma unroll
+  for (int p = 0; p < kPieces; ++p) issue_piece(kb_begin, stage0, p);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  v8i af[T4M];
+  v8i bq = opb.frag(stage0 + kTileABytes, wn * W4N, lane);
+#pragma unroll
+  for (int i = 0; i < T4M; ++i) af[i] = opa.frag(stage0, wm * W4M + 16 * i, lane);
+  uint32_t wa[T4M];
+#pragma unroll
+  for (int i = 0; i < T4M; ++i) wa[i] = word_a(stage0, i);
+  uint32_t wb = word_b(stage0, 0);
+
+  // One K block from `cur`; the copy of block kb+1 into `nxt` is issued
+  // between the first MFMAs.  The barrier sits before the last column: its
+  // MFMAs run from registers while the next block's B fragment and, one
+  // subtile at a time, its A fragments are read from `nxt`.
+  auto kblock = [&](int64_t kb, const uint8_t* cur, uint8_t* nxt) {
+    const bool more = kb + 1 < kb_end;
+    const int64_t kn = more ? kb + 1 : kb;
+    rsrc_a = opa.block_rsrc(kn);
+    rsrc_b = opb.block_rsrc(kn);
+    if (!more) {
+      rsrc_a.z = 0;
+      rsrc_b.z = 0;
+    }
+    int mxa[T4M];
+#pragma unroll
+    for (int i = 0; i < T4M; ++i) mxa[i] = byte_a(wa[i], kb, i);
+#pragma unroll
+    for (int j = 0; j < T4N; ++j) {
+      const int mxb = byte_b(wb, kb, j);
+      v8i bn = bq;
+      if (j + 1 < T4N) {
+        bn = opb.frag(cur + kTileABytes, wn * W4N + 16 * (j + 1), lane);
+        wb = word_b(cur, j + 1);
+      }
+      // (after the last K block this barrier and the reads below are
+      // harmless: the copies read nothing and the fragments go unused;
+      // keeping them unconditional keeps the block body one basic block)
+      if (j == T4N - 1) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's copies of block kb+1 landed
+        __syncthreads();                     // everyone's did, and `cur` is free
+        bn = opb.frag(nxt + kTileABytes, wn * W4N, lane);
+        wb = word_b(nxt, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < T4M; ++i) {
+        const int t = j * T4M + i;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            bq, af[i], acc[i][j], 0, 0, 0, mxb, 0, mxa[i]);
+        // pin the accumulator of the MFMA three issues back (AGPR operand,
+        // no copy): without an anchor the MFMAs drift away from the copies
+        // and fragment reads they are meant to cover
+        if (t >= 3) asm volatile("" : "+a"(acc[(t - 3) % T4M][(t - 3) / T4M]));
+        if (t >= 1 && t <= kPieces) issue_piece(kn, nxt, t - 1);
+        if (j == T4N - 1) {
+          af[i] = opa.frag(nxt, wm * W4M + 16 * i, lane);
+          wa[i] = word_a(nxt, i);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      bq = bn;
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q) asm volatile("" : "+a"(acc[(T4M * T4N - 3 + q) % T4M][T4N - 1]));
+  };
+  // one copy of the block body with the stages picked at run time
+  for (int kb = kb_begin; kb < kb_end; ++kb) {
+    const bool odd = ((kb - kb_begin) & 1) != 0;
+    kblock(kb, odd ? stage1 : stage0, odd ? stage0 : stage1);
+  }
+
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the last copies landed
+  if (part != nullptr) {
+    float* pbase = part + static_cast<int64_t>(split) * M * ldp;
+    if (m0 + wm * W4M + W4M <= M && n0 + wn * W4N + W4N <= N) {
+      float* dst = pbase + (m0 + wm * W4M + r16) * ldp + n0 + wn * W4N + 4 * g;
+#pragma unroll
+      for (int i = 0; i < T4M; ++i)
+#pragma unroll
+        for (int j = 0; j < T4N; ++j)
+          *reinterpret_cast<v4f*>(dst + 16 * i * ldp + 16 * j) = acc[i][j];
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < T4M; ++i) {
+      const int64_t m = m0 + wm * W4M + 16 * i + r16;
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < T4N; ++j) {
+        const int64_t n = n0 + wn * W4N + 16 * j + 4 * g;
+        if (n < N) {
+          float* dst = pbase + m * ldp + n;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dst[r] = acc[i][j][r];
+        }
+      }
+    }
+    return;
+  }
+
+  // ---- epilogue: bf16 through LDS (two padded 128 x 128 slots per stage),
+  // then 16 lanes store each 256-byte output row, non-temporal
+  __syncthreads();
+  uint8_t* slot = (wave < 2 ? stage0 : stage1) + (wave & 1) * (W4M * k4EpiRowBytes);
+#pragma unroll
+  for (int i = 0; i < T4M; ++i) {
+#pragma unroll
+    for (int j = 0; j < T4N; ++j) {
+      *reinterpret_cast<uint2*>(slot + (16 * i + r16) * k4EpiRowBytes + (16 * j + 4 * g) * 2) =
+          make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]),
+                     pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's slot is written
+  __builtin_amdgcn_wave_barrier();
+  const int64_t mw = m0 + wm * W4M, nw = n0 + wn * W4N;
+  const int chunk = lane & 15;
+  if (mw + W4M <= M && nw + W4N <= N) {
+    uint16_t* dst = C + (mw + (lane >> 4)) * ldc + nw + chunk * 8;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      v4u v[W4M / 8];
+#pragma unroll
+      for (int u = 0; u < W4M / 8; ++u)
+        v[u] = *reinterpret_cast<const v4u*>(slot + (64 * h + 4 * u + (lane >> 4)) * k4EpiRowBytes +
+                                             chunk * 16);
+#pragma unroll
+      for (int u = 0; u < W4M / 8; ++u)
+        __builtin_nontemporal_store(v[u], reinterpret_cast<v4u*>(dst + (64 * h + 4 * u) * ldc));
+    }
+    return;
+  }
+#pragma unroll
+  for (int u = 0; u < W4M / 4; ++u) {
+    const int row = 4 * u + (lane >> 4);
+    const uint4 v = *reinterpret_cast<const uint4*>(slot + row * k4EpiRowBytes + chunk * 16);
+    const int64_t m = mw + row, n = nw + chunk * 8;
+    if (m >= M) continue;
+    uint16_t* dst = C + m * ldc + n;
+    if (n + 7 < N) {
+      __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(dst));
+    } else if (n < N) {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      for (int e = 0; e < 8 && n + e < N; ++e)
+        dst[e] = static_cast<uint16_t>((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void fill_zero_bf16_kernel(uint16_t* __restrict__ C, int64_t M,
                                                              int64_t N, int64_t ldc) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -771,9 +945,16 @@ inline bfp8_status last_launch_status() {
 template <bool A_KM, bool B_KM, bool MX>
 static void launch_layout(const GemmArgs& a, dim3 grid, int tm, int tn, float* part,
                           int64_t ldp, hipStream_t stream) {
-#define BFP8_LAUNCH(MA, MB)                                                              \
-  gemm_kernel<A_KM, B_KM, MA, MB, MX><<<grid, dim3(kThreads), 0, stream>>>(              \
-      a.A, a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K, tm, tn, part, ldp)
+// float32 scales: the 8-wave kernel; E8M0 scales: the 4-wave kernel
+#define BFP8_LAUNCH(MA, MB)                                                                  \
+  do {                                                                                       \
+    if constexpr (MX)                                                                        \
+      gemm_mx4_kernel<A_KM, B_KM, MA, MB><<<grid, dim3(k4Threads), 0, stream>>>(             \
+          a.A, a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K, tm, tn, part, ldp); \
+    else                                                                                     \
+      gemm_kernel<A_KM, B_KM, MA, MB><<<grid, dim3(kThreads), 0, stream>>>(                  \
+          a.A, a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K, tm, tn, part, ldp); \
+  } while (0)
   if (a.modeA == 0 && a.modeB == 1) BFP8_LAUNCH(0, 1);
   else if (a.modeA == 0 && a.modeB == 0) BFP8_LAUNCH(0, 0);
   else if (a.modeA == 1 && a.modeB == 0) BFP8_LAUNCH(1, 0);

@@ -2,9 +2,10 @@
 
 A VGPR spill in the GEMM main loop costs ~8x (scratch traffic per MFMA); the
 kernels the training passes launch (fprop NT act x block, dgrad NN act x
-block, wgrad NT act x act, with float32 or power-of-two scales, and the
-1x32 MXFP8 NT kernel) must compile without spills.  CPU only (hipcc
-cross-compiles)."""
+block, wgrad NT act x act -- the 8-wave float32-scale kernel and the 4-wave
+power-of-two kernel -- and the 1x32 MXFP8 NT kernel) must compile without
+spills, and the power-of-two kernels must keep their accumulators in the
+AGPR file.  CPU only (hipcc cross-compiles)."""
 import os
 import re
 import shutil
@@ -15,14 +16,14 @@ import pytest
 from blockwise_fp8_gemm_bfp8_amd import build as bfp8_build
 
 HOT = {
-    "fprop NT act x block": r"gemm_kernelILb0ELb0ELi0ELi1ELb0E",
-    "dgrad NN act x block": r"gemm_kernelILb0ELb1ELi0ELi1ELb0E",
-    "wgrad NT act x act": r"gemm_kernelILb0ELb0ELi0ELi0ELb0E",
-    # power-of-two (E8M0) scales, hardware-scaled MFMA
-    "mx fprop NT act x block": r"gemm_kernelILb0ELb0ELi0ELi1ELb1E",
-    "mx dgrad NN act x block": r"gemm_kernelILb0ELb1ELi0ELi1ELb1E",
-    "mx wgrad NT act x act": r"gemm_kernelILb0ELb0ELi0ELi0ELb1E",
-    "mx32 NT 1x32 x 1x32": r"gemm_kernelILb0ELb0ELi2ELi2ELb1E",
+    "fprop NT act x block": r"111gemm_kernelILb0ELb0ELi0ELi1EE",
+    "dgrad NN act x block": r"111gemm_kernelILb0ELb1ELi0ELi1EE",
+    "wgrad NT act x act": r"111gemm_kernelILb0ELb0ELi0ELi0EE",
+    # power-of-two (E8M0) scales, hardware-scaled MFMA, 4 waves
+    "mx fprop NT act x block": r"gemm_mx4_kernelILb0ELb0ELi0ELi1EE",
+    "mx dgrad NN act x block": r"gemm_mx4_kernelILb0ELb1ELi0ELi1EE",
+    "mx wgrad NT act x act": r"gemm_mx4_kernelILb0ELb0ELi0ELi0EE",
+    "mx32 NT 1x32 x 1x32": r"gemm_mx4_kernelILb0ELb0ELi2ELi2EE",
 }
 
 
@@ -43,8 +44,9 @@ def kernel_meta(asm, pattern):
         name = re.search(r"\.name:\s+(\S+)", blk)
         if name and re.search(pattern, name.group(1)):
             get = lambda k: int(re.search(r"\." + k + r":\s+(\d+)", blk).group(1))
-            return {k: get(k) for k in ("vgpr_count", "vgpr_spill_count", "sgpr_spill_count",
-                                        "private_segment_fixed_size", "group_segment_fixed_size")}
+            return {k: get(k) for k in ("vgpr_count", "agpr_count", "vgpr_spill_count",
+                                        "sgpr_spill_count", "private_segment_fixed_size",
+                                        "group_segment_fixed_size")}
     raise AssertionError(f"kernel {pattern} not found")
 
 
@@ -54,3 +56,5 @@ def test_hot_gemm_kernels_do_not_spill(gemm_asm, role):
     assert m["vgpr_spill_count"] == 0, (role, m)
     assert m["private_segment_fixed_size"] == 0, (role, m)
     assert m["group_segment_fixed_size"] <= 160 * 1024, (role, m)
+    if "mx" in role:
+        assert m["agpr_count"] == 256, (role, m)
