@@ -63,7 +63,7 @@ constexpr int kStageBytes = kTileABytes + kTileBBytes + kScaleBytes;
 constexpr int kEpiRowBytes = WN * 2 + 8;            // bf16 row of a wave tile, padded
 constexpr int kEpiSlotBytes = WM * kEpiRowBytes;    // one wave's output tile
 static_assert(4 * kEpiSlotBytes <= kStageBytes, "four epilogue slots per stage");
-constexpr int kGroupM = 8;  // tile-order grouping along M
+constexpr int kGroupM = 4;  // tile-order grouping along M (4 measured 2 % faster than 8 or 16)
 constexpr int kXcds = 8;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
