@@ -110,8 +110,9 @@ def test_mx_act_transposed(group, dtype, rows, cols):
 
 @pytest.mark.parametrize("group", [32, 128])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("rows,cols", [(128, 128), (384, 256), (1024, 2048)])
+@pytest.mark.parametrize("rows,cols", [(128, 128), (384, 256), (1024, 2048), (256, 6144)])
 def test_mx_act_dual(group, dtype, rows, cols):
+    # 6144 channels: the 128 x 256 tile form for bf16
     x = rand((rows, cols), rows * 11 + cols + group, dtype, 1.0, heavy=True)
     q, s, qt, st = bfp8.quantize_mx_act_dual(dev(x), group)
     xn = to_numpy_input(x)

@@ -160,8 +160,11 @@ def test_transposed_equals_act_of_transpose_on_gpu():
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("rows,cols", [(128, 128), (384, 256), (1024, 2048), (8192, 384)])
+@pytest.mark.parametrize("rows,cols", [(128, 128), (384, 256), (1024, 2048), (8192, 384),
+                                       (256, 6144), (256, 6272), (384, 12288)])
 def test_quantize_act_dual_equals_both_quantisers(dtype, rows, cols):
+    # 6144 and 12288 channels take the 128 x 256 tiles for bf16 (paired
+    # scale stores); 6272 = 49 blocks keeps the 128 x 128 tiles
     g = torch.Generator().manual_seed(rows * 3 + cols)
     x = (torch.randn((rows, cols), generator=g) * 2).to(dtype)
     x[:, cols // 3] = 0
