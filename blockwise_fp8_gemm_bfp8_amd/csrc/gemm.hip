@@ -22,10 +22,10 @@
 //   * v_mfma_f32_16x16x128_f8f6f4 (E4M3 x E4M3 -> fp32), one instruction per
 //     16x16 subtile per K block, issued with the B tile as the first operand
 //     so each lane owns 4 consecutive output columns of one row;
-//   * promotion acc += P * (sA * sB) on the VALU, software-pipelined one
-//     subtile column behind the MFMAs so it overlaps matrix-core work; the
-//     last column of a K block is promoted after the barrier, under the LDS
-//     reads of the next block's fragments;
+//   * promotion acc += P * (sA * sB) on the VALU, three MFMA issues behind
+//     the MFMA that produced P, so it overlaps matrix-core work; the last
+//     three partials of a K block are promoted after the barrier, under the
+//     LDS reads of the next block's fragments;
 //   * XCD-aware tile order: consecutive tiles go to the same XCD (the
 //     hardware deals workgroups to the 8 XCDs round robin) and tiles are
 //     grouped along M so concurrent tiles on an XCD share A rows and B
