@@ -22,6 +22,7 @@ the binding; every step runs in libbfp8's kernels.
           so all three GEMMs are NT.
 """
 
+import ctypes
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional
 
@@ -32,6 +33,58 @@ from . import (_scale_bytes, gemm, gemm_mx, gemm_workspace_bytes, quantize_act,
                quantize_mx_weight, quantize_weight)
 
 SCALE_FORMATS = ("fp32", "mx128", "mx32")
+
+_HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+_hip_rt = None
+
+
+def _hip():
+    """The HIP runtime torch has loaded (its SONAME is libamdhip64.so.7, so this
+    dlopen returns that same instance and its streams are torch's)."""
+    global _hip_rt
+    if _hip_rt is None:
+        torch.cuda.init()
+        h = ctypes.CDLL("libamdhip64.so.7")
+        vp = ctypes.c_void_p
+        h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+        h.hipEventRecord.argtypes = [vp, vp]
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        h.hipEventDestroy.argtypes = [vp]
+        _hip_rt = h
+    return _hip_rt
+
+
+class TimingEvent:
+    """A HIP event used only to time kernels, created with
+    hipEventDisableSystemFence.  torch.cuda.Event records with a system-scope
+    fence, whose cache writeback and invalidation leave the GPU idle for about
+    6 us per record between two kernels; a pass timed GEMM by GEMM records 24
+    of them.  Same interface as torch.cuda.Event for record/elapsed_time."""
+
+    def __init__(self):
+        self._h = _hip()
+        self.ev = ctypes.c_void_p()
+        rc = self._h.hipEventCreateWithFlags(ctypes.byref(self.ev), _HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self):
+        rc = self._h.hipEventRecord(self.ev, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end: "TimingEvent") -> float:
+        """Milliseconds from this event to `end` (both recorded and complete)."""
+        ms = ctypes.c_float()
+        rc = self._h.hipEventElapsedTime(ctypes.byref(ms), self.ev, end.ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if self.ev:
+            self._h.hipEventDestroy(self.ev)
+            self.ev = ctypes.c_void_p()
 
 
 @dataclass
@@ -122,8 +175,8 @@ class HotPath:
         fn = gemm if self.scales == "fp32" else gemm_mx
         ev = self.gemm_events
         if ev is not None:
-            s = torch.cuda.Event(enable_timing=True)
-            e = torch.cuda.Event(enable_timing=True)
+            s = TimingEvent()
+            e = TimingEvent()
             s.record()
             out = fn(*args, **kw)
             e.record()
