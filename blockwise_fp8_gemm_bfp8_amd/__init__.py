@@ -10,6 +10,7 @@ Functions (same names as the C ABI in include/bfp8.h, without the prefix):
   quantize_act_transposed(x)    -> (qt uint8 [C][M], st f32 [C][M/128])
   quantize_act_dual(x)          -> (q, s, qt, st): both of the above from one read
   quantize_weight(w)            -> (q uint8 [R][C], s f32 [ceil(R/128)][ceil(C/128)])
+  quantize_weight_batch(ws)     -> [(q, s), ...]: several weights in one launch
   gemm(layout, qa, sa, qb, sb, mode_a, mode_b) -> bf16 [M][N]
 Power-of-two (E8M0) scales, group 32 or 128 (scales are uint8 tensors):
   quantize_mx_act(x, group)            -> (q, s u8 [R][C/group])
@@ -32,6 +33,7 @@ __all__ = [
     "quantize_act_dual",
     "quantize_act_transposed",
     "quantize_weight",
+    "quantize_weight_batch",
     "gemm",
     "gemm_workspace_bytes",
     "quantize_mx_act",
@@ -69,6 +71,7 @@ _SIGNATURES = {
     "bfp8_quantize_act": [_vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _vp],
     "bfp8_quantize_act_transposed": [_vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _vp],
     "bfp8_quantize_weight": [_vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _vp],
+    "bfp8_quantize_weight_batch": [_vp, _int, _int, _vp],
     "bfp8_quantize_act_dual": [_vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp],
     "bfp8_gemm": [_int, _i64, _i64, _i64, _vp, _i64, _vp, _int, _vp, _i64, _vp, _int, _vp,
                   _i64, _vp, ctypes.c_size_t, _vp],
@@ -87,6 +90,15 @@ _RESTYPES = {
     "bfp8_gemm_workspace_bytes": ctypes.c_size_t,
     "bfp8_status_str": ctypes.c_char_p,
 }
+
+MAX_WEIGHT_JOBS = 16  # BFP8_MAX_WEIGHT_JOBS
+
+
+class WeightJob(ctypes.Structure):
+    """bfp8_weight_job."""
+    _fields_ = [("w", _vp), ("rows", _i64), ("cols", _i64), ("ldw", _i64), ("q", _vp),
+                ("ldq", _i64), ("s", _vp)]
+
 
 _lib = None
 
@@ -188,6 +200,37 @@ def quantize_act_dual(x: torch.Tensor, q=None, s=None, qt=None, st=None):
         x.data_ptr(), DTYPES[x.dtype], M, C, x.stride(0), q.data_ptr(), q.stride(0),
         s.data_ptr(), qt.data_ptr(), qt.stride(0), st.data_ptr(), _stream(x)))
     return q, s, qt, st
+
+
+def quantize_weight_batch(ws, qs=None, ss=None):
+    """128x128 blocks of several weights (same dtype, same device) in one
+    launch; see bfp8_quantize_weight_batch.  Returns [(q, s), ...]."""
+    ws = list(ws)
+    if len(ws) > MAX_WEIGHT_JOBS:
+        raise ValueError(f"at most {MAX_WEIGHT_JOBS} weights per batch")
+    if not ws:
+        return []
+    qs = list(qs) if qs is not None else [None] * len(ws)
+    ss = list(ss) if ss is not None else [None] * len(ws)
+    if len(qs) != len(ws) or len(ss) != len(ws):
+        raise ValueError("qs and ss must match ws in length")
+    dt = ws[0].dtype
+    jobs = (WeightJob * len(ws))()
+    out = []
+    for i, w in enumerate(ws):
+        _check_input(w, f"ws[{i}]")
+        if w.dtype != dt or w.device != ws[0].device:
+            raise ValueError("all weights of a batch share dtype and device")
+        R, C = w.shape
+        q = qs[i] if qs[i] is not None else _padded_empty(R, C, torch.uint8, w.device, 16)
+        s = ss[i] if ss[i] is not None else torch.empty(((R + 127) // 128, (C + 127) // 128),
+                                                         dtype=torch.float32, device=w.device)
+        jobs[i] = WeightJob(w.data_ptr(), R, C, w.stride(0), q.data_ptr(), q.stride(0),
+                            s.data_ptr())
+        out.append((q, s))
+    _check("bfp8_quantize_weight_batch", lib().bfp8_quantize_weight_batch(
+        ctypes.cast(jobs, _vp), len(ws), DTYPES[dt], _stream(ws[0])))
+    return out
 
 
 def quantize_weight(w: torch.Tensor, q: torch.Tensor = None, s: torch.Tensor = None):

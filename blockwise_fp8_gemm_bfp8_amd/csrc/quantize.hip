@@ -206,13 +206,14 @@ __global__ __launch_bounds__(256) void quantize_act_t_kernel(
 // elements in registers between the block-wide amax and the encode; partial
 // edge blocks mask their missing elements to zero and store byte-wise.
 // ---------------------------------------------------------------------------
+// One 128x128 block (block row bm, block column bk) by the calling 256-thread
+// workgroup; `red` is the workgroup's 4-float reduction buffer in LDS.
 template <typename T, int RULE>
-__global__ __launch_bounds__(256) void quantize_weight_kernel(
+__device__ __forceinline__ void quantize_weight_block(
     const T* __restrict__ w, int64_t ldw, int64_t rows, int64_t cols, uint8_t* __restrict__ q,
-    int64_t ldq, typename ScaleRule<RULE>::type* __restrict__ s, int64_t n_col_blocks) {
-  __shared__ float red[4];
+    int64_t ldq, typename ScaleRule<RULE>::type* __restrict__ s, int64_t n_col_blocks,
+    int64_t bm, int64_t bk, float* red) {
   const int tid = threadIdx.x;
-  const int64_t bm = blockIdx.y, bk = blockIdx.x;
   const int64_t r0 = bm * kGroup, k0 = bk * kGroup;
   float v[8][8];
   int nv[8];
@@ -251,6 +252,31 @@ __global__ __launch_bounds__(256) void quantize_weight_kernel(
         dst[e] = static_cast<uint8_t>((e < 4 ? codes.x >> (8 * e) : codes.y >> (8 * (e - 4))) & 0xFFu);
     }
   }
+}
+
+template <typename T, int RULE>
+__global__ __launch_bounds__(256) void quantize_weight_kernel(
+    const T* __restrict__ w, int64_t ldw, int64_t rows, int64_t cols, uint8_t* __restrict__ q,
+    int64_t ldq, typename ScaleRule<RULE>::type* __restrict__ s, int64_t n_col_blocks) {
+  __shared__ float red[4];
+  quantize_weight_block<T, RULE>(w, ldw, rows, cols, q, ldq, s, n_col_blocks, blockIdx.y,
+                                 blockIdx.x, red);
+}
+
+// Several weights in one launch: the flat block index walks the weights in
+// order (first_block holds each weight's first index, kMaxWeightJobs + 1
+// entries), so the blocks of every weight run side by side and a weight
+// too small to fill the GPU on its own no longer leaves it idle.
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_weight_batch_kernel(WeightBatch b) {
+  __shared__ float red[4];
+  const int64_t blk = blockIdx.x;
+  int j = 0;
+  while (j + 1 < b.n && blk >= b.first_block[j + 1]) ++j;
+  const int64_t local = blk - b.first_block[j];
+  const int64_t cb = b.col_blocks[j];
+  quantize_weight_block<T, 0>(static_cast<const T*>(b.w[j]), b.ldw[j], b.rows[j], b.cols[j],
+                              b.q[j], b.ldq[j], b.s[j], cb, local / cb, local % cb, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -457,6 +483,19 @@ bfp8_status launch_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t ro
   BFP8_DISPATCH((quantize_dual_kernel<T, R, G, 1><<<grid, dim3(256), 0, stream>>>(
       static_cast<const T*>(x), ldx, q, ldq, static_cast<typename ScaleRule<R>::type*>(s), qt,
       ldqt, static_cast<typename ScaleRule<R>::type*>(st), ch_blocks, tok_blocks)));
+  return last_launch_status();
+}
+
+bfp8_status launch_quantize_weight_batch(const WeightBatch& b, bfp8_in_dtype dt,
+                                         hipStream_t stream) {
+  const int64_t blocks = b.first_block[b.n];
+  if (blocks == 0) return BFP8_OK;
+  if (dt == BFP8_IN_BF16)
+    quantize_weight_batch_kernel<uint16_t><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                                             stream>>>(b);
+  else
+    quantize_weight_batch_kernel<float><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                                          stream>>>(b);
   return last_launch_status();
 }
 

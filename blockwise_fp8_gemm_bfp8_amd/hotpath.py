@@ -6,7 +6,8 @@ the Puro-2B paper translation (papers.lianghsun.dev), section 3.2:
   dgrad:  quantize_act(dy), gemm NN with W's codes as stored -> dx [M][in]
   wgrad:  quantize_act_transposed(dy), quantize_act_transposed(x),
           gemm NT on the two token-grouped operands          -> dW [out][in]
-where a tensor needed in both layouts is read once (quantize_act_dual).
+where a tensor needed in both layouts is read once (quantize_act_dual), and
+all the weights are quantised in one launch (quantize_weight_batch).
 All buffers (codes, scales, outputs, split-K workspaces) are allocated once, so a
 pass only enqueues kernels on the current stream.  This module only calls
 the binding; every step runs in libbfp8's kernels.
@@ -23,14 +24,15 @@ the binding; every step runs in libbfp8's kernels.
 """
 
 import ctypes
+import sys
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional
 
 import torch
 
-from . import (_scale_bytes, gemm, gemm_mx, gemm_workspace_bytes, quantize_act,
+from . import (MAX_WEIGHT_JOBS, _scale_bytes, gemm, gemm_mx, gemm_workspace_bytes, quantize_act,
                quantize_act_dual, quantize_act_transposed, quantize_mx_act_dual,
-               quantize_mx_weight, quantize_weight)
+               quantize_mx_weight, quantize_weight_batch)
 
 SCALE_FORMATS = ("fp32", "mx128", "mx32")
 
@@ -82,9 +84,10 @@ class TimingEvent:
         return ms.value
 
     def __del__(self):
-        if self.ev:
+        # at interpreter exit the HIP runtime may already be torn down
+        if self.ev and not sys.is_finalizing():
             self._h.hipEventDestroy(self.ev)
-            self.ev = ctypes.c_void_p()
+        self.ev = ctypes.c_void_p()
 
 
 @dataclass
@@ -195,9 +198,14 @@ class HotPath:
             return self._run_mx()
         both_x = "fprop" in self.roles and "wgrad" in self.roles
         both_dy = "dgrad" in self.roles and "wgrad" in self.roles
+        # every weight's 128x128 blocks in one launch (the weights are
+        # independent of the rest of the pass)
+        for i in range(0, len(self.layers), MAX_WEIGHT_JOBS):
+            group = self.layers[i:i + MAX_WEIGHT_JOBS]
+            quantize_weight_batch([L.w for L in group], [L.buf["wq"] for L in group],
+                                  [L.buf["ws"] for L in group])
         for L in self.layers:
             b = L.buf
-            quantize_weight(L.w, b["wq"], b["ws"])
             if "fprop" in self.roles:
                 if both_x:
                     quantize_act_dual(L.x, b["xq"], b["xs"], b["xqt"], b["xst"])

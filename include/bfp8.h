@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define BFP8_ABI_VERSION 2
+#define BFP8_ABI_VERSION 3
 
 typedef enum {
   BFP8_OK = 0,
@@ -153,6 +153,32 @@ bfp8_status bfp8_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t rows
 bfp8_status bfp8_quantize_weight(const void* w, bfp8_in_dtype dt, int64_t rows, int64_t cols,
                                  int64_t ldw, uint8_t* q, int64_t ldq, float* s,
                                  hipStream_t stream);
+
+/*
+ * Batched weight quantiser: several weights in one launch, each job's result
+ * bit-identical to bfp8_quantize_weight on it.  The same 128x128 blocks
+ * (Puro-2B translation, section 3.2).  The blocks of all jobs run side by
+ * side, so weights too small to fill the GPU alone (for example 2048 x 2048:
+ * 256 blocks) do not leave it idle.
+ *
+ *   jobs  host array of n job descriptions (read during the call only); each
+ *         job's arguments mean what bfp8_quantize_weight's do, and all jobs
+ *         share the input dtype dt
+ *   n     0 .. BFP8_MAX_WEIGHT_JOBS
+ * Every job is validated as bfp8_quantize_weight validates its arguments;
+ * the first failing job's status is returned and nothing is launched.
+ * Jobs must not overlap in their outputs.
+ */
+#define BFP8_MAX_WEIGHT_JOBS 16
+typedef struct {
+  const void* w;
+  int64_t rows, cols, ldw;
+  uint8_t* q;
+  int64_t ldq;
+  float* s;
+} bfp8_weight_job;
+bfp8_status bfp8_quantize_weight_batch(const bfp8_weight_job* jobs, int n, bfp8_in_dtype dt,
+                                       hipStream_t stream);
 
 /*
  * Blockwise FP8 GEMM with per-128-K-block scale promotion and bf16 output.

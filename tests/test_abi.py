@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["bfp8_quantize_act", "bfp8_quantize_act_transposed",
                             "bfp8_quantize_act_dual",
-                            "bfp8_quantize_weight", "bfp8_gemm", "bfp8_gemm_workspace_bytes",
+                            "bfp8_quantize_weight", "bfp8_quantize_weight_batch",
+                            "bfp8_gemm", "bfp8_gemm_workspace_bytes",
                             "bfp8_quantize_mx_act", "bfp8_quantize_mx_act_transposed",
                             "bfp8_quantize_mx_act_dual", "bfp8_quantize_mx_weight",
                             "bfp8_gemm_mx", "bfp8_status_str", "bfp8_abi_version"])
@@ -47,10 +48,40 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.bfp8_abi_version() == 2
+    assert L.bfp8_abi_version() == 3
     for code in range(9):
         assert len(L.bfp8_status_str(code)) > 0
     assert L.bfp8_status_str(99) == b"unknown status"
+
+
+def test_weight_job_struct_matches_header():
+    # bfp8_weight_job: w, rows, cols, ldw, q, ldq, s (pointers and int64s, no padding)
+    assert ctypes.sizeof(bfp8.WeightJob) == 56
+    assert [f[0] for f in bfp8.WeightJob._fields_] == ["w", "rows", "cols", "ldw", "q", "ldq", "s"]
+    src = open(HEADER).read()
+    assert "#define BFP8_MAX_WEIGHT_JOBS %d" % bfp8.MAX_WEIGHT_JOBS in src
+
+
+def test_quantize_weight_batch_errors(L):
+    def batch(*jobs, n=None, dt=0):
+        arr = (bfp8.WeightJob * max(len(jobs), 1))(*jobs)
+        return L.bfp8_quantize_weight_batch(ctypes.cast(arr, ctypes.c_void_p),
+                                            len(jobs) if n is None else n, dt, None)
+    good = dict(w=P, rows=384, cols=256, ldw=256, q=P, ldq=256, s=P)
+    J = lambda **k: bfp8.WeightJob(**{**good, **k})
+    assert L.bfp8_quantize_weight_batch(None, 0, 0, None) == OK   # nothing to do
+    assert L.bfp8_quantize_weight_batch(None, 1, 0, None) == NULL
+    assert batch(J(), n=-1) == SHAPE
+    assert batch(J(), n=bfp8.MAX_WEIGHT_JOBS + 1) == SHAPE
+    assert batch(J(), J(w=None)) == NULL                           # second job checked too
+    assert batch(J(s=None)) == NULL
+    assert batch(J(q=P + 4)) == ALIGN
+    assert batch(J(ldw=260)) == ALIGN                              # bf16 row not 16-byte aligned
+    assert batch(J(ldq=128)) == SHAPE                              # ldq < cols
+    assert batch(J(rows=-1)) == SHAPE
+    assert batch(J(), dt=5) == DTYPE
+    # empty jobs are skipped; a batch of only empty jobs launches nothing
+    assert batch(J(w=None, q=None, s=None, rows=0), J(w=None, q=None, s=None, cols=0)) == OK
 
 
 def qa(L, x=P, dt=0, rows=256, cols=512, ldx=512, q=P, ldq=512, s=P):

@@ -230,6 +230,43 @@ def test_weight_block_with_outlier_and_zero_block():
     assert s[0, 0].item() == 1.0
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_quantize_weight_batch_matches_oracle_and_single_calls(dtype):
+    """One launch over weights of mixed sizes (ragged edge blocks, a
+    2048 x 2048 weight of 256 blocks, an empty one): each job bit-exact
+    against the oracle and against bfp8_quantize_weight on it; a second
+    batch on a subset into the same buffers gives the same bytes."""
+    shapes = [(384, 512), (100, 200), (2048, 2048), (0, 256), (300, 2048), (128, 6144)]
+    ws = []
+    for i, (r, c) in enumerate(shapes):
+        g = torch.Generator().manual_seed(1000 + i)
+        ws.append((torch.randn((r, c), generator=g) * 0.02 * (i + 1)).to(dtype))
+    got = bfp8.quantize_weight_batch([dev(w) for w in ws])
+    for (r, c), w, (q, s) in zip(shapes, ws, got):
+        if r == 0:
+            continue
+        eq, es = oracle_quantize_weight_ragged(to_numpy_input(w))
+        assert_same_codes(q, s, eq, es, f"batch weight {r}x{c} {dtype}")
+        q1, s1 = bfp8.quantize_weight(dev(w))
+        assert torch.equal(q, q1) and torch.equal(s.view(torch.int32), s1.view(torch.int32))
+    again = bfp8.quantize_weight_batch([dev(w) for w in ws[1:3]],
+                                       [q for q, _ in got[1:3]], [s for _, s in got[1:3]])
+    torch.cuda.synchronize()
+    for (q, s), w in zip(again, ws[1:3]):
+        eq, es = oracle_quantize_weight_ragged(to_numpy_input(w))
+        assert_same_codes(q, s, eq, es, "batch again")
+
+
+def test_quantize_weight_batch_max_jobs():
+    """BFP8_MAX_WEIGHT_JOBS small weights in one launch."""
+    n = bfp8.MAX_WEIGHT_JOBS
+    ws = [rand_bf16((128 * (1 + i % 3), 256), 50 + i, 0.01 * (1 + i)) for i in range(n)]
+    got = bfp8.quantize_weight_batch([dev(w) for w in ws])
+    for w, (q, s) in zip(ws, got):
+        eq, es = oracle.quantize_weight(to_numpy_input(w))
+        assert_same_codes(q, s, eq, es, "max-jobs batch")
+
+
 # ---------------------------------------------------------------- workloads
 
 
