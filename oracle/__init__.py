@@ -24,7 +24,7 @@ What it computes follows these passages:
   1x128 / 128x128 groups and the MXFP8 1x32 groups of the tutorial's MXFP
   figure).
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 scale = fl32(amax / 448); element map fl32(x * fl32(448 / amax)); saturating
 round-to-nearest-even; an all-zero group gets scale 1.0; signed zeros are
 kept; fp32 accumulation is promoted once per 128-deep K block.

@@ -11,7 +11,7 @@ Format: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits.
   * S.1111.111 is NaN; there are no infinities; largest finite is 0x7E = 448.
 
 Encoding is saturating round-to-nearest-even (a reading: the pages name the
-format but not the rounding; see DESIGN.md).  All arithmetic below is done
+format but not the rounding).  All arithmetic below is done
 in float64 on values that are exactly representable there, so every step is
 exact except the one rounding the definition asks for (numpy.rint, which
 rounds halves to even).

@@ -13,7 +13,7 @@ What the pages say:
     MXFP8 shares one scale X per block of 32 elements and an element decodes
     as V_i = Q_i * X.
 
-Readings (the pages leave these open; the design doc lists them):
+Readings (the pages leave these open):
   * scale exponent e = the smallest integer with 448 * 2**e >= amax (the
     power of two is rounded up, so no element of the group saturates),
     clamped to [-127, 127]; an all-zero group gets e = 0;

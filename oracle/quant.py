@@ -8,7 +8,7 @@ weights use 128x128 2-D blocks, each with its own scale.  The decode rule
 value = code * scale is the MXFP figure of the Puro-2B tutorial
 (bloombook.cn), FP8/MuonH section.
 
-Readings (the pages leave these open; the design doc lists them):
+Readings (the pages leave these open):
   * scale s = fl32(amax / 448), an IEEE float32 division;
   * element map y = fl32(x * fl32(448 / amax)), one float32 multiply, then
     saturating round-to-nearest-even to E4M3;

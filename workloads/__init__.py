@@ -11,7 +11,7 @@ Shapes follow the model and batch geometry on the pages:
   * Puro-2B paper translation (papers.lianghsun.dev), section 2 and
     section 3.1.3: sequence length 4096, micro-batch size 2, so one
     micro-batch holds M = 8192 tokens.
-Distributions (readings, listed in the design doc): activations N(0,1) with a
+Distributions (readings; the pages do not fix them): activations N(0,1) with a
 seeded 0.5% of feature columns multiplied by 50 (the pages only say that
 outliers exist, section 3.2); weights N(0, 0.02); activation gradients
 N(0, 1e-3); the full-layer workload uses unscaled Student-t(3) activations.
