@@ -17,6 +17,7 @@ Power-of-two (E8M0) scales, group 32 or 128 (scales are uint8 tensors):
   quantize_mx_act_transposed(x, group) -> (qt, st u8 [C][M/group])
   quantize_mx_act_dual(x, group)       -> (q, s, qt, st)
   quantize_mx_weight(w)                -> (q, s u8 [ceil(R/128)][ceil(C/128)])
+  quantize_mx_weight_batch(ws)         -> [(q, s), ...]: several weights in one launch
   gemm_mx(layout, qa, sa, qb, sb, mode_a, mode_b) -> bf16 [M][N]
     (modes 'act' = 1x128, 'block' = 128x128, 'mx32' = 1x32)
 """
@@ -40,6 +41,7 @@ __all__ = [
     "quantize_mx_act_transposed",
     "quantize_mx_act_dual",
     "quantize_mx_weight",
+    "quantize_mx_weight_batch",
     "gemm_mx",
     "lib",
     "BFP8Error",
@@ -81,6 +83,7 @@ _SIGNATURES = {
     "bfp8_quantize_mx_act_dual": [_vp, _int, _i64, _i64, _i64, _int, _vp, _i64, _vp, _vp, _i64,
                                   _vp, _vp],
     "bfp8_quantize_mx_weight": [_vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _vp],
+    "bfp8_quantize_mx_weight_batch": [_vp, _int, _int, _vp],
     "bfp8_gemm_mx": [_int, _i64, _i64, _i64, _vp, _i64, _vp, _int, _vp, _i64, _vp, _int, _vp,
                      _i64, _vp, ctypes.c_size_t, _vp],
     "bfp8_status_str": [_int],
@@ -95,7 +98,8 @@ MAX_WEIGHT_JOBS = 16  # BFP8_MAX_WEIGHT_JOBS
 
 
 class WeightJob(ctypes.Structure):
-    """bfp8_weight_job."""
+    """bfp8_weight_job, and bfp8_mx_weight_job (the same layout; s points at
+    E8M0 bytes there)."""
     _fields_ = [("w", _vp), ("rows", _i64), ("cols", _i64), ("ldw", _i64), ("q", _vp),
                 ("ldq", _i64), ("s", _vp)]
 
@@ -202,9 +206,7 @@ def quantize_act_dual(x: torch.Tensor, q=None, s=None, qt=None, st=None):
     return q, s, qt, st
 
 
-def quantize_weight_batch(ws, qs=None, ss=None):
-    """128x128 blocks of several weights (same dtype, same device) in one
-    launch; see bfp8_quantize_weight_batch.  Returns [(q, s), ...]."""
+def _weight_batch(fn, ws, qs, ss, scale_dtype):
     ws = list(ws)
     if len(ws) > MAX_WEIGHT_JOBS:
         raise ValueError(f"at most {MAX_WEIGHT_JOBS} weights per batch")
@@ -224,13 +226,18 @@ def quantize_weight_batch(ws, qs=None, ss=None):
         R, C = w.shape
         q = qs[i] if qs[i] is not None else _padded_empty(R, C, torch.uint8, w.device, 16)
         s = ss[i] if ss[i] is not None else torch.empty(((R + 127) // 128, (C + 127) // 128),
-                                                         dtype=torch.float32, device=w.device)
+                                                         dtype=scale_dtype, device=w.device)
         jobs[i] = WeightJob(w.data_ptr(), R, C, w.stride(0), q.data_ptr(), q.stride(0),
                             s.data_ptr())
         out.append((q, s))
-    _check("bfp8_quantize_weight_batch", lib().bfp8_quantize_weight_batch(
-        ctypes.cast(jobs, _vp), len(ws), DTYPES[dt], _stream(ws[0])))
+    _check(fn, getattr(lib(), fn)(ctypes.cast(jobs, _vp), len(ws), DTYPES[dt], _stream(ws[0])))
     return out
+
+
+def quantize_weight_batch(ws, qs=None, ss=None):
+    """128x128 blocks of several weights (same dtype, same device) in one
+    launch; see bfp8_quantize_weight_batch.  Returns [(q, s), ...]."""
+    return _weight_batch("bfp8_quantize_weight_batch", ws, qs, ss, torch.float32)
 
 
 def quantize_weight(w: torch.Tensor, q: torch.Tensor = None, s: torch.Tensor = None):
@@ -362,6 +369,12 @@ def quantize_mx_weight(w: torch.Tensor, q=None, s=None):
         s.data_ptr(), _stream(w)))
     return q, s
 
+
+
+def quantize_mx_weight_batch(ws, qs=None, ss=None):
+    """Power-of-two 128x128 blocks of several weights in one launch; see
+    bfp8_quantize_mx_weight_batch.  Returns [(q, s u8), ...]."""
+    return _weight_batch("bfp8_quantize_mx_weight_batch", ws, qs, ss, torch.uint8)
 
 def gemm_mx(layout: str, qa, sa, qb, sb, mode_a: str = "act", mode_b: str = "block",
             out: torch.Tensor = None, workspace: torch.Tensor = None, split_k: bool = True):

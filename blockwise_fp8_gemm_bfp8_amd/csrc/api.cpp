@@ -97,6 +97,43 @@ bfp8_status gemm_common(bfp8_layout layout, int64_t M, int64_t N, int64_t K, con
   return launch_gemm(g, workspace, workspace_bytes, stream);
 }
 
+// Validate the jobs of a batched weight quantiser (each as the single call
+// would) and launch them; JOB is bfp8_weight_job or bfp8_mx_weight_job.
+template <typename JOB>
+bfp8_status weight_batch(const JOB* jobs, int n, bfp8_in_dtype dt, int rule, hipStream_t stream) {
+  if (n < 0 || n > BFP8_MAX_WEIGHT_JOBS) return BFP8_ERR_SHAPE;
+  if (n == 0) return BFP8_OK;
+  if (jobs == nullptr) return BFP8_ERR_NULL;
+  if (!valid_dtype(dt)) return BFP8_ERR_DTYPE;
+  WeightBatch b{};
+  int m = 0;
+  int64_t total = 0;
+  for (int i = 0; i < n; ++i) {
+    const JOB& j = jobs[i];
+    bfp8_status st = check_quant_common(j.w, dt, j.rows, j.cols, j.ldw, j.q, j.ldq, j.s);
+    if (st != BFP8_OK) return st;
+    if (j.rows == 0 || j.cols == 0) continue;  // nothing to do for this job
+    if (j.ldq < j.cols) return BFP8_ERR_SHAPE;
+    const int64_t rb = cdiv(j.rows, 128), cb = cdiv(j.cols, 128);
+    if (rb > kMaxGridY || cb >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+    b.w[m] = j.w;
+    b.q[m] = j.q;
+    b.s[m] = j.s;
+    b.ldw[m] = j.ldw;
+    b.rows[m] = j.rows;
+    b.cols[m] = j.cols;
+    b.ldq[m] = j.ldq;
+    b.col_blocks[m] = cb;
+    b.first_block[m] = total;
+    total += rb * cb;
+    if (total >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+    ++m;
+  }
+  b.n = m;
+  b.first_block[m] = total;
+  if (m == 0) return BFP8_OK;
+  return launch_quantize_weight_batch(b, dt, rule, stream);
+}
 }  // namespace
 
 extern "C" {
@@ -169,38 +206,7 @@ bfp8_status bfp8_quantize_weight(const void* w, bfp8_in_dtype dt, int64_t rows, 
 
 bfp8_status bfp8_quantize_weight_batch(const bfp8_weight_job* jobs, int n, bfp8_in_dtype dt,
                                        hipStream_t stream) {
-  if (n < 0 || n > BFP8_MAX_WEIGHT_JOBS) return BFP8_ERR_SHAPE;
-  if (n == 0) return BFP8_OK;
-  if (jobs == nullptr) return BFP8_ERR_NULL;
-  if (!valid_dtype(dt)) return BFP8_ERR_DTYPE;
-  WeightBatch b{};
-  int m = 0;
-  int64_t total = 0;
-  for (int i = 0; i < n; ++i) {
-    const bfp8_weight_job& j = jobs[i];
-    bfp8_status st = check_quant_common(j.w, dt, j.rows, j.cols, j.ldw, j.q, j.ldq, j.s);
-    if (st != BFP8_OK) return st;
-    if (j.rows == 0 || j.cols == 0) continue;  // nothing to do for this job
-    if (j.ldq < j.cols) return BFP8_ERR_SHAPE;
-    const int64_t rb = cdiv(j.rows, 128), cb = cdiv(j.cols, 128);
-    if (rb > kMaxGridY || cb >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
-    b.w[m] = j.w;
-    b.q[m] = j.q;
-    b.s[m] = j.s;
-    b.ldw[m] = j.ldw;
-    b.rows[m] = j.rows;
-    b.cols[m] = j.cols;
-    b.ldq[m] = j.ldq;
-    b.col_blocks[m] = cb;
-    b.first_block[m] = total;
-    total += rb * cb;
-    if (total >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
-    ++m;
-  }
-  b.n = m;
-  b.first_block[m] = total;
-  if (m == 0) return BFP8_OK;
-  return launch_quantize_weight_batch(b, dt, stream);
+  return weight_batch(jobs, n, dt, 0, stream);
 }
 
 // ---- power-of-two (E8M0) scale rule ----------------------------------------
@@ -255,6 +261,11 @@ bfp8_status bfp8_quantize_mx_weight(const void* w, bfp8_in_dtype dt, int64_t row
   if (ldq < cols) return BFP8_ERR_SHAPE;
   if (cdiv(rows, 128) > kMaxGridY || cdiv(cols, 128) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
   return launch_quantize_weight(w, dt, rows, cols, ldw, 1, q, ldq, s, stream);
+}
+
+bfp8_status bfp8_quantize_mx_weight_batch(const bfp8_mx_weight_job* jobs, int n,
+                                          bfp8_in_dtype dt, hipStream_t stream) {
+  return weight_batch(jobs, n, dt, 1, stream);
 }
 
 size_t bfp8_gemm_workspace_bytes(bfp8_layout layout, bfp8_scale_mode modeA,

@@ -142,14 +142,14 @@ bfp8_status launch_quantize_weight(const void* w, bfp8_in_dtype dt, int64_t rows
                                    int64_t ldw, int rule, uint8_t* q, int64_t ldq, void* s,
                                    hipStream_t stream);
 
-// Kernel argument of the batched weight quantiser (float32 scales): the
-// jobs' pointers and sizes, and the flat index of each job's first
-// 128x128 block (first_block[n] = total blocks).
+// Kernel argument of the batched weight quantiser: the jobs' pointers and
+// sizes (scales float32 or E8M0 bytes, by the launch's rule), and the flat
+// index of each job's first 128x128 block (first_block[n] = total blocks).
 constexpr int kMaxWeightJobs = BFP8_MAX_WEIGHT_JOBS;
 struct WeightBatch {
   const void* w[kMaxWeightJobs];
   uint8_t* q[kMaxWeightJobs];
-  float* s[kMaxWeightJobs];
+  void* s[kMaxWeightJobs];
   int64_t ldw[kMaxWeightJobs];
   int64_t rows[kMaxWeightJobs];
   int64_t cols[kMaxWeightJobs];
@@ -158,7 +158,7 @@ struct WeightBatch {
   int64_t first_block[kMaxWeightJobs + 1];
   int n;
 };
-bfp8_status launch_quantize_weight_batch(const WeightBatch& b, bfp8_in_dtype dt,
+bfp8_status launch_quantize_weight_batch(const WeightBatch& b, bfp8_in_dtype dt, int rule,
                                          hipStream_t stream);
 
 struct GemmArgs {

@@ -267,7 +267,7 @@ __global__ __launch_bounds__(256) void quantize_weight_kernel(
 // order (first_block holds each weight's first index, kMaxWeightJobs + 1
 // entries), so the blocks of every weight run side by side and a weight
 // too small to fill the GPU on its own no longer leaves it idle.
-template <typename T>
+template <typename T, int RULE>
 __global__ __launch_bounds__(256) void quantize_weight_batch_kernel(WeightBatch b) {
   __shared__ float red[4];
   const int64_t blk = blockIdx.x;
@@ -275,8 +275,10 @@ __global__ __launch_bounds__(256) void quantize_weight_batch_kernel(WeightBatch 
   while (j + 1 < b.n && blk >= b.first_block[j + 1]) ++j;
   const int64_t local = blk - b.first_block[j];
   const int64_t cb = b.col_blocks[j];
-  quantize_weight_block<T, 0>(static_cast<const T*>(b.w[j]), b.ldw[j], b.rows[j], b.cols[j],
-                              b.q[j], b.ldq[j], b.s[j], cb, local / cb, local % cb, red);
+  quantize_weight_block<T, RULE>(static_cast<const T*>(b.w[j]), b.ldw[j], b.rows[j], b.cols[j],
+                                 b.q[j], b.ldq[j],
+                                 static_cast<typename ScaleRule<RULE>::type*>(b.s[j]), cb,
+                                 local / cb, local % cb, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -486,16 +488,18 @@ bfp8_status launch_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t ro
   return last_launch_status();
 }
 
-bfp8_status launch_quantize_weight_batch(const WeightBatch& b, bfp8_in_dtype dt,
+bfp8_status launch_quantize_weight_batch(const WeightBatch& b, bfp8_in_dtype dt, int rule,
                                          hipStream_t stream) {
   const int64_t blocks = b.first_block[b.n];
   if (blocks == 0) return BFP8_OK;
-  if (dt == BFP8_IN_BF16)
-    quantize_weight_batch_kernel<uint16_t><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                                             stream>>>(b);
-  else
-    quantize_weight_batch_kernel<float><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                                          stream>>>(b);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  if (dt == BFP8_IN_BF16) {
+    if (rule == 0) quantize_weight_batch_kernel<uint16_t, 0><<<grid, block, 0, stream>>>(b);
+    else quantize_weight_batch_kernel<uint16_t, 1><<<grid, block, 0, stream>>>(b);
+  } else {
+    if (rule == 0) quantize_weight_batch_kernel<float, 0><<<grid, block, 0, stream>>>(b);
+    else quantize_weight_batch_kernel<float, 1><<<grid, block, 0, stream>>>(b);
+  }
   return last_launch_status();
 }
 

@@ -32,7 +32,7 @@ import torch
 
 from . import (MAX_WEIGHT_JOBS, _scale_bytes, gemm, gemm_mx, gemm_workspace_bytes, quantize_act,
                quantize_act_dual, quantize_act_transposed, quantize_mx_act_dual,
-               quantize_mx_weight, quantize_weight_batch)
+               quantize_mx_weight_batch, quantize_weight_batch)
 
 SCALE_FORMATS = ("fp32", "mx128", "mx32")
 
@@ -236,13 +236,17 @@ class HotPath:
         groups for dgrad), otherwise its 128x128 blocks serve both GEMMs."""
         grp = 32 if self.scales == "mx32" else 128
         mode = "mx32" if grp == 32 else "act"
+        if grp == 128:
+            for i in range(0, len(self.layers), MAX_WEIGHT_JOBS):
+                group = self.layers[i:i + MAX_WEIGHT_JOBS]
+                quantize_mx_weight_batch([L.w for L in group], [L.buf["wq"] for L in group],
+                                         [L.buf["ws"] for L in group])
         for L in self.layers:
             b = L.buf
             if grp == 32:
                 quantize_mx_act_dual(L.w, 32, b["wq"], b["ws"], b["wqt"], b["wst"])
                 wmode = "mx32"
             else:
-                quantize_mx_weight(L.w, b["wq"], b["ws"])
                 wmode = "block"
             quantize_mx_act_dual(L.x, grp, b["xq"], b["xs"], b["xqt"], b["xst"])
             self._gemm("NT", b["xq"], b["xs"], b["wq"], b["ws"], mode, wmode, out=b["y"])

@@ -244,6 +244,19 @@ bfp8_status bfp8_quantize_mx_weight(const void* w, bfp8_in_dtype dt, int64_t row
                                     int64_t ldw, uint8_t* q, int64_t ldq, uint8_t* s,
                                     hipStream_t stream);
 
+/* Batched form of bfp8_quantize_mx_weight, as bfp8_quantize_weight_batch is
+ * of bfp8_quantize_weight: up to BFP8_MAX_WEIGHT_JOBS weights in one launch,
+ * each job bit-identical to the single call, validated the same way. */
+typedef struct {
+  const void* w;
+  int64_t rows, cols, ldw;
+  uint8_t* q;
+  int64_t ldq;
+  uint8_t* s;
+} bfp8_mx_weight_job;
+bfp8_status bfp8_quantize_mx_weight_batch(const bfp8_mx_weight_job* jobs, int n,
+                                          bfp8_in_dtype dt, hipStream_t stream);
+
 /*
  * GEMM on E8M0-scaled operands: C[m][n] = sum over K of dec(A) * dec(B) with
  * each product scaled by its two groups' powers of two, accumulated in fp32,

@@ -39,6 +39,7 @@ def test_header_declares_the_boundary():
                             "bfp8_gemm", "bfp8_gemm_workspace_bytes",
                             "bfp8_quantize_mx_act", "bfp8_quantize_mx_act_transposed",
                             "bfp8_quantize_mx_act_dual", "bfp8_quantize_mx_weight",
+                            "bfp8_quantize_mx_weight_batch",
                             "bfp8_gemm_mx", "bfp8_status_str", "bfp8_abi_version"])
 
 
@@ -82,6 +83,22 @@ def test_quantize_weight_batch_errors(L):
     assert batch(J(), dt=5) == DTYPE
     # empty jobs are skipped; a batch of only empty jobs launches nothing
     assert batch(J(w=None, q=None, s=None, rows=0), J(w=None, q=None, s=None, cols=0)) == OK
+
+
+def test_quantize_mx_weight_batch_errors(L):
+    def batch(*jobs, n=None, dt=0):
+        arr = (bfp8.WeightJob * max(len(jobs), 1))(*jobs)
+        return L.bfp8_quantize_mx_weight_batch(ctypes.cast(arr, ctypes.c_void_p),
+                                               len(jobs) if n is None else n, dt, None)
+    good = dict(w=P, rows=384, cols=256, ldw=256, q=P, ldq=256, s=P)
+    J = lambda **k: bfp8.WeightJob(**{**good, **k})
+    assert L.bfp8_quantize_mx_weight_batch(None, 0, 0, None) == OK
+    assert L.bfp8_quantize_mx_weight_batch(None, 2, 0, None) == NULL
+    assert batch(J(), n=bfp8.MAX_WEIGHT_JOBS + 1) == SHAPE
+    assert batch(J(), J(q=None)) == NULL
+    assert batch(J(w=P + 8)) == ALIGN
+    assert batch(J(ldq=128)) == SHAPE                              # ldq < cols
+    assert batch(J(), dt=3) == DTYPE
 
 
 def qa(L, x=P, dt=0, rows=256, cols=512, ldx=512, q=P, ldq=512, s=P):

@@ -143,6 +143,23 @@ def test_mx_weight(dtype, rows, cols):
     same(q, s, eq, es, f"mx weight {rows}x{cols}")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_mx_weight_batch_matches_oracle_and_single_calls(dtype):
+    """One launch over weights of mixed sizes (ragged edge blocks, an empty
+    weight): each job's codes and scale bytes equal the oracle's and the
+    single call's."""
+    shapes = [(128, 128), (300, 200), (0, 128), (2048, 6144), (2048, 2048)]
+    ws = [rand((r, c), 7 * i + r + c, dtype, 0.02, heavy=True) for i, (r, c) in enumerate(shapes)]
+    got = bfp8.quantize_mx_weight_batch([dev(w) for w in ws])
+    for (r, c), w, (q, s) in zip(shapes, ws, got):
+        if r == 0:
+            continue
+        eq, es = oracle.quantize_mx_weight(to_numpy_input(w))
+        same(q, s, eq, es, f"mx weight batch {r}x{c}")
+        q1, s1 = bfp8.quantize_mx_weight(dev(w))
+        assert torch.equal(q, q1) and torch.equal(s, s1)
+
+
 # ---------------------------------------------------------------- GEMM
 
 
