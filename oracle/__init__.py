@@ -43,11 +43,12 @@ from .quant import (
     quantize_weight,
     GROUP,
 )
-from .gemm import dequantize_operand, gemm_ref, normwise_error, rel_error
+from .gemm import dequantize_operand, gemm_ref, logical_operand, normwise_error, o6_error
 from .mx import (
     E8M0_BIAS,
     dequantize_mx_operand,
     e8m0_decode,
+    logical_mx_operand,
     gemm_mx_ref,
     pow2_exponent,
     quantize_mx_act,
@@ -67,7 +68,8 @@ __all__ = [
     "GROUP",
     "dequantize_operand",
     "gemm_ref",
-    "rel_error",
+    "o6_error",
+    "logical_operand",
     "normwise_error",
     "E8M0_BIAS",
     "pow2_exponent",
@@ -77,5 +79,6 @@ __all__ = [
     "quantize_mx_act_transposed",
     "quantize_mx_weight",
     "dequantize_mx_operand",
+    "logical_mx_operand",
     "gemm_mx_ref",
 ]

@@ -133,8 +133,9 @@ def quantize_mx_weight(w):
 _MODE_GROUP = {"act": 128, "mx32": 32}
 
 
-def dequantize_mx_operand(q, s, role, trans, mode):
-    """Dequantise one stored operand with E8M0 scales, in logical orientation.
+def logical_mx_operand(q, s, role, trans, mode):
+    """Codes and per-element E8M0 scales (as float64 powers of two) of one
+    stored operand, in logical orientation (A: [M][K], B: [K][N]).
 
     role 'A' (logical [M][K]) or 'B' (logical [K][N]); trans 'N' or 'T' as in
     gemm.py; mode 'act' (1x128 along K), 'mx32' (1x32 along K) or 'block'
@@ -156,8 +157,16 @@ def dequantize_mx_operand(q, s, role, trans, mode):
         full = np.repeat(np.repeat(sc, 128, axis=0), 128, axis=1)[:R, :C]
     else:
         raise ValueError(mode)
-    stored = e4m3_decode(q) * full
-    return stored if trans == "N" else stored.T
+    if trans == "T":
+        return q.T, full.T
+    return q, full
+
+
+def dequantize_mx_operand(q, s, role, trans, mode):
+    """Dequantise one stored operand with E8M0 scales, in logical orientation
+    (arguments as for logical_mx_operand): decoded code times its scale."""
+    codes, scales = logical_mx_operand(q, s, role, trans, mode)
+    return e4m3_decode(codes) * scales
 
 
 def gemm_mx_ref(layout, qa, sa, mode_a, qb, sb, mode_b):

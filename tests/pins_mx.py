@@ -209,3 +209,33 @@ def random_mx_operands(rng, layout, mode_a, mode_b, M, N, K):
     sa = scales(a_shape, 1 if layout[0] == "N" else 0, mode_a)
     sb = scales(b_shape, 0 if layout[1] == "N" else 1, mode_b)
     return qa, sa, qb, sb
+
+
+def check_mx_weight_transpose(quant_weight_fn, rng):
+    """128x128 blocks commute with transposition: the codes and scales of
+    W^T are those of W, transposed (ragged shapes included)."""
+    for shape in [(300, 200), (256, 384), (129, 1), (1, 130)]:
+        w = (rng.standard_t(3, shape) * 0.02).astype(np.float32)
+        q, s = quant_weight_fn(w)
+        qt, st = quant_weight_fn(np.ascontiguousarray(w.T))
+        assert (q == qt.T).all(), ("codes", shape)
+        assert (s == st.T).all(), ("scales", shape)
+
+
+def check_mx_weight_single_row(quant_weight_fn, quant_act_fn, rng):
+    """A block with one non-zero row (not its first) quantises as that row's
+    1x128 group; the all-zero blocks get the zero-group scale (byte 127)."""
+    w = np.zeros((384, 384), np.float32)
+    r = 128 + 1 + int(rng.integers(0, 126))
+    row = (rng.standard_normal(128) * rng.uniform(1e-3, 1e3)).astype(np.float32)
+    w[r, 256:384] = row
+    q, s = quant_weight_fn(w)
+    qa, sa = quant_act_fn(row[None, :], 128)
+    assert s[1, 2] == sa[0, 0]
+    assert (q[r, 256:384] == qa[0]).all()
+    blk = q[128:256, 256:384].copy()
+    blk[r - 128] = 0
+    assert (blk == 0).all()
+    others = np.ones(s.shape, bool)
+    others[1, 2] = False
+    assert (s[others] == 127).all()

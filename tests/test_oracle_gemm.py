@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import pins
-from oracle import gemm_ref, quantize_act, quantize_weight, rel_error
+from oracle import gemm_ref, quantize_act, quantize_weight
 
 LAYOUTS = ["NT", "NN", "TN"]
 MODES = [("act", "block"), ("act", "act"), ("block", "act"), ("block", "block")]

@@ -227,3 +227,46 @@ def test_mx_gemm_scale_axis_mutant_is_caught():
     want = pins_mx.fraction_gemm_mx("NT", qa, sa, "mx32", qb, sb, "mx32")
     got = gemm_mx32_scales_on_wrong_axis("NT", qa, sa, "mx32", qb, sb, "mx32")
     assert not np.allclose(got, want, rtol=0, atol=1e-12 * np.max(np.abs(want)))
+
+
+# ---- E8M0 weight-quantiser mutants ------------------------------------------
+
+from oracle import quantize_mx_group, quantize_mx_weight  # noqa: E402
+
+
+def mxw_first_row_amax(w):
+    """Each block's scale taken from its first row's amax only."""
+    w = np.asarray(w, np.float32)
+    q, s = quantize_mx_weight(w)
+    for i in range(s.shape[0]):
+        for j in range(s.shape[1]):
+            blk = w[128 * i:128 * (i + 1), 128 * j:128 * (j + 1)]
+            e = pow2_exponent(np.max(np.abs(blk[0])))
+            y = (blk.astype(np.float64) * np.exp2(-float(e))).astype(np.float32)
+            q[128 * i:128 * (i + 1), 128 * j:128 * (j + 1)] = e4m3_encode(np.clip(y, -448, 448))
+            s[i, j] = np.uint8(e + 127)
+    return q, s
+
+
+def mxw_row_strips(w):
+    """1x128 groups along each row instead of 128x128 blocks, the scale of
+    the block taken from the block's first row group."""
+    w = np.asarray(w, np.float32)
+    N, K = w.shape
+    q = np.zeros((N, K), np.uint8)
+    s = np.zeros((-(-N // 128), -(-K // 128)), np.uint8)
+    for r in range(N):
+        for j in range(-(-K // 128)):
+            qg, bg = quantize_mx_group(w[r, 128 * j:128 * (j + 1)])
+            q[r, 128 * j:128 * (j + 1)] = qg
+            if r % 128 == 0:
+                s[r // 128, j] = bg
+    return q, s
+
+
+@pytest.mark.parametrize("mutant", [mxw_first_row_amax, mxw_row_strips])
+def test_mx_weight_mutants_are_caught(mutant):
+    r = np.random.default_rng(3)
+    caught = (_fails(pins_mx.check_mx_weight_transpose, mutant, r)
+              or _fails(pins_mx.check_mx_weight_single_row, mutant, quantize_mx_act, r))
+    assert caught

@@ -13,6 +13,8 @@ from pins_mx import (
     check_mx_fill,
     check_mx_group_locality,
     check_mx_scale_invariance,
+    check_mx_weight_single_row,
+    check_mx_weight_transpose,
     check_mx_zero_group,
     check_pow2_exponent,
     fraction_gemm_mx,
@@ -85,6 +87,15 @@ def test_mx_weight_blocks_and_ragged_edges():
     blk = w[:128, :128]
     q2, b2 = oracle.quantize_mx_group(blk.reshape(-1))
     assert b2 == s[0, 0] and (q2.reshape(128, 128) == q[:128, :128]).all()
+
+
+def test_mx_weight_transpose_identity():
+    check_mx_weight_transpose(oracle.quantize_mx_weight, rng(16))
+
+
+def test_mx_weight_single_row_block_is_an_act_group():
+    for seed in (17, 18, 19):
+        check_mx_weight_single_row(oracle.quantize_mx_weight, oracle.quantize_mx_act, rng(seed))
 
 
 def test_mx_bf16_input_equals_fp32_input():

@@ -4,19 +4,18 @@ grid of the dual quantiser, and the largest leading dimension the GEMM
 addresses (4 MiB rows, K = 2**22).  Inputs are drawn on the device from a
 seeded generator; the sampled rows, groups and outputs are copied back and
 checked element by element (codes and scale bits exactly, GEMM outputs
-within the 1e-2 tolerance)."""
+under the gate of tests/gate.py)."""
 import numpy as np
 import pytest
 import torch
 
+import gate
 import oracle
 from workloads import to_numpy_input
 
 pytestmark = pytest.mark.gpu
 
 import blockwise_fp8_gemm_bfp8_amd as bfp8  # noqa: E402
-
-TOL = 1e-2
 
 
 def same_codes(got_q, got_s, exp_q, exp_s, what):
@@ -81,10 +80,8 @@ def test_gemm_largest_leading_dimension():
     C = bfp8.gemm("NT", qa, sa, qb, sb, "act", "act")
     torch.cuda.synchronize()
     rows, cols = [0, 1, 255, 256, 259], [0, 3, 255, 256, 263]
-    A = oracle.dequantize_operand(qa[rows].cpu().numpy(), sa[rows].cpu().numpy(), "A", "N", "act")
-    B = oracle.dequantize_operand(qb[cols].cpu().numpy(), sb[cols].cpu().numpy(), "B", "T", "act")
-    R = A @ B
+    ac, asc = oracle.logical_operand(qa[rows].cpu().numpy(), sa[rows].cpu().numpy(), "A", "N", "act")
+    bc, bsc = oracle.logical_operand(qb[cols].cpu().numpy(), sb[cols].cpu().numpy(), "B", "T", "act")
     got = C.float().cpu().numpy()[np.ix_(rows, cols)]
-    err = oracle.rel_error(got, R)
-    assert err <= TOL, err
+    gate.check(got, ac, asc, bc, bsc, ("largest leading dimension", M, N, K))
     release(qa, qb, sa, sb, C)

@@ -1,9 +1,11 @@
 """GPU parity of the power-of-two (E8M0) path against the CPU oracle (oracle/mx.py).
 
 Quantisers: bit-exact codes and bit-exact scale bytes, groups of 32 and 128.
-GEMM: rel_error <= 1e-2 against the float64 product of the dequantised
-operands (same reading of the tolerance as tests/test_parity_gemm.py), and
-bit-exact bf16 where every fp32 step is exact (integer-valued codes).
+GEMM: the gate of tests/gate.py (|C - R| <= 1e-2 |R| + (1 + 2**-9) E, E from
+the matrix core's pinned arithmetic; the scaled MFMA sums its groups of 8 the
+same way, tests/test_mfma_arithmetic.py) against the float64 product of the
+dequantised operands, and bit-exact bf16 where every fp32 step is exact
+(integer-valued codes).
 """
 import itertools
 
@@ -11,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import gate
 import oracle
 import pins_mx
 from workloads import make_inputs, to_numpy_input
@@ -18,8 +21,6 @@ from workloads import make_inputs, to_numpy_input
 pytestmark = pytest.mark.gpu
 
 import blockwise_fp8_gemm_bfp8_amd as bfp8  # noqa: E402
-
-TOL = 1e-2
 
 
 def dev(t):
@@ -184,10 +185,9 @@ MX_CASES = [("NT", "act", "block"), ("NT", "act", "act"), ("NT", "mx32", "mx32")
 def test_gemm_mx_random(layout, ma, mb, M, N, K):
     rng = np.random.default_rng(M + 3 * N + 7 * K + len(ma) * 13 + len(mb))
     qa, sa, qb, sb = pins_mx.random_mx_operands(rng, layout, ma, mb, M, N, K)
-    R = ref_mx(layout, qa, sa, ma, qb, sb, mb)
     C = run_mx(layout, qa, sa, ma, qb, sb, mb)
-    err = oracle.rel_error(C.float().cpu().numpy(), R)
-    assert err <= TOL, (layout, ma, mb, M, N, K, err)
+    gate.check_stored(C.float().cpu().numpy(), layout, qa, sa, ma, qb, sb, mb,
+                      (layout, ma, mb, M, N, K), mx=True)
 
 
 def integer_mx_operands(rng, layout, ma, mb, M, N, K):
@@ -221,11 +221,12 @@ def test_gemm_mx_split_k(M, N, K, ma, mb):
     rng = np.random.default_rng(M + N)
     qa, sa, qb, sb = pins_mx.random_mx_operands(rng, "NT", ma, mb, M, N, K)
     assert bfp8.gemm_workspace_bytes("NT", ma, mb, M, N, K) > 0
-    R = ref_mx("NT", qa, sa, ma, qb, sb, mb)
+    parts = gate.operand_parts("NT", qa, sa, ma, qb, sb, mb, mx=True)
+    R = gate.reference(*parts)
     split = run_mx("NT", qa, sa, ma, qb, sb, mb)
     unsplit = run_mx("NT", qa, sa, ma, qb, sb, mb, split_k=False)
-    assert oracle.rel_error(split.float().cpu().numpy(), R) <= TOL
-    assert oracle.rel_error(unsplit.float().cpu().numpy(), R) <= TOL
+    gate.check(split.float().cpu().numpy(), *parts, ("split", M, N, K), R=R)
+    gate.check(unsplit.float().cpu().numpy(), *parts, ("unsplit", M, N, K), R=R)
 
 
 @pytest.mark.parametrize("group", [32, 128])
@@ -259,15 +260,15 @@ def test_mx_linear_layer_end_to_end(group):
     if group == 32:
         wqo, wso = oracle.quantize_mx_act(wn, 32)
         wqto, wsto = oracle.quantize_mx_act_transposed(wn, 32)
-        Ry = oracle.gemm_mx_ref("NT", eq, es, mode, wqo, wso, mode)
-        Rdx = oracle.gemm_mx_ref("NT", dqo, dso, mode, wqto, wsto, mode)
+        py = gate.operand_parts("NT", eq, es, mode, wqo, wso, mode, mx=True)
+        pdx = gate.operand_parts("NT", dqo, dso, mode, wqto, wsto, mode, mx=True)
     else:
         wqo, wso = oracle.quantize_mx_weight(wn)
-        Ry = oracle.gemm_mx_ref("NT", eq, es, mode, wqo, wso, "block")
-        Rdx = oracle.gemm_mx_ref("NN", dqo, dso, mode, wqo, wso, "block")
+        py = gate.operand_parts("NT", eq, es, mode, wqo, wso, "block", mx=True)
+        pdx = gate.operand_parts("NN", dqo, dso, mode, wqo, wso, "block", mx=True)
     xqto, xsto = oracle.quantize_mx_act_transposed(xn, group)
     dqto, dsto = oracle.quantize_mx_act_transposed(dyn, group)
-    Rdw = oracle.gemm_mx_ref("NT", dqto, dsto, mode, xqto, xsto, mode)
-    assert oracle.rel_error(y.float().cpu().numpy()[rows], Ry) <= TOL
-    assert oracle.rel_error(dx.float().cpu().numpy()[rows], Rdx) <= TOL
-    assert oracle.rel_error(dw.float().cpu().numpy(), Rdw) <= TOL
+    pdw = gate.operand_parts("NT", dqto, dsto, mode, xqto, xsto, mode, mx=True)
+    gate.check(y.float().cpu().numpy()[rows], *py, ("mx fprop", group))
+    gate.check(dx.float().cpu().numpy()[rows], *pdx, ("mx dgrad", group))
+    gate.check(dw.float().cpu().numpy(), *pdw, ("mx wgrad", group))
