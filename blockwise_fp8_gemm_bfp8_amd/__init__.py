@@ -60,6 +60,7 @@ STATUS = {
     6: "BFP8_ERR_SCALE_MODE",
     7: "BFP8_ERR_WORKSPACE",
     8: "BFP8_ERR_HIP",
+    9: "BFP8_ERR_NONFINITE",
 }
 LAYOUTS = {"NN": 0, "NT": 1, "TN": 2}
 MODES = {"act": 0, "block": 1, "mx32": 2}

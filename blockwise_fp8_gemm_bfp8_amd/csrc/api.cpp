@@ -132,6 +132,12 @@ bfp8_status weight_batch(const JOB* jobs, int n, bfp8_in_dtype dt, int rule, hip
   b.n = m;
   b.first_block[m] = total;
   if (m == 0) return BFP8_OK;
+  if (debug_checks_enabled()) {
+    for (int i = 0; i < m; ++i) {
+      const bfp8_status st = check_finite(b.w[i], dt, b.rows[i], b.cols[i], b.ldw[i], stream);
+      if (st != BFP8_OK) return st;
+    }
+  }
   return launch_quantize_weight_batch(b, dt, rule, stream);
 }
 }  // namespace
@@ -152,6 +158,7 @@ const char* bfp8_status_str(bfp8_status status) {
     case BFP8_ERR_SCALE_MODE: return "unknown scale mode";
     case BFP8_ERR_WORKSPACE: return "workspace missing or too small";
     case BFP8_ERR_HIP: return "HIP launch failed";
+    case BFP8_ERR_NONFINITE: return "input holds Inf or NaN (reported only with BFP8_DEBUG set)";
   }
   return "unknown status";
 }
@@ -164,6 +171,8 @@ bfp8_status bfp8_quantize_act(const void* x, bfp8_in_dtype dt, int64_t rows, int
   if (st != BFP8_OK || rows == 0 || cols == 0) return st;
   if (ldq < cols) return BFP8_ERR_SHAPE;
   if (rows * (cols / 128) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+  if (debug_checks_enabled() && (st = check_finite(x, dt, rows, cols, ldx, stream)) != BFP8_OK)
+    return st;
   return launch_quantize_act(x, dt, rows, cols, ldx, 0, 128, q, ldq, s, stream);
 }
 
@@ -175,6 +184,8 @@ bfp8_status bfp8_quantize_act_transposed(const void* x, bfp8_in_dtype dt, int64_
   if (st != BFP8_OK || rows == 0 || cols == 0) return st;
   if (ldqt < rows) return BFP8_ERR_SHAPE;
   if (rows / 128 > kMaxGridY || cdiv(cols, 64) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+  if (debug_checks_enabled() && (st = check_finite(x, dt, rows, cols, ldx, stream)) != BFP8_OK)
+    return st;
   return launch_quantize_act_transposed(x, dt, rows, cols, ldx, 0, 128, qt, ldqt, st_, stream);
 }
 
@@ -190,6 +201,8 @@ bfp8_status bfp8_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t rows
   if (ldq < cols || ldqt < rows) return BFP8_ERR_SHAPE;
   if (ldqt % 16 != 0) return BFP8_ERR_ALIGN;
   if (rows / 128 > kMaxGridY || cols / 128 >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+  if (debug_checks_enabled() && (st = check_finite(x, dt, rows, cols, ldx, stream)) != BFP8_OK)
+    return st;
   return launch_quantize_act_dual(x, dt, rows, cols, ldx, 0, 128, q, ldq, s, qt, ldqt, st_,
                                   stream);
 }
@@ -201,6 +214,8 @@ bfp8_status bfp8_quantize_weight(const void* w, bfp8_in_dtype dt, int64_t rows, 
   if (st != BFP8_OK || rows == 0 || cols == 0) return st;
   if (ldq < cols) return BFP8_ERR_SHAPE;
   if (cdiv(rows, 128) > kMaxGridY || cdiv(cols, 128) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+  if (debug_checks_enabled() && (st = check_finite(w, dt, rows, cols, ldw, stream)) != BFP8_OK)
+    return st;
   return launch_quantize_weight(w, dt, rows, cols, ldw, 0, q, ldq, s, stream);
 }
 
@@ -220,6 +235,8 @@ bfp8_status bfp8_quantize_mx_act(const void* x, bfp8_in_dtype dt, int64_t rows, 
   if (st != BFP8_OK || rows == 0 || cols == 0) return st;
   if (ldq < cols) return BFP8_ERR_SHAPE;
   if (rows * (cols / 128) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+  if (debug_checks_enabled() && (st = check_finite(x, dt, rows, cols, ldx, stream)) != BFP8_OK)
+    return st;
   return launch_quantize_act(x, dt, rows, cols, ldx, 1, group, q, ldq, s, stream);
 }
 
@@ -232,6 +249,8 @@ bfp8_status bfp8_quantize_mx_act_transposed(const void* x, bfp8_in_dtype dt, int
   if (st != BFP8_OK || rows == 0 || cols == 0) return st;
   if (ldqt < rows) return BFP8_ERR_SHAPE;
   if (rows / 128 > kMaxGridY || cdiv(cols, 64) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+  if (debug_checks_enabled() && (st = check_finite(x, dt, rows, cols, ldx, stream)) != BFP8_OK)
+    return st;
   return launch_quantize_act_transposed(x, dt, rows, cols, ldx, 1, group, qt, ldqt, st_, stream);
 }
 
@@ -249,6 +268,8 @@ bfp8_status bfp8_quantize_mx_act_dual(const void* x, bfp8_in_dtype dt, int64_t r
   if (ldq < cols || ldqt < rows) return BFP8_ERR_SHAPE;
   if (ldqt % 16 != 0) return BFP8_ERR_ALIGN;
   if (rows / 128 > kMaxGridY || cols / 128 >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+  if (debug_checks_enabled() && (st = check_finite(x, dt, rows, cols, ldx, stream)) != BFP8_OK)
+    return st;
   return launch_quantize_act_dual(x, dt, rows, cols, ldx, 1, group, q, ldq, s, qt, ldqt, st_,
                                   stream);
 }
@@ -260,6 +281,8 @@ bfp8_status bfp8_quantize_mx_weight(const void* w, bfp8_in_dtype dt, int64_t row
   if (st != BFP8_OK || rows == 0 || cols == 0) return st;
   if (ldq < cols) return BFP8_ERR_SHAPE;
   if (cdiv(rows, 128) > kMaxGridY || cdiv(cols, 128) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+  if (debug_checks_enabled() && (st = check_finite(w, dt, rows, cols, ldw, stream)) != BFP8_OK)
+    return st;
   return launch_quantize_weight(w, dt, rows, cols, ldw, 1, q, ldq, s, stream);
 }
 

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 #include "bfp8.h"
 
 namespace bfp8 {
@@ -122,6 +125,38 @@ __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, __shfl_xor(v, 32));
   return v;
 }
+
+// Kernel launch that reports this launch's own status: the return value of
+// hipLaunchKernel, not HIP's thread-wide last error (which an unrelated
+// earlier call may have left set).  The arguments are converted to the
+// kernel's parameter types before their addresses are taken.  On failure
+// HIP also records the error as the calling thread's last error; the caller
+// reads and clears it with hipGetLastError.
+template <typename... KArgs, size_t... I>
+inline bfp8_status launch_packed(void (*kernel)(KArgs...), dim3 grid, dim3 block,
+                                 hipStream_t stream, std::tuple<KArgs...>& vals,
+                                 std::index_sequence<I...>) {
+  void* argv[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1] = {static_cast<void*>(&std::get<I>(vals))...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, stream) ==
+                 hipSuccess
+             ? BFP8_OK
+             : BFP8_ERR_HIP;
+}
+template <typename... KArgs, typename... Args>
+inline bfp8_status launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                          Args&&... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+  std::tuple<KArgs...> vals(static_cast<KArgs>(std::forward<Args>(args))...);
+  return launch_packed(kernel, grid, block, stream, vals, std::index_sequence_for<KArgs...>{});
+}
+
+// Opt-in input check (environment variable BFP8_DEBUG set to anything but
+// "" or "0", read once per process): true when enabled.
+bool debug_checks_enabled();
+// Scan x [rows][ldx] for Inf / NaN on `stream`, wait for the result, and
+// return BFP8_ERR_NONFINITE if one is found (BFP8_ERR_HIP on a HIP failure).
+bfp8_status check_finite(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
+                         hipStream_t stream);
 
 // Host-side launch helpers (defined in the .hip files).  `rule` selects the
 // scale rule (0: float32 amax/448, 1: power-of-two E8M0 byte) and `s` points

@@ -936,24 +936,22 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
-inline bfp8_status last_launch_status() {
-  return hipPeekAtLastError() == hipSuccess ? BFP8_OK : BFP8_ERR_HIP;
-}
-
 }  // namespace
 
 template <bool A_KM, bool B_KM, bool MX>
-static void launch_layout(const GemmArgs& a, dim3 grid, int tm, int tn, float* part,
-                          int64_t ldp, hipStream_t stream) {
+static bfp8_status launch_layout(const GemmArgs& a, dim3 grid, int tm, int tn, float* part,
+                                 int64_t ldp, hipStream_t stream) {
 // float32 scales: the 8-wave kernel; E8M0 scales: the 4-wave kernel
-#define BFP8_LAUNCH(MA, MB)                                                                  \
-  do {                                                                                       \
-    if constexpr (MX)                                                                        \
-      gemm_mx4_kernel<A_KM, B_KM, MA, MB><<<grid, dim3(k4Threads), 0, stream>>>(             \
-          a.A, a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K, tm, tn, part, ldp); \
-    else                                                                                     \
-      gemm_kernel<A_KM, B_KM, MA, MB><<<grid, dim3(kThreads), 0, stream>>>(                  \
-          a.A, a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K, tm, tn, part, ldp); \
+#define BFP8_LAUNCH(MA, MB)                                                                   \
+  do {                                                                                        \
+    if constexpr (MX)                                                                         \
+      return launch(&gemm_mx4_kernel<A_KM, B_KM, MA, MB>, grid, dim3(k4Threads), stream, a.A, \
+                    a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K, tm, tn, part,   \
+                    ldp);                                                                     \
+    else                                                                                      \
+      return launch(&gemm_kernel<A_KM, B_KM, MA, MB>, grid, dim3(kThreads), stream, a.A,      \
+                    a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K, tm, tn, part,   \
+                    ldp);                                                                     \
   } while (0)
   if (a.modeA == 0 && a.modeB == 1) BFP8_LAUNCH(0, 1);
   else if (a.modeA == 0 && a.modeB == 0) BFP8_LAUNCH(0, 0);
@@ -973,6 +971,7 @@ static void launch_layout(const GemmArgs& a, dim3 grid, int tm, int tn, float* p
     }
   }
 #undef BFP8_LAUNCH
+  return BFP8_ERR_SCALE_MODE;
 }
 
 // Split-K plan for shapes whose 256x256 tiles under-fill the chip: choose
@@ -1026,32 +1025,30 @@ bfp8_status launch_gemm(const GemmArgs& a, void* workspace, size_t workspace_byt
   const int64_t ldp = split_ldp(a.N);
   const dim3 grid(static_cast<unsigned>(nblk), static_cast<unsigned>(S));
   const int tm = static_cast<int>(tiles_m), tn = static_cast<int>(tiles_n);
+  bfp8_status st;
   if (a.mx) {
-    if (!a.a_kmajor && !a.b_kmajor) launch_layout<false, false, true>(a, grid, tm, tn, part, ldp, stream);
-    else if (!a.a_kmajor && a.b_kmajor) launch_layout<false, true, true>(a, grid, tm, tn, part, ldp, stream);
-    else if (a.a_kmajor && a.b_kmajor) launch_layout<true, true, true>(a, grid, tm, tn, part, ldp, stream);
+    if (!a.a_kmajor && !a.b_kmajor) st = launch_layout<false, false, true>(a, grid, tm, tn, part, ldp, stream);
+    else if (!a.a_kmajor && a.b_kmajor) st = launch_layout<false, true, true>(a, grid, tm, tn, part, ldp, stream);
+    else if (a.a_kmajor && a.b_kmajor) st = launch_layout<true, true, true>(a, grid, tm, tn, part, ldp, stream);
     else return BFP8_ERR_LAYOUT;
   } else {
-    if (!a.a_kmajor && !a.b_kmajor) launch_layout<false, false, false>(a, grid, tm, tn, part, ldp, stream);
-    else if (!a.a_kmajor && a.b_kmajor) launch_layout<false, true, false>(a, grid, tm, tn, part, ldp, stream);
-    else if (a.a_kmajor && a.b_kmajor) launch_layout<true, true, false>(a, grid, tm, tn, part, ldp, stream);
+    if (!a.a_kmajor && !a.b_kmajor) st = launch_layout<false, false, false>(a, grid, tm, tn, part, ldp, stream);
+    else if (!a.a_kmajor && a.b_kmajor) st = launch_layout<false, true, false>(a, grid, tm, tn, part, ldp, stream);
+    else if (a.a_kmajor && a.b_kmajor) st = launch_layout<true, true, false>(a, grid, tm, tn, part, ldp, stream);
     else return BFP8_ERR_LAYOUT;
   }
-  if (S > 1) {
-    const int64_t n = a.M * ((a.N + 3) / 4);
-    splitk_reduce_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream>>>(
-        part, ldp, S, a.C, a.ldc, a.M, a.N);
-  }
-  return last_launch_status();
+  if (st != BFP8_OK || S == 1) return st;
+  const int64_t n = a.M * ((a.N + 3) / 4);
+  return launch(&splitk_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                stream, part, ldp, static_cast<int64_t>(S), a.C, a.ldc, a.M, a.N);
 }
 
 bfp8_status launch_fill_bf16_zero(uint16_t* C, int64_t M, int64_t N, int64_t ldc,
                                   hipStream_t stream) {
   const int64_t n = M * N;
   if (n == 0) return BFP8_OK;
-  fill_zero_bf16_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream>>>(
-      C, M, N, ldc);
-  return last_launch_status();
+  return launch(&fill_zero_bf16_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                stream, C, M, N, ldc);
 }
 
 }  // namespace bfp8

@@ -15,6 +15,8 @@
 // enough bytes in flight per CU, and reductions that stay in registers
 // (DPP within 16 lanes) or in a few LDS words.
 
+#include <stdlib.h>
+
 #include "common.h"
 
 namespace bfp8 {
@@ -412,8 +414,35 @@ __global__ __launch_bounds__(256 * CB) void quantize_dual_kernel(
   }
 }
 
-inline bfp8_status last_launch_status() {
-  return hipPeekAtLastError() == hipSuccess ? BFP8_OK : BFP8_ERR_HIP;
+// ---- opt-in input check (BFP8_DEBUG) ---------------------------------------
+// One flag word per GPU: set to 1 by any thread that finds a non-finite
+// input element.  Cleared by a kernel (not a memset) before each check.
+__device__ __align__(16) uint32_t nonfinite_flag[4];
+
+__global__ __launch_bounds__(64) void clear_flag_kernel(uint32_t* flag) {
+  if (threadIdx.x == 0) flag[0] = 0u;
+}
+
+// Grid-stride over the rows x cols elements of x (row stride ldx); exponent
+// field all ones marks Inf or NaN for both bf16 and float32.
+template <typename T>
+__global__ __launch_bounds__(256) void find_nonfinite_kernel(const T* __restrict__ x, int64_t ldx,
+                                                             int64_t rows, int64_t cols,
+                                                             uint32_t* flag) {
+  const int64_t n = rows * cols;
+  bool bad = false;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t r = i / cols, c = i - r * cols;
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t b = x[r * ldx + c];
+      bad |= (b & 0x7F80u) == 0x7F80u;
+    } else {
+      const uint32_t b = __float_as_uint(x[r * ldx + c]);
+      bad |= (b & 0x7F800000u) == 0x7F800000u;
+    }
+  }
+  if (bad) flag[0] = 1u;
 }
 
 }  // namespace
@@ -444,12 +473,12 @@ bfp8_status launch_quantize_act(const void* x, bfp8_in_dtype dt, int64_t rows, i
   const int64_t per_block = 16 * kActUnroll;
   int64_t blocks = (n_groups + per_block - 1) / per_block;
   if (blocks > 16384) blocks = 16384;
-  BFP8_DISPATCH((quantize_act_kernel<T, R, G>
-                 <<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(
-                     static_cast<const T*>(x), ldx, q, ldq,
-                     static_cast<typename ScaleRule<R>::type*>(s), static_cast<uint32_t>(gpr),
-                     static_cast<uint32_t>(n_groups))));
-  return last_launch_status();
+  bfp8_status st = BFP8_OK;
+  BFP8_DISPATCH((st = launch(&quantize_act_kernel<T, R, G>, dim3(static_cast<unsigned>(blocks)),
+                             dim3(256), stream, static_cast<const T*>(x), ldx, q, ldq,
+                             static_cast<typename ScaleRule<R>::type*>(s),
+                             static_cast<uint32_t>(gpr), static_cast<uint32_t>(n_groups))));
+  return st;
 }
 
 bfp8_status launch_quantize_act_transposed(const void* x, bfp8_in_dtype dt, int64_t rows,
@@ -459,10 +488,11 @@ bfp8_status launch_quantize_act_transposed(const void* x, bfp8_in_dtype dt, int6
   if (rows == 0 || cols == 0) return BFP8_OK;
   const int64_t tok_blocks = rows / kTrTok;
   dim3 grid(static_cast<unsigned>((cols + kTrCh - 1) / kTrCh), static_cast<unsigned>(tok_blocks));
-  BFP8_DISPATCH((quantize_act_t_kernel<T, R, G><<<grid, dim3(256), 0, stream>>>(
-      static_cast<const T*>(x), ldx, cols, qt, ldqt,
-      static_cast<typename ScaleRule<R>::type*>(st), tok_blocks)));
-  return last_launch_status();
+  bfp8_status status = BFP8_OK;
+  BFP8_DISPATCH((status = launch(&quantize_act_t_kernel<T, R, G>, grid, dim3(256), stream,
+                                 static_cast<const T*>(x), ldx, cols, qt, ldqt,
+                                 static_cast<typename ScaleRule<R>::type*>(st), tok_blocks)));
+  return status;
 }
 
 bfp8_status launch_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
@@ -476,16 +506,22 @@ bfp8_status launch_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t ro
   // slower on narrower inputs)
   if (dt == BFP8_IN_BF16 && ch_blocks % 2 == 0 && ch_blocks >= 48) {
     dim3 grid2(static_cast<unsigned>(ch_blocks / 2), static_cast<unsigned>(tok_blocks));
-    BFP8_DISPATCH((quantize_dual_kernel<uint16_t, R, G, 2><<<grid2, dim3(512), 0, stream>>>(
-        static_cast<const uint16_t*>(x), ldx, q, ldq, static_cast<typename ScaleRule<R>::type*>(s),
-        qt, ldqt, static_cast<typename ScaleRule<R>::type*>(st), ch_blocks, tok_blocks)));
-    return last_launch_status();
+    bfp8_status status = BFP8_OK;
+    BFP8_DISPATCH((status = launch(&quantize_dual_kernel<uint16_t, R, G, 2>, grid2, dim3(512),
+                                   stream, static_cast<const uint16_t*>(x), ldx, q, ldq,
+                                   static_cast<typename ScaleRule<R>::type*>(s), qt, ldqt,
+                                   static_cast<typename ScaleRule<R>::type*>(st), ch_blocks,
+                                   tok_blocks)));
+    return status;
   }
   dim3 grid(static_cast<unsigned>(ch_blocks), static_cast<unsigned>(tok_blocks));
-  BFP8_DISPATCH((quantize_dual_kernel<T, R, G, 1><<<grid, dim3(256), 0, stream>>>(
-      static_cast<const T*>(x), ldx, q, ldq, static_cast<typename ScaleRule<R>::type*>(s), qt,
-      ldqt, static_cast<typename ScaleRule<R>::type*>(st), ch_blocks, tok_blocks)));
-  return last_launch_status();
+  bfp8_status status = BFP8_OK;
+  BFP8_DISPATCH((status = launch(&quantize_dual_kernel<T, R, G, 1>, grid, dim3(256), stream,
+                                 static_cast<const T*>(x), ldx, q, ldq,
+                                 static_cast<typename ScaleRule<R>::type*>(s), qt, ldqt,
+                                 static_cast<typename ScaleRule<R>::type*>(st), ch_blocks,
+                                 tok_blocks)));
+  return status;
 }
 
 bfp8_status launch_quantize_weight_batch(const WeightBatch& b, bfp8_in_dtype dt, int rule,
@@ -494,13 +530,11 @@ bfp8_status launch_quantize_weight_batch(const WeightBatch& b, bfp8_in_dtype dt,
   if (blocks == 0) return BFP8_OK;
   const dim3 grid(static_cast<unsigned>(blocks)), block(256);
   if (dt == BFP8_IN_BF16) {
-    if (rule == 0) quantize_weight_batch_kernel<uint16_t, 0><<<grid, block, 0, stream>>>(b);
-    else quantize_weight_batch_kernel<uint16_t, 1><<<grid, block, 0, stream>>>(b);
-  } else {
-    if (rule == 0) quantize_weight_batch_kernel<float, 0><<<grid, block, 0, stream>>>(b);
-    else quantize_weight_batch_kernel<float, 1><<<grid, block, 0, stream>>>(b);
+    if (rule == 0) return launch(&quantize_weight_batch_kernel<uint16_t, 0>, grid, block, stream, b);
+    return launch(&quantize_weight_batch_kernel<uint16_t, 1>, grid, block, stream, b);
   }
-  return last_launch_status();
+  if (rule == 0) return launch(&quantize_weight_batch_kernel<float, 0>, grid, block, stream, b);
+  return launch(&quantize_weight_batch_kernel<float, 1>, grid, block, stream, b);
 }
 
 bfp8_status launch_quantize_weight(const void* w, bfp8_in_dtype dt, int64_t rows, int64_t cols,
@@ -511,13 +545,46 @@ bfp8_status launch_quantize_weight(const void* w, bfp8_in_dtype dt, int64_t rows
   const int64_t cb = (cols + kGroup - 1) / kGroup;
   dim3 grid(static_cast<unsigned>(cb), static_cast<unsigned>(rb));
   const int group = 128;
-  BFP8_DISPATCH((quantize_weight_kernel<T, R><<<grid, dim3(256), 0, stream>>>(
-      static_cast<const T*>(w), ldw, rows, cols, q, ldq,
-      static_cast<typename ScaleRule<R>::type*>(s), cb)));
+  bfp8_status status = BFP8_OK;
+  BFP8_DISPATCH((status = launch(&quantize_weight_kernel<T, R>, grid, dim3(256), stream,
+                                 static_cast<const T*>(w), ldw, rows, cols, q, ldq,
+                                 static_cast<typename ScaleRule<R>::type*>(s), cb)));
   (void)group;
-  return last_launch_status();
+  return status;
 }
 
 #undef BFP8_DISPATCH
+
+bool debug_checks_enabled() {
+  static const bool on = [] {
+    const char* v = getenv("BFP8_DEBUG");
+    return v != nullptr && v[0] != '\0' && !(v[0] == '0' && v[1] == '\0');
+  }();
+  return on;
+}
+
+bfp8_status check_finite(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
+                         hipStream_t stream) {
+  if (rows == 0 || cols == 0) return BFP8_OK;
+  void* flag = nullptr;
+  if (hipGetSymbolAddress(&flag, HIP_SYMBOL(nonfinite_flag)) != hipSuccess) return BFP8_ERR_HIP;
+  uint32_t* f = static_cast<uint32_t*>(flag);
+  bfp8_status st = launch(&clear_flag_kernel, dim3(1), dim3(64), stream, f);
+  if (st != BFP8_OK) return st;
+  int64_t blocks = (rows * cols + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  const dim3 grid(static_cast<unsigned>(blocks));
+  st = dt == BFP8_IN_BF16
+           ? launch(&find_nonfinite_kernel<uint16_t>, grid, dim3(256), stream,
+                    static_cast<const uint16_t*>(x), ldx, rows, cols, f)
+           : launch(&find_nonfinite_kernel<float>, grid, dim3(256), stream,
+                    static_cast<const float*>(x), ldx, rows, cols, f);
+  if (st != BFP8_OK) return st;
+  uint32_t host = 0;
+  if (hipMemcpyAsync(&host, f, sizeof(host), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return BFP8_ERR_HIP;
+  return host != 0u ? BFP8_ERR_NONFINITE : BFP8_OK;
+}
 
 }  // namespace bfp8

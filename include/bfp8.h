@@ -52,8 +52,21 @@
  *
  * Errors: every entry point validates its arguments on the host BEFORE any
  * HIP call and returns a bfp8_status; nothing aborts or throws.  A launch
- * failure returns BFP8_ERR_HIP (the HIP error stays readable through
- * hipGetLastError / hipPeekAtLastError).
+ * failure returns BFP8_ERR_HIP.  The status is that of the call's own
+ * launches (the return value of hipLaunchKernel), never an error an earlier,
+ * unrelated HIP call left behind.  HIP also records a failed launch as the
+ * calling thread's last error; the library never clears it, the caller reads
+ * and clears it with hipGetLastError.
+ *
+ * Debug mode: with the environment variable BFP8_DEBUG set (to anything but
+ * "" or "0"; read once per process), every quantiser first scans its input
+ * for Inf / NaN, waits for the answer (a stream synchronisation) and returns
+ * BFP8_ERR_NONFINITE, launching nothing, if it finds one.  Off by default:
+ * the check costs a read of the input and a host round trip, and breaks the
+ * never-synchronise contract, so it is for debugging only (not under graph
+ * capture; concurrent debug-mode calls on one GPU share one flag word).
+ * Without it, non-finite inputs are outside the contract (output
+ * unspecified, no fault).
  *
  * Preconditions common to all calls: pointers of non-empty operands are
  * non-null and 16-byte aligned; leading dimensions are >= the row length
@@ -73,7 +86,7 @@
 extern "C" {
 #endif
 
-#define BFP8_ABI_VERSION 3
+#define BFP8_ABI_VERSION 4
 
 typedef enum {
   BFP8_OK = 0,
@@ -84,7 +97,8 @@ typedef enum {
   BFP8_ERR_LAYOUT = 5,      /* unknown GEMM layout                         */
   BFP8_ERR_SCALE_MODE = 6,  /* unknown scale mode                          */
   BFP8_ERR_WORKSPACE = 7,   /* workspace smaller than required             */
-  BFP8_ERR_HIP = 8          /* a HIP launch failed                         */
+  BFP8_ERR_HIP = 8,         /* a HIP launch failed                         */
+  BFP8_ERR_NONFINITE = 9    /* Inf / NaN input (only with BFP8_DEBUG set)  */
 } bfp8_status;
 
 typedef enum { BFP8_IN_BF16 = 0, BFP8_IN_F32 = 1 } bfp8_in_dtype;

@@ -49,9 +49,12 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.bfp8_abi_version() == 3
-    for code in range(9):
+    assert L.bfp8_abi_version() == 4
+    for code in range(10):
         assert len(L.bfp8_status_str(code)) > 0
+    assert b"Inf or NaN" in L.bfp8_status_str(9)
+    src = open(HEADER).read()
+    assert "BFP8_ERR_NONFINITE = 9" in src and bfp8.STATUS[9] == "BFP8_ERR_NONFINITE"
     assert L.bfp8_status_str(99) == b"unknown status"
 
 
