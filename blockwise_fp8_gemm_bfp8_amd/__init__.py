@@ -37,6 +37,8 @@ __all__ = [
     "quantize_weight_batch",
     "gemm",
     "gemm_workspace_bytes",
+    "gemm_static_scratch",
+    "STATIC_SCRATCH_BYTES",
     "quantize_mx_act",
     "quantize_mx_act_transposed",
     "quantize_mx_act_dual",
@@ -87,6 +89,8 @@ _SIGNATURES = {
     "bfp8_quantize_mx_weight_batch": [_vp, _int, _int, _vp],
     "bfp8_gemm_mx": [_int, _i64, _i64, _i64, _vp, _i64, _vp, _int, _vp, _i64, _vp, _int, _vp,
                      _i64, _vp, ctypes.c_size_t, _vp],
+    "bfp8_gemm_static_scratch": [_int, _i64, _i64, _i64, _vp, _i64, _vp, _int, _vp, _i64, _vp,
+                                 _int, _vp, _i64, _vp],
     "bfp8_status_str": [_int],
     "bfp8_abi_version": [],
 }
@@ -96,6 +100,7 @@ _RESTYPES = {
 }
 
 MAX_WEIGHT_JOBS = 16  # BFP8_MAX_WEIGHT_JOBS
+STATIC_SCRATCH_BYTES = 64 << 20  # BFP8_STATIC_SCRATCH_BYTES
 
 
 class WeightJob(ctypes.Structure):
@@ -298,6 +303,27 @@ def gemm(layout: str, qa, sa, qb, sb, mode_a: str = "act", mode_b: str = "block"
         LAYOUTS[layout], M, N, K, qa.data_ptr(), qa.stride(0), sa.data_ptr(), MODES[mode_a],
         qb.data_ptr(), qb.stride(0), sb.data_ptr(), MODES[mode_b], out.data_ptr(),
         out.stride(0), workspace.data_ptr() if ws_bytes else None, ws_bytes, _stream(qa)))
+    return out
+
+
+def gemm_static_scratch(layout: str, qa, sa, qb, sb, mode_a: str = "act",
+                        mode_b: str = "block", out: torch.Tensor = None):
+    """bfp8_gemm with its split-K partials in the library's static device
+    array (no workspace, no allocation inside the library); see
+    bfp8_gemm_static_scratch.  Raises BFP8Error (BFP8_ERR_WORKSPACE) when the
+    problem's partials exceed STATIC_SCRATCH_BYTES."""
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    M, N, K = gemm_dims(layout, qa, qb)
+    for name, sc in (("sa", sa), ("sb", sb)):
+        if not sc.is_contiguous() or sc.dtype != torch.float32:
+            raise ValueError(f"{name} must be a dense float32 tensor")
+    if out is None:
+        out = _padded_empty(M, N, torch.bfloat16, qa.device, 8)
+    _check("bfp8_gemm_static_scratch", lib().bfp8_gemm_static_scratch(
+        LAYOUTS[layout], M, N, K, qa.data_ptr(), qa.stride(0), sa.data_ptr(), MODES[mode_a],
+        qb.data_ptr(), qb.stride(0), sb.data_ptr(), MODES[mode_b], out.data_ptr(),
+        out.stride(0), _stream(qa)))
     return out
 
 

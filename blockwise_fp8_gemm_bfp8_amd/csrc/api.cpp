@@ -56,7 +56,8 @@ inline int mode_index(bfp8_scale_mode m) {
 bfp8_status gemm_common(bfp8_layout layout, int64_t M, int64_t N, int64_t K, const uint8_t* A,
                         int64_t lda, const void* sA, bfp8_scale_mode modeA, const uint8_t* B,
                         int64_t ldb, const void* sB, bfp8_scale_mode modeB, void* C, int64_t ldc,
-                        void* workspace, size_t workspace_bytes, bool mx, hipStream_t stream) {
+                        void* workspace, size_t workspace_bytes, bool mx, hipStream_t stream,
+                        bool static_scratch = false) {
   if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return BFP8_ERR_SHAPE;
   if (M == 0 || N == 0) return BFP8_OK;
   if (C == nullptr) return BFP8_ERR_NULL;
@@ -94,6 +95,7 @@ bfp8_status gemm_common(bfp8_layout layout, int64_t M, int64_t N, int64_t K, con
   g.N = N;
   g.K = K;
   g.mx = mx;
+  if (static_scratch) return launch_gemm_static_scratch(g, stream);
   return launch_gemm(g, workspace, workspace_bytes, stream);
 }
 
@@ -156,7 +158,8 @@ const char* bfp8_status_str(bfp8_status status) {
     case BFP8_ERR_DTYPE: return "unknown input dtype";
     case BFP8_ERR_LAYOUT: return "unknown GEMM layout";
     case BFP8_ERR_SCALE_MODE: return "unknown scale mode";
-    case BFP8_ERR_WORKSPACE: return "workspace missing or too small";
+    case BFP8_ERR_WORKSPACE: return "workspace missing or too small (static-scratch GEMM: the "
+                                    "split-K partials exceed BFP8_STATIC_SCRATCH_BYTES)";
     case BFP8_ERR_HIP: return "HIP launch failed";
     case BFP8_ERR_NONFINITE: return "input holds Inf or NaN (reported only with BFP8_DEBUG set)";
   }
@@ -312,6 +315,19 @@ bfp8_status bfp8_gemm(bfp8_layout layout, int64_t M, int64_t N, int64_t K, const
     return BFP8_ERR_SCALE_MODE;
   return gemm_common(layout, M, N, K, A, lda, sA, modeA, B, ldb, sB, modeB, C, ldc, workspace,
                      workspace_bytes, false, stream);
+}
+
+bfp8_status bfp8_gemm_static_scratch(bfp8_layout layout, int64_t M, int64_t N, int64_t K,
+                                     const uint8_t* A, int64_t lda, const float* sA,
+                                     bfp8_scale_mode modeA, const uint8_t* B, int64_t ldb,
+                                     const float* sB, bfp8_scale_mode modeB, void* C, int64_t ldc,
+                                     hipStream_t stream) {
+  if (layout != BFP8_NN && layout != BFP8_NT && layout != BFP8_TN) return BFP8_ERR_LAYOUT;
+  if ((modeA != BFP8_SCALE_1x128 && modeA != BFP8_SCALE_128x128) ||
+      (modeB != BFP8_SCALE_1x128 && modeB != BFP8_SCALE_128x128))
+    return BFP8_ERR_SCALE_MODE;
+  return gemm_common(layout, M, N, K, A, lda, sA, modeA, B, ldb, sB, modeB, C, ldc, nullptr, 0,
+                     false, stream, true);
 }
 
 bfp8_status bfp8_gemm_mx(bfp8_layout layout, int64_t M, int64_t N, int64_t K, const uint8_t* A,

@@ -218,6 +218,9 @@ struct GemmArgs {
 
 bfp8_status launch_gemm(const GemmArgs& a, void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
+// bfp8_gemm with its split-K partials in the library's static device array:
+// BFP8_ERR_WORKSPACE (before any HIP call) if they would not fit.
+bfp8_status launch_gemm_static_scratch(const GemmArgs& a, hipStream_t stream);
 int gemm_splits(int64_t M, int64_t N, int64_t K);
 size_t gemm_split_workspace(int64_t M, int64_t N, int64_t K);
 bfp8_status launch_fill_bf16_zero(uint16_t* C, int64_t M, int64_t N, int64_t ldc,

@@ -44,6 +44,9 @@
 // (measured on gfx950) -- so the lane's byte is always its row's scale of
 // chunk j = lane / 16.
 
+#include <atomic>
+#include <mutex>
+
 #include "common.h"
 
 namespace bfp8 {
@@ -1041,6 +1044,52 @@ bfp8_status launch_gemm(const GemmArgs& a, void* workspace, size_t workspace_byt
   const int64_t n = a.M * ((a.N + 3) / 4);
   return launch(&splitk_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
                 stream, part, ldp, static_cast<int64_t>(S), a.C, a.ldc, a.M, a.N);
+}
+
+// ---- split-K partials in a static device array -------------------------
+// For callers that cannot allocate (bfp8_gemm_static_scratch): the float32
+// split-K partials live in this file-scope array instead of a caller
+// workspace.  Each GPU the library runs on holds its own copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the
+// device memory: its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[BFP8_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the calling thread's current device.
+bfp8_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BFP8_ERR_HIP;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+        return BFP8_ERR_HIP;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return BFP8_OK;
+}
+}  // namespace
+
+bfp8_status launch_gemm_static_scratch(const GemmArgs& a, hipStream_t stream) {
+  const size_t need = gemm_split_workspace(a.M, a.N, a.K);
+  if (need > static_cast<size_t>(BFP8_STATIC_SCRATCH_BYTES)) return BFP8_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    const bfp8_status st = scratch_address(&ws);
+    if (st != BFP8_OK) return st;
+  }
+  // every split writes all of its partials before the reduction reads them,
+  // so nothing in the array needs clearing between calls
+  return launch_gemm(a, ws, need, stream);
 }
 
 bfp8_status launch_fill_bf16_zero(uint16_t* C, int64_t M, int64_t N, int64_t ldc,

@@ -290,6 +290,31 @@ bfp8_status bfp8_gemm_mx(bfp8_layout layout, int64_t M, int64_t N, int64_t K, co
                          int64_t ldc, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
+/*
+ * For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: bfp8_gemm
+ * with no workspace argument and the same split-K plan, its float32 split-K
+ * partials kept in a static device array of the library (one array of
+ * BFP8_STATIC_SCRATCH_BYTES per GPU the library runs on, held until the
+ * process ends).  Results are bit-identical to bfp8_gemm given the workspace
+ * bfp8_gemm_workspace_bytes asks for.  Arguments, layouts and errors as for
+ * bfp8_gemm; in addition BFP8_ERR_WORKSPACE, before any HIP call and with
+ * nothing launched, when the problem's split-K partials
+ * (bfp8_gemm_workspace_bytes) exceed BFP8_STATIC_SCRATCH_BYTES -- such a
+ * problem can run allocation-free through bfp8_gemm with a NULL workspace
+ * (unsplit).  Allocates nothing and never synchronises.  The array's device
+ * address is looked up on the calling thread's current device, which must be
+ * the stream's device.  Every call on one GPU uses that GPU's one array:
+ * calls that overlap in time on one GPU (concurrent streams, or threads)
+ * race on it and must be serialised by the caller.
+ */
+#define BFP8_STATIC_SCRATCH_BYTES (64u << 20)
+bfp8_status bfp8_gemm_static_scratch(bfp8_layout layout, int64_t M, int64_t N, int64_t K,
+                                     const uint8_t* A, int64_t lda, const float* sA,
+                                     bfp8_scale_mode modeA, const uint8_t* B, int64_t ldb,
+                                     const float* sB, bfp8_scale_mode modeB, void* C, int64_t ldc,
+                                     hipStream_t stream);
+
 /* Workspace bytes that let bfp8_gemm (or bfp8_gemm_mx) use its split-K plan
  * for this problem (0 when the problem runs unsplit).  Returns (size_t)-1 for
  * an invalid layout, scale mode or size. */

@@ -40,7 +40,8 @@ def test_header_declares_the_boundary():
                             "bfp8_quantize_mx_act", "bfp8_quantize_mx_act_transposed",
                             "bfp8_quantize_mx_act_dual", "bfp8_quantize_mx_weight",
                             "bfp8_quantize_mx_weight_batch",
-                            "bfp8_gemm_mx", "bfp8_status_str", "bfp8_abi_version"])
+                            "bfp8_gemm_mx", "bfp8_gemm_static_scratch",
+                            "bfp8_status_str", "bfp8_abi_version"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -259,3 +260,19 @@ def test_gemm_mx_errors(L):
     assert gemm_mx(L, sB=P + 1) == ALIGN
     assert gemm_mx(L, M=0, A=None, B=None, C=None) == OK
     assert L.bfp8_gemm_workspace_bytes(1, 2, 2, 8192, 4096, 2048) == 0
+
+
+def test_static_scratch_gemm_rejects_before_any_launch(L):
+    """bfp8_gemm_static_scratch validates like bfp8_gemm and refuses, on the
+    host, a problem whose split-K partials exceed the static array."""
+    def call(layout=1, M=12288, N=2048, K=16384, A=P, sA=P, ma=0, B=P, sB=P, mb=0, C=P, ldc=2048):
+        return L.bfp8_gemm_static_scratch(layout, M, N, K, A, K, sA, ma, B, K, sB, mb, C, ldc,
+                                          None)
+    assert call(layout=7) == LAYOUT
+    assert call(ma=2) == SMODE
+    assert call(C=None) == NULL
+    assert call(K=100) == SHAPE
+    assert bfp8.gemm_workspace_bytes("NT", "act", "act", 12288, 2048, 16384) > bfp8.STATIC_SCRATCH_BYTES
+    assert call() == WS
+    assert "BFP8_STATIC_SCRATCH_BYTES (64u << 20)" in open(HEADER).read()
+    assert bfp8.STATIC_SCRATCH_BYTES == 64 << 20
