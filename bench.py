@@ -1,30 +1,54 @@
 """Benchmark: blockwise-FP8 linear layers (quantise + GEMM) on one MI355X.
 
-A step is one full pass of the hot path over one batch of synthetic input:
-for each of the four linears of a Puro-2B decoder layer at M = 16384 tokens
-(QKV 2048->4096, o_proj 2048->2048, gate/up 2048->12288, down 6144->2048):
-weight quantisation, activation quantisation and the fprop GEMM; gradient
-quantisation and the dgrad GEMM; token-axis quantisation of dY and X and the
-wgrad GEMM -- 12 GEMMs, 4.95 TFLOP.  Inputs are resident in HBM before the
-timed region.  Prints ONE JSON line on stdout; details go to stderr.
+A step is one full pass of the hot path over one batch of synthetic input.
+The default workload is one Puro-2B decoder layer's four linears at M = 16384
+tokens (QKV 2048->4096, o_proj 2048->2048, gate/up 2048->12288, down
+6144->2048): weight quantisation, activation quantisation and the fprop GEMM;
+gradient quantisation and the dgrad GEMM; token-axis quantisation of dY and X
+and the wgrad GEMM -- 12 GEMMs, 4.95 TFLOP.  Inputs are resident in HBM before
+any timed region.  Prints ONE JSON line on stdout; details go to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--scales fp32|mx128|mx32] [--no-cpu-baseline] [--no-bf16-baseline]
-                  [--copy-calibration]
+                  [--scales fp32|mx128|mx32] [--reps R] [--no-sweep]
+                  [--no-cpu-baseline] [--no-bf16-baseline] [--copy-calibration]
+
+Phases, in order (each after a synchronisation):
+  1. W warm-up passes;
+  2. the headline: exactly K passes bracketed by synchronisations; `value` is
+     the workload's flops per pass over the mean pass time.  Each pass is also
+     bracketed by a pair of HIP events (fence-free, on the launch stream), which
+     give the median and p10/p90 of the pass time;
+  3. an instrumented copy of the same K passes, every kernel call bracketed
+     by its own pair of events: the mean launch time per kernel, from which
+     `roofline` (the GEMM family) and `quant_roofline` (the quantisers) are
+     computed;
+  4. a per-call sweep (unless --no-sweep): every kernel call of the pass run R
+     times (default 50), each repetition after a read of a 1 GiB buffer that
+     flushes the L2 caches and the 256 MB last-level cache, giving cold
+     median / p10 / p90 per call, the per-GEMM TFLOP/s including the share of
+     quantisation that feeds it, 2MNK / (t_act_quant + t_gemm), and the weight
+     quantisation time amortised over the 64 micro-batches of one optimizer step.
+  5. a clock window: passes back to back for about 2 s while amd-smi samples
+     the graphics clock and the socket power (`clock`), with the sustained
+     throughput of that window.
 
 --scales picks the scale format of the pass: fp32 (float32 amax/448 scales,
 promotion on the VALU; the default and the headline), mx128 (the same groups
-with power-of-two E8M0 scales applied by the scaled MFMA) or mx32 (MXFP8,
-1x32 power-of-two groups).  The line also carries `bf16_baseline`: the same
-12 GEMMs on the unquantised bf16 tensors through torch.matmul (hipBLASLt),
-timed the same way, for the FP8-over-BF16 ratio.
+with power-of-two E8M0 scales applied by the scaled MFMA) or mx32 (MXFP8, 1x32
+power-of-two groups).  The line also carries `bf16_baseline`: the same GEMMs on
+the unquantised bf16 tensors through torch.matmul (hipBLASLt), timed the same
+way, for the FP8-over-BF16 ratio.
 """
 
 import argparse
 import hashlib
 import json
 import os
+import platform
+import statistics
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -32,7 +56,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "blockwise-FP8 GEMM TFLOP/s incl. quantize at Puro-2B shapes; % FP8 MFMA peak"
 FP8_DENSE_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, published
-HBM_PEAK_GBS = 8000.0
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+MICROBATCHES_PER_STEP = 64      # 1536 sequences / (12 data-parallel ranks x 2 per micro-batch)
 DEFAULT_WORKLOAD = "layer_fwd_bwd_m16384"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 GEMM_SOURCE = os.path.join(ROOT, "blockwise_fp8_gemm_bfp8_amd", "csrc", "gemm.hip")
@@ -40,6 +65,16 @@ GEMM_SOURCE = os.path.join(ROOT, "blockwise_fp8_gemm_bfp8_amd", "csrc", "gemm.hi
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def pct(xs, q):
+    """q-th percentile (0..100) by linear interpolation."""
+    xs = sorted(xs)
+    if not xs:
+        return None
+    k = (len(xs) - 1) * q / 100.0
+    lo, hi = int(k), min(int(k) + 1, len(xs) - 1)
+    return xs[lo] + (xs[hi] - xs[lo]) * (k - lo)
 
 
 def gemm_source_hash():
@@ -60,10 +95,79 @@ def load_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
+class ClockSampler:
+    """amd-smi in a background thread: graphics clock (mean over the XCDs) and
+    socket power, sampled back to back while the GPU work runs."""
+
+    def __init__(self):
+        self.samples = []
+        self._stop = threading.Event()
+        self._t = None
+
+    def _one(self):
+        out = subprocess.run(["amd-smi", "metric", "-c", "-p", "--json"], capture_output=True,
+                             text=True, timeout=20)
+        data = json.loads(out.stdout)
+        gpus = data if isinstance(data, list) else data.get("gpu_data", [data])
+        g = gpus[0]
+        clocks = []
+        for k, v in g.get("clock", {}).items():
+            if k.startswith("gfx") and isinstance(v, dict):
+                c = v.get("clk", {})
+                c = c.get("value") if isinstance(c, dict) else c
+                if isinstance(c, (int, float)):
+                    clocks.append(float(c))
+        p = g.get("power", {}).get("socket_power", {})
+        p = p.get("value") if isinstance(p, dict) else p
+        if clocks:
+            self.samples.append((time.perf_counter(), sum(clocks) / len(clocks),
+                                 float(p) if isinstance(p, (int, float)) else None))
+
+    def _loop(self):
+        while not self._stop.is_set():
+            try:
+                self._one()
+            except Exception:  # amd-smi missing or its output not understood
+                return
+
+    def start(self):
+        self._t = threading.Thread(target=self._loop, daemon=True)
+        self._t.start()
+
+    def stop(self):
+        self._stop.set()
+        if self._t is not None:
+            self._t.join(timeout=30)
+
+    def summary(self, t0, t1):
+        s = [x for x in self.samples if t0 <= x[0] <= t1]
+        if not s:
+            return None
+        clk = [x[1] for x in s]
+        pw = [x[2] for x in s if x[2] is not None]
+        return {"gfx_mhz_median": round(statistics.median(clk), 1), "gfx_mhz_min": min(clk),
+                "gfx_mhz_max": max(clk), "socket_power_w_median":
+                round(statistics.median(pw), 1) if pw else None, "samples": len(s),
+                "source": "amd-smi metric -c -p, mean over the 8 XCD clocks"}
+
+
+def host_facts(threads):
+    model = platform.processor() or None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "blas_threads": threads}
+
+
 def cpu_baseline(workload_name, tokens_sample, scales="fp32"):
     """The oracle (numpy, float64 GEMM) on the same workload with M cut to
     `tokens_sample` tokens: every quantiser and all GEMMs of the step."""
-    import numpy as np
+    import numpy as np  # noqa: F401
 
     import oracle
     from workloads import WORKLOADS, make_inputs, to_numpy_input
@@ -128,28 +232,32 @@ def cpu_baseline(workload_name, tokens_sample, scales="fp32"):
         "kind": "oracle",
         "sample": f"{workload_name} with M cut to {M} tokens (all quantisers and GEMMs of "
                   f"one step, {scales} scales, {flops / 1e9:.1f} GFLOP, {dt:.1f} s)",
+        "host": host_facts(int(threads)),
     }
 
 
 def bf16_baseline(tensors, wl, steps, fp8_value):
-    """The step's 12 GEMMs on the unquantised bf16 tensors via torch.matmul
+    """The step's GEMMs on the unquantised bf16 tensors via torch.matmul
     (hipBLASLt), no quantisation: fprop X W^T, dgrad dY W, wgrad dY^T X."""
     import torch
 
     # every operand contiguous: the transposes W^T and dY^T are materialised
     # once, outside the timed steps, so each product is a plain row-major
-    # matmul (transposed-view bf16 products are avoided altogether: their
-    # batched form has faulted on this software stack)
-    lin = [(tensors["x." + L.name], tensors["w." + L.name], tensors["dy." + L.name],
-            tensors["w." + L.name].t().contiguous(), tensors["dy." + L.name].t().contiguous())
+    # 2-D matmul
+    lin = [(tensors["x." + L.name], tensors["w." + L.name], tensors.get("dy." + L.name),
+            tensors["w." + L.name].t().contiguous(),
+            tensors["dy." + L.name].t().contiguous() if "dy." + L.name in tensors else None)
            for L in wl.linears]
 
     def step():
-        for x, _, _, wt, _ in lin:
-            torch.matmul(x, wt)
+        if "fprop" in wl.roles:
+            for x, _, _, wt, _ in lin:
+                torch.matmul(x, wt)
         for x, w, dy, _, dyt in lin:
-            torch.matmul(dy, w)
-            torch.matmul(dyt, x)
+            if "dgrad" in wl.roles:
+                torch.matmul(dy, w)
+            if "wgrad" in wl.roles:
+                torch.matmul(dyt, x)
 
     for _ in range(2):
         step()
@@ -162,8 +270,122 @@ def bf16_baseline(tensors, wl, steps, fp8_value):
     value = wl.flops / dt / 1e12
     log(f"[bench] bf16 baseline (torch.matmul): {dt * 1e3:.3f} ms per step, {value:.1f} TFLOP/s")
     return {"value": round(value, 2), "unit": "TFLOP/s", "ms_per_step": round(dt * 1e3, 4),
-            "kind": "the same 12 GEMMs in bf16 via torch.matmul (hipBLASLt), unquantised",
+            "kind": "the same GEMMs in bf16 via torch.matmul (hipBLASLt), unquantised",
             "fp8_over_bf16": round(fp8_value / value, 3)}
+
+
+def family_roofline(hp, mean_us, kind, fields):
+    """Roofline of one kernel family from the instrumented passes: the mean
+    algorithmic work per launch over the mean launch time."""
+    idx = [i for i, op in enumerate(hp.ops) if op.kind in kind]
+    if not idx:
+        return None
+    t = sum(mean_us[i] for i in idx) / len(idx)
+    if fields == "flops":
+        work = sum(hp.ops[i].flops for i in idx) / len(idx)
+        ach = work / (t * 1e-6) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 1), "peak": FP8_DENSE_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / FP8_DENSE_PEAK_TFLOPS, 4),
+                "avg_launch_us": round(t, 2), "launches_per_step": len(idx),
+                "algorithmic_flops_per_launch": int(work)}
+    work = sum(hp.ops[i].bytes for i in idx) / len(idx)
+    ach = work / (t * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "avg_launch_us": round(t, 2),
+            "launches_per_step": len(idx), "algorithmic_bytes_per_launch": int(work)}
+
+
+def sweep(hp, reps):
+    """Every kernel call of the pass, `reps` times, each after a read of a
+    1 GiB buffer that evicts the L2 caches and the 256 MB last-level cache
+    (a read, so no dirty lines are left for the timed call to write back):
+    cold median / p10 / p90 in microseconds."""
+    import torch
+
+    from blockwise_fp8_gemm_bfp8_amd.hotpath import TimingEvent
+
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    out = []
+    for op in hp.ops:
+        evs = []
+        for _ in range(reps):
+            torch.sum(flush, dim=(0,), out=sink)
+            s, e = TimingEvent(), TimingEvent()
+            s.record()
+            op.fn()
+            e.record()
+            evs.append((s, e))
+        torch.cuda.synchronize()
+        us = [s.elapsed_time(e) * 1e3 for s, e in evs]
+        out.append({"median": statistics.median(us), "p10": pct(us, 10), "p90": pct(us, 90)})
+    del flush
+    return out
+
+
+def _short_kernel_name(name):
+    """'void ns::(anonymous namespace)::gemm_kernel<false, true, 0, 1>(args)' ->
+    'gemm_kernel<false, true, 0, 1>'."""
+    import re
+
+    m = re.search(r"(\w+)(<[^()]*>)?\(", name)
+    return (m.group(1) + (m.group(2) or "")) if m else name[:80]
+
+
+def summarize_trace(db, warmup, steps):
+    """Markdown summary of a rocprofv3 --kernel-trace database of this
+    script: every kernel over the whole run, then the timed passes alone.
+
+    The first dispatches of the run are the W warm-up passes, then the K
+    headline passes, then the K instrumented passes; a pass is found as the
+    period of the dispatch sequence.  A GEMM call is its gemm kernel plus the
+    split-K reduction that follows it, which is what the line's event timing
+    brackets."""
+    import sqlite3
+
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, duration from kernels order by start").fetchall()
+    names = [_short_kernel_name(r[0]) for r in rows]
+    dur = [r[1] / 1e3 for r in rows]  # us
+    total = warmup + 2 * steps
+    period = None
+    for p in range(1, 400):
+        if total * p <= len(names) and all(names[i] == names[i + p] for i in range((total - 1) * p)):
+            period = p
+            break
+    lines = ["| kernel | calls | total us | avg us | % |", "|---|---|---|---|---|"]
+    agg = {}
+    for n, d in zip(names, dur):
+        a = agg.setdefault(n, [0, 0.0])
+        a[0] += 1
+        a[1] += d
+    grand = sum(a[1] for a in agg.values())
+    for n, (c, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        lines.append(f"| `{n}` | {c} | {t:.1f} | {t / c:.2f} | {100 * t / grand:.1f} |")
+    out = ["Every dispatch of the run:", ""] + lines
+    if period is None:
+        out += ["", "(no periodic pass structure found for the given --warmup / --steps)"]
+        return "\n".join(out)
+    a0, a1 = warmup * period, (warmup + steps) * period
+    calls, kern = [], []
+    per = {}
+    for i in range(a0, a1):
+        n = names[i]
+        per.setdefault(n, []).append(dur[i])
+        if n.startswith("gemm_kernel") or n.startswith("gemm_mx4_kernel"):
+            calls.append(dur[i])
+            kern.append(dur[i])
+        elif n.startswith("splitk_reduce") and calls:
+            calls[-1] += dur[i]
+    out += ["", f"The {steps} headline passes alone (dispatches {a0}..{a1 - 1}, {period} per pass):",
+            "", "| kernel | calls | avg us | median us |", "|---|---|---|---|"]
+    for n, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"| `{n}` | {len(v)} | {sum(v) / len(v):.2f} | {statistics.median(v):.2f} |")
+    if calls:
+        out += ["", f"GEMM calls per pass: {len(calls) // steps}; mean GEMM call (kernel + its "
+                f"split-K reduction) {sum(calls) / len(calls):.2f} us; mean gemm kernel alone "
+                f"{sum(kern) / len(kern):.2f} us."]
+    return "\n".join(out)
 
 
 def main():
@@ -176,9 +398,20 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--scales", default="fp32", choices=["fp32", "mx128", "mx32"])
     ap.add_argument("--no-bf16-baseline", action="store_true")
+    ap.add_argument("--reps", type=int, default=50, help="repetitions per call in the sweep")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--clock-window", type=float, default=2.0,
+                    help="seconds of back-to-back passes sampled for the clock (0: none)")
+    ap.add_argument("--summarize-trace", metavar="DB",
+                    help="summarise a rocprofv3 kernel trace of this script (no GPU needed) "
+                         "and exit; --steps / --warmup must match the traced run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.warmup, args.steps))
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
@@ -192,19 +425,17 @@ def main():
 
     if not os.path.exists(_build.LIB_PATH):
         _build.build()
-    from blockwise_fp8_gemm_bfp8_amd.hotpath import HotPath
+    from blockwise_fp8_gemm_bfp8_amd.hotpath import HotPath, TimingEvent
     from workloads import WORKLOADS, make_inputs
 
     wl = WORKLOADS[args.workload]
     log(f"[bench] workload {wl.name}: generating inputs")
     tensors = {k: v.cuda() for k, v in make_inputs(wl.name).items()}
+    if args.scales != "fp32" and set(wl.roles) != {"fprop", "dgrad", "wgrad"}:
+        log("[bench] power-of-two scales run only on the full fprop + dgrad + wgrad layer")
+        sys.exit(2)
     hp = HotPath(tensors, [L.name for L in wl.linears], wl.roles, scales=args.scales)
     flops_step = wl.flops
-    # HotPath.run launches the GEMMs in this order:
-    order = [g for g in wl.gemms if g.role == "fprop"]
-    for L in wl.linears:
-        order += [g for g in wl.gemms if g.linear is L and g.role in ("dgrad", "wgrad")]
-    gemm_flops = [g.flops for g in order]
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -217,56 +448,136 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         log("[bench] copy calibration: 1 GiB read + 1 GiB write")
+        del a, b
 
+    # ---- phase 2: the headline -------------------------------------------
     log(f"[bench] timing {args.steps} steps")
-    hp.gemm_events = []
+    step_ev = [(TimingEvent(), TimingEvent()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for s, e in step_ev:
+        s.record()
         hp.run()
+        e.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed / args.steps * 1e3
     value = flops_step / (elapsed / args.steps) / 1e12
+    step_ms = [s.elapsed_time(e) for s, e in step_ev]
+    log(f"[bench] {ms_per_step:.3f} ms per step (wall), events median "
+        f"{statistics.median(step_ms):.3f} ms, {value:.1f} TFLOP/s")
 
-    durs = [s.elapsed_time(e) for s, e in hp.gemm_events]  # ms
-    n_g = len(gemm_flops)
-    per_gemm = {}
-    for i, d in enumerate(durs):
-        per_gemm.setdefault(i % n_g, []).append(d)
-    total_gemm_ms = sum(durs)
-    total_gemm_flops = sum(gemm_flops) * args.steps
-    avg_launch_ms = total_gemm_ms / len(durs)
-    avg_flops = sum(gemm_flops) / n_g
-    achieved = avg_flops / (avg_launch_ms * 1e-3) / 1e12
-    traffic = load_traffic()
-    roofline = {
-        "kernel": ("gemm_kernel (blockwise FP8 GEMM; mean over the step's GEMM launches)"
-                   if args.scales == "fp32" else
-                   f"gemm_kernel, E8M0 instantiation ({args.scales}; mean over the step's GEMM "
-                   "launches)"),
-        "bound": "mfma",
-        "achieved": round(achieved, 1),
-        "peak": FP8_DENSE_PEAK_TFLOPS,
-        "unit": "TFLOP/s",
-        "frac": round(achieved / FP8_DENSE_PEAK_TFLOPS, 4),
-        "traffic": traffic,
-        "avg_launch_us": round(avg_launch_ms * 1e3, 2),
-    }
-    for i, g in enumerate(order):
-        d = sum(per_gemm[i]) / len(per_gemm[i])
-        log(f"[bench] {g.linear.name:8s} {g.role:5s} {g.layout} M,N,K={g.mnk}: "
-            f"{d * 1e3:8.1f} us  {g.flops / (d * 1e-3) / 1e12:7.1f} TFLOP/s")
-    log(f"[bench] GEMM time {total_gemm_ms / args.steps:.3f} ms of {ms_per_step:.3f} ms per step")
+    # ---- phase 3: the same passes with every kernel call bracketed -----------
+    events = []
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        hp.run(events)
+    torch.cuda.synchronize()
+    per_op = {}
+    for i, s, e in events:
+        per_op.setdefault(i, []).append(s.elapsed_time(e) * 1e3)
+    mean_us = {i: sum(v) / len(v) for i, v in per_op.items()}
+    roofline = family_roofline(hp, mean_us, ("gemm",), "flops")
+    roofline["kernel"] = ("gemm_kernel: the blockwise FP8 GEMM launches of the step (float32 "
+                          "scales; each call's time includes its split-K reduction kernel "
+                          "where the call splits K)" if args.scales == "fp32" else
+                          f"gemm_mx4_kernel ({args.scales}; each call's time includes its "
+                          "split-K reduction kernel where the call splits K)")
+    roofline["traffic"] = load_traffic() if args.scales == "fp32" else None
+    qroof = family_roofline(hp, mean_us, ("quant", "weight_quant"), "bytes")
+    if qroof is not None:
+        qroof["kernel"] = ("the step's quantiser launches (activation, gradient and weight): "
+                           "mean algorithmic bytes per launch over the mean launch time")
+        qroof["per_call"] = [
+            {"call": hp.ops[i].label, "us": round(mean_us[i], 2),
+             "gbs": round(hp.ops[i].bytes / (mean_us[i] * 1e-6) / 1e9, 1),
+             "frac": round(hp.ops[i].bytes / (mean_us[i] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            for i in range(len(hp.ops)) if hp.ops[i].kind != "gemm"]
+
+    # ---- phase 4: cold per-call sweep ----------------------------------------
+    per_gemm = None
+    weight_quant = None
+    if not args.no_sweep:
+        log(f"[bench] sweep: {args.reps} cold repetitions of each of {len(hp.ops)} calls")
+        sw = sweep(hp, args.reps)
+        act_us = {}
+        for op, st in zip(hp.ops, sw):
+            for g, share in op.feeds:
+                act_us[g] = act_us.get(g, 0.0) + share * st["median"]
+        per_gemm = []
+        for op, st in zip(hp.ops, sw):
+            if op.kind != "gemm":
+                continue
+            tq = act_us.get(op.label, 0.0)
+            per_gemm.append({
+                "gemm": op.label, "layout": op.layout, "mnk": list(op.mnk),
+                "gemm_us": {k: round(v, 2) for k, v in st.items()},
+                "gemm_tflops": round(op.flops / (st["median"] * 1e-6) / 1e12, 1),
+                "act_quant_us": round(tq, 2),
+                "incl_quant_tflops": round(op.flops / ((st["median"] + tq) * 1e-6) / 1e12, 1)})
+            log(f"[bench] {op.label:15s} {op.layout} M,N,K={op.mnk}: median "
+                f"{st['median']:8.1f} us (p10 {st['p10']:.1f}, p90 {st['p90']:.1f})  "
+                f"{per_gemm[-1]['gemm_tflops']:7.1f} TFLOP/s; incl. quant "
+                f"{per_gemm[-1]['incl_quant_tflops']:7.1f}")
+        quant_cold = []
+        for op, st in zip(hp.ops, sw):
+            if op.kind == "gemm":
+                continue
+            gbs = op.bytes / (st["median"] * 1e-6) / 1e9
+            quant_cold.append({"call": op.label, "median_us": round(st["median"], 2),
+                               "p10_us": round(st["p10"], 2), "p90_us": round(st["p90"], 2),
+                               "gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)})
+            log(f"[bench] {op.label:22s} median {st['median']:7.1f} us  {gbs:7.1f} GB/s "
+                f"({100 * gbs / HBM_PEAK_GBS:.1f} % of HBM)")
+            if op.kind == "weight_quant":
+                weight_quant = (weight_quant or 0.0) + st["median"]
+        if qroof is not None:
+            qroof["cold_per_call"] = quant_cold
+    # ---- phase 5: clock window ------------------------------------------------
+    clocks = ClockSampler()
+    torch.cuda.synchronize()
+    clocks.start()
+    t_c0 = time.perf_counter()
+    n_win = 0
+    while time.perf_counter() - t_c0 < args.clock_window:
+        for _ in range(10):
+            hp.run()
+        torch.cuda.synchronize()
+        n_win += 10
+    t_c1 = time.perf_counter()
+    clocks.stop()
+    clock = clocks.summary(t_c0, t_c1)
+    if clock is not None:
+        clock["window_s"] = round(t_c1 - t_c0, 2)
+        clock["window_tflops"] = round(flops_step * n_win / (t_c1 - t_c0) / 1e12, 1)
+        log(f"[bench] clock window: {n_win} passes, {clock['window_tflops']} TFLOP/s, gfx "
+            f"{clock['gfx_mhz_median']} MHz median, {clock['socket_power_w_median']} W")
+
+    for i, op in enumerate(hp.ops):
+        if op.kind == "gemm":
+            log(f"[bench] in-pass {op.label:15s} {mean_us[i]:8.1f} us  "
+                f"{op.flops / (mean_us[i] * 1e-6) / 1e12:7.1f} TFLOP/s")
+    gemm_ms = sum(mean_us[i] for i, op in enumerate(hp.ops) if op.kind == "gemm") / 1e3
+    log(f"[bench] GEMM time {gemm_ms:.3f} ms of {statistics.median(step_ms):.3f} ms per step")
 
     bf16 = None
-    if not args.no_bf16_baseline and set(wl.roles) == {"fprop", "dgrad", "wgrad"}:
+    if not args.no_bf16_baseline:
         bf16 = bf16_baseline(tensors, wl, max(args.steps // 3, 3), value)
 
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
         cpu = cpu_baseline(wl.name, args.cpu_tokens, args.scales)
+
+    wq_amortised = None
+    if weight_quant is not None:
+        wq_amortised = {"weight_quant_us_per_step": round(weight_quant, 2),
+                        "amortised_us_per_microbatch": round(weight_quant / MICROBATCHES_PER_STEP, 3),
+                        "microbatches_per_optimizer_step": MICROBATCHES_PER_STEP,
+                        "value_with_amortised_weight_quant": round(
+                            flops_step / ((statistics.median(step_ms) - weight_quant * 1e-3
+                                           + weight_quant * 1e-3 / MICROBATCHES_PER_STEP) * 1e-3)
+                            / 1e12, 2)}
 
     line = {
         "metric": METRIC,
@@ -276,6 +587,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "step_ms": {"median": round(statistics.median(step_ms), 4),
+                    "p10": round(pct(step_ms, 10), 4), "p90": round(pct(step_ms, 90), 4),
+                    "source": "HIP events around each timed pass"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -287,11 +601,16 @@ def main():
             "workload": wl.name,
             "tokens": wl.tokens,
             "linears": {L.name: [L.in_features, L.out_features] for L in wl.linears},
+            "roles": wl.roles,
             "gemms_per_step": len(wl.gemms),
             "tflop_per_step": round(flops_step / 1e12, 4),
-            "includes": "weight, activation, gradient and token-axis quantisers + 12 GEMMs",
+            "includes": "weight, activation, gradient and token-axis quantisers + every GEMM",
         },
         "roofline": roofline,
+        "quant_roofline": qroof,
+        "per_gemm": per_gemm,
+        "weight_quant": wq_amortised,
+        "clock": clock,
         "cpu_baseline": cpu,
         "bf16_baseline": bf16,
     }

@@ -9,8 +9,10 @@ the Puro-2B paper translation (papers.lianghsun.dev), section 3.2:
 where a tensor needed in both layouts is read once (quantize_act_dual), and
 all the weights are quantised in one launch (quantize_weight_batch).
 All buffers (codes, scales, outputs, split-K workspaces) are allocated once, so a
-pass only enqueues kernels on the current stream.  This module only calls
-the binding; every step runs in libbfp8's kernels.
+pass only enqueues kernels on the current stream.  The pass is kept as a list of
+kernel calls with the work each does (flops, algorithmic bytes), which is what
+the benchmark times call by call.  This module only calls the binding; every
+step runs in libbfp8's kernels.
 
 `scales` selects the scale format:
   "fp32"  float32 amax/448 scales, per-128-K promotion on the VALU (the above);
@@ -26,7 +28,7 @@ the binding; every step runs in libbfp8's kernels.
 import ctypes
 import sys
 from dataclasses import dataclass, field
-from typing import Dict, List, Optional
+from typing import Callable, Dict, List, Optional, Tuple
 
 import torch
 
@@ -99,8 +101,36 @@ class LinearState:
     buf: Dict[str, torch.Tensor] = field(default_factory=dict)
 
 
+@dataclass
+class Op:
+    """One kernel call of the pass, with the work it does.
+
+    kind: 'gemm', 'quant' (activation / gradient quantiser) or 'weight_quant'.
+    flops: 2MNK for a GEMM (0 otherwise).  bytes: the algorithmic HBM bytes
+    -- inputs read once, codes and scales written once (for a GEMM: both code
+    operands, their scales and the bf16 output).  feeds: for a quantiser, the
+    GEMMs whose operands it writes, with the share of its time charged to
+    each (a dual quantiser serves two GEMMs, half each)."""
+
+    label: str
+    kind: str
+    fn: Callable[[], None]
+    flops: int = 0
+    bytes: int = 0
+    layout: str = ""
+    mnk: Tuple[int, int, int] = (0, 0, 0)
+    feeds: List[Tuple[str, float]] = field(default_factory=list)
+
+
+def _esize(t: torch.Tensor) -> int:
+    return t.element_size()
+
+
 class HotPath:
-    """Preallocated fprop/dgrad/wgrad pass over a list of linear layers."""
+    """Preallocated fprop/dgrad/wgrad pass over a list of linear layers.
+
+    The pass is a fixed list of kernel calls (`ops`) on preallocated buffers;
+    run() enqueues them in order on the current stream."""
 
     def __init__(self, tensors: Dict[str, torch.Tensor], names: List[str], roles: List[str],
                  scales: str = "fp32"):
@@ -115,7 +145,22 @@ class HotPath:
             L = LinearState(n, tensors["x." + n], tensors["w." + n], tensors.get("dy." + n))
             self._alloc(L)
             self.layers.append(L)
-        self.gemm_events = None
+        self.ops: List[Op] = self._build_ops() if scales == "fp32" else self._build_ops_mx()
+
+    def run(self, events: Optional[list] = None):
+        """Enqueue one full pass on the current stream.  With `events` (a
+        list), each kernel call is bracketed by a pair of TimingEvents and
+        (op index, start, end) is appended."""
+        if events is None:
+            for op in self.ops:
+                op.fn()
+            return
+        for i, op in enumerate(self.ops):
+            s, e = TimingEvent(), TimingEvent()
+            s.record()
+            op.fn()
+            e.record()
+            events.append((i, s, e))
 
     def _alloc(self, L: LinearState):
         if self.scales != "fp32":
@@ -174,88 +219,147 @@ class HotPath:
         nb = gemm_workspace_bytes("NT", mode, mode, dout, din, M)
         b["ws_wgrad"] = torch.empty((max(nb, 16),), dtype=u8, device=dev)
 
-    def _gemm(self, *args, **kw):
-        fn = gemm if self.scales == "fp32" else gemm_mx
-        ev = self.gemm_events
-        if ev is not None:
-            s = TimingEvent()
-            e = TimingEvent()
-            s.record()
-            out = fn(*args, **kw)
-            e.record()
-            ev.append((s, e))
-            return out
-        return fn(*args, **kw)
+    # ---- the pass as a list of kernel calls ---------------------------------
 
-    def run(self):
-        """Enqueue one full pass (every quantiser and GEMM) on the current stream.
-
-        When a pass has both fprop and wgrad, X is quantised once into both
-        layouts (the token-grouped codes are kept for wgrad, FP8 being the
-        activation storage format); likewise dY serves dgrad and wgrad from
-        one read."""
-        if self.scales != "fp32":
-            return self._run_mx()
-        both_x = "fprop" in self.roles and "wgrad" in self.roles
-        both_dy = "dgrad" in self.roles and "wgrad" in self.roles
-        # every weight's 128x128 blocks in one launch (the weights are
-        # independent of the rest of the pass)
+    def _build_ops(self) -> List[Op]:
+        """float32 scales.  When a pass has both fprop and wgrad, X is
+        quantised once into both layouts (the token-grouped codes are kept
+        for wgrad, FP8 being the activation storage format); likewise dY
+        serves dgrad and wgrad from one read.  Every weight's 128x128 blocks
+        are quantised in one launch (the weights are independent of the rest
+        of the pass)."""
+        ops: List[Op] = []
+        roles = self.roles
+        both_x = "fprop" in roles and "wgrad" in roles
+        both_dy = "dgrad" in roles and "wgrad" in roles
         for i in range(0, len(self.layers), MAX_WEIGHT_JOBS):
             group = self.layers[i:i + MAX_WEIGHT_JOBS]
-            quantize_weight_batch([L.w for L in group], [L.buf["wq"] for L in group],
-                                  [L.buf["ws"] for L in group])
-        for L in self.layers:
-            b = L.buf
-            if "fprop" in self.roles:
-                if both_x:
-                    quantize_act_dual(L.x, b["xq"], b["xs"], b["xqt"], b["xst"])
-                else:
-                    quantize_act(L.x, b["xq"], b["xs"])
-                self._gemm("NT", b["xq"], b["xs"], b["wq"], b["ws"], "act", "block", out=b["y"])
-        for L in self.layers:
-            b = L.buf
-            if both_dy:
-                quantize_act_dual(L.dy, b["dyq"], b["dys"], b["dyqt"], b["dyst"])
-            elif "dgrad" in self.roles:
-                quantize_act(L.dy, b["dyq"], b["dys"])
-            elif "wgrad" in self.roles:
-                quantize_act_transposed(L.dy, b["dyqt"], b["dyst"])
-            if "dgrad" in self.roles:
-                self._gemm("NN", b["dyq"], b["dys"], b["wq"], b["ws"], "act", "block",
-                           out=b["dx"])
-            if "wgrad" in self.roles:
-                if not both_x:
-                    quantize_act_transposed(L.x, b["xqt"], b["xst"])
-                self._gemm("NT", b["dyqt"], b["dyst"], b["xqt"], b["xst"], "act", "act",
-                           out=b["dw"], workspace=b["ws_wgrad"])
+            nbytes = sum(L.w.numel() * (_esize(L.w) + 1) + L.buf["ws"].numel() * 4 for L in group)
+            ops.append(Op("weights", "weight_quant",
+                          lambda g=group: quantize_weight_batch(
+                              [L.w for L in g], [L.buf["wq"] for L in g],
+                              [L.buf["ws"] for L in g]), bytes=nbytes))
 
-    def _run_mx(self):
+        def gemm_op(L, role, layout, a, sa, b, sb, ma, mb, out, M, N, K, ws=None):
+            nbytes = a.numel() + b.numel() + 4 * (sa.numel() + sb.numel()) + 2 * M * N
+            fn = (lambda: gemm(layout, a, sa, b, sb, ma, mb, out=out, workspace=ws)) if ws is not None \
+                else (lambda: gemm(layout, a, sa, b, sb, ma, mb, out=out))
+            return Op(f"{L.name}.{role}", "gemm", fn, flops=2 * M * N * K, bytes=nbytes,
+                      layout=layout, mnk=(M, N, K))
+
+        for L in self.layers:
+            b = L.buf
+            M, din = L.x.shape
+            dout = L.w.shape[0]
+            e = _esize(L.x)
+            if "fprop" in roles:
+                if both_x:
+                    ops.append(Op(f"{L.name}.x dual", "quant",
+                                  lambda L=L, b=b: quantize_act_dual(L.x, b["xq"], b["xs"],
+                                                                     b["xqt"], b["xst"]),
+                                  bytes=M * din * (e + 2) + 4 * (b["xs"].numel() + b["xst"].numel()),
+                                  feeds=[(f"{L.name}.fprop", 0.5), (f"{L.name}.wgrad", 0.5)]))
+                else:
+                    ops.append(Op(f"{L.name}.x act", "quant",
+                                  lambda L=L, b=b: quantize_act(L.x, b["xq"], b["xs"]),
+                                  bytes=M * din * (e + 1) + 4 * b["xs"].numel(),
+                                  feeds=[(f"{L.name}.fprop", 1.0)]))
+                ops.append(gemm_op(L, "fprop", "NT", b["xq"], b["xs"], b["wq"], b["ws"], "act",
+                                   "block", b["y"], M, dout, din))
+        for L in self.layers:
+            b = L.buf
+            M, din = L.x.shape
+            dout = L.w.shape[0]
+            e = _esize(L.x)
+            if both_dy:
+                ops.append(Op(f"{L.name}.dy dual", "quant",
+                              lambda L=L, b=b: quantize_act_dual(L.dy, b["dyq"], b["dys"],
+                                                                 b["dyqt"], b["dyst"]),
+                              bytes=M * dout * (e + 2) + 4 * (b["dys"].numel() + b["dyst"].numel()),
+                              feeds=[(f"{L.name}.dgrad", 0.5), (f"{L.name}.wgrad", 0.5)]))
+            elif "dgrad" in roles:
+                ops.append(Op(f"{L.name}.dy act", "quant",
+                              lambda L=L, b=b: quantize_act(L.dy, b["dyq"], b["dys"]),
+                              bytes=M * dout * (e + 1) + 4 * b["dys"].numel(),
+                              feeds=[(f"{L.name}.dgrad", 1.0)]))
+            elif "wgrad" in roles:
+                ops.append(Op(f"{L.name}.dy transposed", "quant",
+                              lambda L=L, b=b: quantize_act_transposed(L.dy, b["dyqt"], b["dyst"]),
+                              bytes=M * dout * (e + 1) + 4 * b["dyst"].numel(),
+                              feeds=[(f"{L.name}.wgrad", 1.0)]))
+            if "dgrad" in roles:
+                ops.append(gemm_op(L, "dgrad", "NN", b["dyq"], b["dys"], b["wq"], b["ws"], "act",
+                                   "block", b["dx"], M, din, dout))
+            if "wgrad" in roles:
+                if not both_x:
+                    ops.append(Op(f"{L.name}.x transposed", "quant",
+                                  lambda L=L, b=b: quantize_act_transposed(L.x, b["xqt"], b["xst"]),
+                                  bytes=M * din * (e + 1) + 4 * b["xst"].numel(),
+                                  feeds=[(f"{L.name}.wgrad", 1.0)]))
+                ops.append(gemm_op(L, "wgrad", "NT", b["dyqt"], b["dyst"], b["xqt"], b["xst"],
+                                   "act", "act", b["dw"], dout, din, M, ws=b["ws_wgrad"]))
+        return ops
+
+    def _build_ops_mx(self) -> List[Op]:
         """One fprop + dgrad + wgrad pass with power-of-two scales.  Every
         activation / gradient is quantised once into both layouts; with 1x32
         groups the weight is too (in-features groups for fprop, out-features
         groups for dgrad), otherwise its 128x128 blocks serve both GEMMs."""
         grp = 32 if self.scales == "mx32" else 128
         mode = "mx32" if grp == 32 else "act"
+        ops: List[Op] = []
+
+        def gemm_op(L, role, layout, a, sa, b, sb, ma, mb, out, M, N, K, ws=None):
+            nbytes = a.numel() + b.numel() + sa.numel() + sb.numel() + 2 * M * N
+            fn = (lambda: gemm_mx(layout, a, sa, b, sb, ma, mb, out=out, workspace=ws)) \
+                if ws is not None else (lambda: gemm_mx(layout, a, sa, b, sb, ma, mb, out=out))
+            return Op(f"{L.name}.{role}", "gemm", fn, flops=2 * M * N * K, bytes=nbytes,
+                      layout=layout, mnk=(M, N, K))
+
         if grp == 128:
             for i in range(0, len(self.layers), MAX_WEIGHT_JOBS):
                 group = self.layers[i:i + MAX_WEIGHT_JOBS]
-                quantize_mx_weight_batch([L.w for L in group], [L.buf["wq"] for L in group],
-                                         [L.buf["ws"] for L in group])
+                nbytes = sum(L.w.numel() * (_esize(L.w) + 1) + L.buf["ws"].numel() for L in group)
+                ops.append(Op("weights", "weight_quant",
+                              lambda g=group: quantize_mx_weight_batch(
+                                  [L.w for L in g], [L.buf["wq"] for L in g],
+                                  [L.buf["ws"] for L in g]), bytes=nbytes))
         for L in self.layers:
             b = L.buf
+            M, din = L.x.shape
+            dout = L.w.shape[0]
+            e = _esize(L.x)
             if grp == 32:
-                quantize_mx_act_dual(L.w, 32, b["wq"], b["ws"], b["wqt"], b["wst"])
+                ops.append(Op(f"{L.name}.w dual", "weight_quant",
+                              lambda L=L, b=b: quantize_mx_act_dual(L.w, 32, b["wq"], b["ws"],
+                                                                    b["wqt"], b["wst"]),
+                              bytes=L.w.numel() * (e + 2) + b["ws"].numel() + b["wst"].numel()))
                 wmode = "mx32"
             else:
                 wmode = "block"
-            quantize_mx_act_dual(L.x, grp, b["xq"], b["xs"], b["xqt"], b["xst"])
-            self._gemm("NT", b["xq"], b["xs"], b["wq"], b["ws"], mode, wmode, out=b["y"])
+            ops.append(Op(f"{L.name}.x dual", "quant",
+                          lambda L=L, b=b: quantize_mx_act_dual(L.x, grp, b["xq"], b["xs"],
+                                                                b["xqt"], b["xst"]),
+                          bytes=M * din * (e + 2) + b["xs"].numel() + b["xst"].numel(),
+                          feeds=[(f"{L.name}.fprop", 0.5), (f"{L.name}.wgrad", 0.5)]))
+            ops.append(gemm_op(L, "fprop", "NT", b["xq"], b["xs"], b["wq"], b["ws"], mode, wmode,
+                               b["y"], M, dout, din))
         for L in self.layers:
             b = L.buf
-            quantize_mx_act_dual(L.dy, grp, b["dyq"], b["dys"], b["dyqt"], b["dyst"])
+            M, din = L.x.shape
+            dout = L.w.shape[0]
+            e = _esize(L.x)
+            ops.append(Op(f"{L.name}.dy dual", "quant",
+                          lambda L=L, b=b: quantize_mx_act_dual(L.dy, grp, b["dyq"], b["dys"],
+                                                                b["dyqt"], b["dyst"]),
+                          bytes=M * dout * (e + 2) + b["dys"].numel() + b["dyst"].numel(),
+                          feeds=[(f"{L.name}.dgrad", 0.5), (f"{L.name}.wgrad", 0.5)]))
             if grp == 32:
-                self._gemm("NT", b["dyq"], b["dys"], b["wqt"], b["wst"], mode, "mx32", out=b["dx"])
+                ops.append(gemm_op(L, "dgrad", "NT", b["dyq"], b["dys"], b["wqt"], b["wst"], mode,
+                                   "mx32", b["dx"], M, din, dout))
             else:
-                self._gemm("NN", b["dyq"], b["dys"], b["wq"], b["ws"], mode, "block", out=b["dx"])
-            self._gemm("NT", b["dyqt"], b["dyst"], b["xqt"], b["xst"], mode, mode, out=b["dw"],
-                       workspace=b["ws_wgrad"])
+                ops.append(gemm_op(L, "dgrad", "NN", b["dyq"], b["dys"], b["wq"], b["ws"], mode,
+                                   "block", b["dx"], M, din, dout))
+            ops.append(gemm_op(L, "wgrad", "NT", b["dyqt"], b["dyst"], b["xqt"], b["xst"], mode,
+                               mode, b["dw"], dout, din, M, ws=b["ws_wgrad"]))
+        return ops
