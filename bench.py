@@ -19,8 +19,9 @@ Phases, in order (each after a synchronisation):
      bracketed by a pair of HIP events (fence-free, on the launch stream), which
      give the median and p10/p90 of the pass time;
   3. an instrumented copy of the same K passes, every kernel call bracketed
-     by its own pair of events: the mean launch time per kernel, from which
-     `roofline` (the GEMM family) and `quant_roofline` (the quantisers) are
+     by its own pair of events: each call's median launch time over the K
+     passes, from which `roofline` (the GEMM family: mean flops per launch
+     over mean launch time) and `quant_roofline` (the quantisers: bytes) are
      computed;
   4. a per-call sweep (unless --no-sweep): every kernel call of the pass run R
      times (default 50), each repetition after a read of a 1 GiB buffer that
@@ -276,7 +277,8 @@ def bf16_baseline(tensors, wl, steps, fp8_value):
 
 def family_roofline(hp, mean_us, kind, fields):
     """Roofline of one kernel family from the instrumented passes: the mean
-    algorithmic work per launch over the mean launch time."""
+    algorithmic work per launch over the mean launch time (each call's time
+    being its median over the passes)."""
     idx = [i for i, op in enumerate(hp.ops) if op.kind in kind]
     if not idx:
         return None
@@ -468,15 +470,27 @@ def main():
         f"{statistics.median(step_ms):.3f} ms, {value:.1f} TFLOP/s")
 
     # ---- phase 3: the same passes with every kernel call bracketed -----------
+    # (every event is created before the passes are enqueued; per call, the
+    # median over the K passes is the launch time used below -- a median, so
+    # that one stalled launch does not move the roofline)
+    pool = [(TimingEvent(), TimingEvent()) for _ in range(args.steps * len(hp.ops))]
     events = []
     torch.cuda.synchronize()
+    k = 0
     for _ in range(args.steps):
-        hp.run(events)
+        for i, op in enumerate(hp.ops):
+            s, e = pool[k]
+            k += 1
+            s.record()
+            op.fn()
+            e.record()
+            events.append((i, s, e))
     torch.cuda.synchronize()
     per_op = {}
     for i, s, e in events:
         per_op.setdefault(i, []).append(s.elapsed_time(e) * 1e3)
-    mean_us = {i: sum(v) / len(v) for i, v in per_op.items()}
+    mean_us = {i: statistics.median(v) for i, v in per_op.items()}
+    spread = {i: (min(v), max(v)) for i, v in per_op.items()}
     roofline = family_roofline(hp, mean_us, ("gemm",), "flops")
     roofline["kernel"] = ("gemm_kernel: the blockwise FP8 GEMM launches of the step (float32 "
                           "scales; each call's time includes its split-K reduction kernel "
@@ -555,8 +569,8 @@ def main():
 
     for i, op in enumerate(hp.ops):
         if op.kind == "gemm":
-            log(f"[bench] in-pass {op.label:15s} {mean_us[i]:8.1f} us  "
-                f"{op.flops / (mean_us[i] * 1e-6) / 1e12:7.1f} TFLOP/s")
+            log(f"[bench] in-pass {op.label:15s} {mean_us[i]:8.1f} us (min {spread[i][0]:.1f}, "
+                f"max {spread[i][1]:.1f})  {op.flops / (mean_us[i] * 1e-6) / 1e12:7.1f} TFLOP/s")
     gemm_ms = sum(mean_us[i] for i, op in enumerate(hp.ops) if op.kind == "gemm") / 1e3
     log(f"[bench] GEMM time {gemm_ms:.3f} ms of {statistics.median(step_ms):.3f} ms per step")
 

@@ -19,7 +19,11 @@ Power-of-two (E8M0) scales, group 32 or 128 (scales are uint8 tensors):
   quantize_mx_weight(w)                -> (q, s u8 [ceil(R/128)][ceil(C/128)])
   quantize_mx_weight_batch(ws)         -> [(q, s), ...]: several weights in one launch
   gemm_mx(layout, qa, sa, qb, sb, mode_a, mode_b) -> bf16 [M][N]
-    (modes 'act' = 1x128, 'block' = 128x128, 'mx32' = 1x32)
+    (modes 'act' = 1x128, 'block' = 128x128, 'mx32' = 1x32, 'act_km' = 1x128 with the
+    scale tensor stored K-block major, [K/128][rows])
+K-block-major scale variants (the layout of mode 'act_km'):
+  quantize_act_kmajor, quantize_act_transposed_kmajor, quantize_act_dual_kmajor,
+  quantize_mx_act_dual_kmajor
 """
 
 import ctypes
@@ -33,6 +37,10 @@ __all__ = [
     "quantize_act",
     "quantize_act_dual",
     "quantize_act_transposed",
+    "quantize_act_kmajor",
+    "quantize_act_transposed_kmajor",
+    "quantize_act_dual_kmajor",
+    "quantize_mx_act_dual_kmajor",
     "quantize_weight",
     "quantize_weight_batch",
     "gemm",
@@ -65,7 +73,7 @@ STATUS = {
     9: "BFP8_ERR_NONFINITE",
 }
 LAYOUTS = {"NN": 0, "NT": 1, "TN": 2}
-MODES = {"act": 0, "block": 1, "mx32": 2}
+MODES = {"act": 0, "block": 1, "mx32": 2, "act_km": 3}
 DTYPES = {torch.bfloat16: 0, torch.float32: 1}
 
 _i64 = ctypes.c_int64
@@ -78,6 +86,12 @@ _SIGNATURES = {
     "bfp8_quantize_weight": [_vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _vp],
     "bfp8_quantize_weight_batch": [_vp, _int, _int, _vp],
     "bfp8_quantize_act_dual": [_vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp],
+    "bfp8_quantize_act_kmajor": [_vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _vp],
+    "bfp8_quantize_act_transposed_kmajor": [_vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _vp],
+    "bfp8_quantize_act_dual_kmajor": [_vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64,
+                                      _vp, _vp],
+    "bfp8_quantize_mx_act_dual_kmajor": [_vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64,
+                                         _vp, _vp],
     "bfp8_gemm": [_int, _i64, _i64, _i64, _vp, _i64, _vp, _int, _vp, _i64, _vp, _int, _vp,
                   _i64, _vp, ctypes.c_size_t, _vp],
     "bfp8_gemm_workspace_bytes": [_int, _int, _int, _i64, _i64, _i64],
@@ -207,6 +221,54 @@ def quantize_act_dual(x: torch.Tensor, q=None, s=None, qt=None, st=None):
     if st is None:
         st = torch.empty((C, max(M // 128, 0)), dtype=torch.float32, device=x.device)
     _check("bfp8_quantize_act_dual", lib().bfp8_quantize_act_dual(
+        x.data_ptr(), DTYPES[x.dtype], M, C, x.stride(0), q.data_ptr(), q.stride(0),
+        s.data_ptr(), qt.data_ptr(), qt.stride(0), st.data_ptr(), _stream(x)))
+    return q, s, qt, st
+
+
+def quantize_act_kmajor(x: torch.Tensor, q=None, s=None):
+    """1x128 groups along rows, scales stored [C/128][R]; see bfp8_quantize_act_kmajor."""
+    _check_input(x, "x")
+    R, C = x.shape
+    if q is None:
+        q = _padded_empty(R, C, torch.uint8, x.device, 16)
+    if s is None:
+        s = torch.empty((max(C // 128, 0), R), dtype=torch.float32, device=x.device)
+    _check("bfp8_quantize_act_kmajor", lib().bfp8_quantize_act_kmajor(
+        x.data_ptr(), DTYPES[x.dtype], R, C, x.stride(0), q.data_ptr(), q.stride(0),
+        s.data_ptr(), _stream(x)))
+    return q, s
+
+
+def quantize_act_transposed_kmajor(x: torch.Tensor, qt=None, st=None):
+    """Token-axis groups written transposed, scales stored [M/128][C]; see
+    bfp8_quantize_act_transposed_kmajor."""
+    _check_input(x, "x")
+    M, C = x.shape
+    if qt is None:
+        qt = _padded_empty(C, M, torch.uint8, x.device, 16)
+    if st is None:
+        st = torch.empty((max(M // 128, 0), C), dtype=torch.float32, device=x.device)
+    _check("bfp8_quantize_act_transposed_kmajor", lib().bfp8_quantize_act_transposed_kmajor(
+        x.data_ptr(), DTYPES[x.dtype], M, C, x.stride(0), qt.data_ptr(), qt.stride(0),
+        st.data_ptr(), _stream(x)))
+    return qt, st
+
+
+def quantize_act_dual_kmajor(x: torch.Tensor, q=None, s=None, qt=None, st=None):
+    """Both layouts from one read, scales K-block major (s [C/128][M],
+    st [M/128][C]); see bfp8_quantize_act_dual_kmajor.  Returns (q, s, qt, st)."""
+    _check_input(x, "x")
+    M, C = x.shape
+    if q is None:
+        q = _padded_empty(M, C, torch.uint8, x.device, 16)
+    if s is None:
+        s = torch.empty((max(C // 128, 0), M), dtype=torch.float32, device=x.device)
+    if qt is None:
+        qt = _padded_empty(C, M, torch.uint8, x.device, 16)
+    if st is None:
+        st = torch.empty((max(M // 128, 0), C), dtype=torch.float32, device=x.device)
+    _check("bfp8_quantize_act_dual_kmajor", lib().bfp8_quantize_act_dual_kmajor(
         x.data_ptr(), DTYPES[x.dtype], M, C, x.stride(0), q.data_ptr(), q.stride(0),
         s.data_ptr(), qt.data_ptr(), qt.stride(0), st.data_ptr(), _stream(x)))
     return q, s, qt, st
@@ -379,6 +441,26 @@ def quantize_mx_act_dual(x: torch.Tensor, group: int = 128, q=None, s=None, qt=N
         st = _scale_bytes(C, max(M // group, 0), x.device)
     _check("bfp8_quantize_mx_act_dual", lib().bfp8_quantize_mx_act_dual(
         x.data_ptr(), DTYPES[x.dtype], M, C, x.stride(0), group, q.data_ptr(), q.stride(0),
+        s.data_ptr(), qt.data_ptr(), qt.stride(0), st.data_ptr(), _stream(x)))
+    return q, s, qt, st
+
+
+def quantize_mx_act_dual_kmajor(x: torch.Tensor, q=None, s=None, qt=None, st=None):
+    """Power-of-two scales, group 128, both layouts from one read with the
+    scale bytes K-block major (s [C/128][M], st [M/128][C]); see
+    bfp8_quantize_mx_act_dual_kmajor.  Returns (q, s, qt, st)."""
+    _check_input(x, "x")
+    M, C = x.shape
+    if q is None:
+        q = _padded_empty(M, C, torch.uint8, x.device, 16)
+    if s is None:
+        s = _scale_bytes(max(C // 128, 0), M, x.device)
+    if qt is None:
+        qt = _padded_empty(C, M, torch.uint8, x.device, 16)
+    if st is None:
+        st = _scale_bytes(max(M // 128, 0), C, x.device)
+    _check("bfp8_quantize_mx_act_dual_kmajor", lib().bfp8_quantize_mx_act_dual_kmajor(
+        x.data_ptr(), DTYPES[x.dtype], M, C, x.stride(0), q.data_ptr(), q.stride(0),
         s.data_ptr(), qt.data_ptr(), qt.stride(0), st.data_ptr(), _stream(x)))
     return q, s, qt, st
 

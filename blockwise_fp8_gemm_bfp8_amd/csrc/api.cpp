@@ -48,7 +48,17 @@ inline bfp8_status check_quant_common(const void* x, bfp8_in_dtype dt, int64_t r
 }
 
 inline int mode_index(bfp8_scale_mode m) {
-  return m == BFP8_SCALE_1x128 ? 0 : (m == BFP8_SCALE_128x128 ? 1 : 2);
+  switch (m) {
+    case BFP8_SCALE_1x128: return 0;
+    case BFP8_SCALE_128x128: return 1;
+    case BFP8_SCALE_1x32: return 2;
+    default: return 3;  // BFP8_SCALE_1x128_KMAJOR
+  }
+}
+
+// Scale modes of the float32-scale GEMM.
+inline bool fp32_mode(bfp8_scale_mode m) {
+  return m == BFP8_SCALE_1x128 || m == BFP8_SCALE_128x128 || m == BFP8_SCALE_1x128_KMAJOR;
 }
 
 // Shape, pointer and alignment checks shared by the two GEMM entry points
@@ -142,6 +152,58 @@ bfp8_status weight_batch(const JOB* jobs, int n, bfp8_in_dtype dt, int rule, hip
   }
   return launch_quantize_weight_batch(b, dt, rule, stream);
 }
+
+// Row-grouped quantiser (bfp8_quantize_act and its variants).
+bfp8_status quant_act(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
+                      int rule, int group, uint8_t* q, int64_t ldq, void* s, bool km,
+                      hipStream_t stream) {
+  if (group != 32 && group != 128) return BFP8_ERR_SCALE_MODE;
+  if (cols % 128 != 0 && cols > 0) return valid_dtype(dt) ? BFP8_ERR_SHAPE : BFP8_ERR_DTYPE;
+  bfp8_status st = check_quant_common(x, dt, rows, cols, ldx, q, ldq, s);
+  if (st != BFP8_OK || rows == 0 || cols == 0) return st;
+  if (ldq < cols) return BFP8_ERR_SHAPE;
+  if (rows * (cols / 128) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+  if (debug_checks_enabled() && (st = check_finite(x, dt, rows, cols, ldx, stream)) != BFP8_OK)
+    return st;
+  return launch_quantize_act(x, dt, rows, cols, ldx, rule, group, q, ldq, s, km, stream);
+}
+
+// Token-grouped quantiser written transposed (bfp8_quantize_act_transposed
+// and its variants).
+bfp8_status quant_act_t(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
+                        int rule, int group, uint8_t* qt, int64_t ldqt, void* st_, bool km,
+                        hipStream_t stream) {
+  if (group != 32 && group != 128) return BFP8_ERR_SCALE_MODE;
+  if (rows % 128 != 0 && rows > 0) return valid_dtype(dt) ? BFP8_ERR_SHAPE : BFP8_ERR_DTYPE;
+  bfp8_status st = check_quant_common(x, dt, rows, cols, ldx, qt, ldqt, st_);
+  if (st != BFP8_OK || rows == 0 || cols == 0) return st;
+  if (ldqt < rows) return BFP8_ERR_SHAPE;
+  if (rows / 128 > kMaxGridY || cdiv(cols, 64) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+  if (debug_checks_enabled() && (st = check_finite(x, dt, rows, cols, ldx, stream)) != BFP8_OK)
+    return st;
+  return launch_quantize_act_transposed(x, dt, rows, cols, ldx, rule, group, qt, ldqt, st_, km,
+                                        stream);
+}
+
+// Both layouts from one read (bfp8_quantize_act_dual and its variants).
+bfp8_status quant_dual(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
+                       int rule, int group, uint8_t* q, int64_t ldq, void* s, uint8_t* qt,
+                       int64_t ldqt, void* st_, bool km, hipStream_t stream) {
+  if (group != 32 && group != 128) return BFP8_ERR_SCALE_MODE;
+  if (((rows % 128 != 0 && rows > 0) || (cols % 128 != 0 && cols > 0)))
+    return valid_dtype(dt) ? BFP8_ERR_SHAPE : BFP8_ERR_DTYPE;
+  bfp8_status st = check_quant_common(x, dt, rows, cols, ldx, q, ldq, s);
+  if (st != BFP8_OK || rows == 0 || cols == 0) return st;
+  if (qt == nullptr || st_ == nullptr) return BFP8_ERR_NULL;
+  if (!aligned16(qt) || !aligned16(st_)) return BFP8_ERR_ALIGN;
+  if (ldq < cols || ldqt < rows) return BFP8_ERR_SHAPE;
+  if (ldqt % 16 != 0) return BFP8_ERR_ALIGN;
+  if (rows / 128 > kMaxGridY || cols / 128 >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
+  if (debug_checks_enabled() && (st = check_finite(x, dt, rows, cols, ldx, stream)) != BFP8_OK)
+    return st;
+  return launch_quantize_act_dual(x, dt, rows, cols, ldx, rule, group, q, ldq, s, qt, ldqt, st_,
+                                  km, stream);
+}
 }  // namespace
 
 extern "C" {
@@ -169,45 +231,38 @@ const char* bfp8_status_str(bfp8_status status) {
 bfp8_status bfp8_quantize_act(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
                               int64_t ldx, uint8_t* q, int64_t ldq, float* s,
                               hipStream_t stream) {
-  if (cols % 128 != 0 && cols > 0) return valid_dtype(dt) ? BFP8_ERR_SHAPE : BFP8_ERR_DTYPE;
-  bfp8_status st = check_quant_common(x, dt, rows, cols, ldx, q, ldq, s);
-  if (st != BFP8_OK || rows == 0 || cols == 0) return st;
-  if (ldq < cols) return BFP8_ERR_SHAPE;
-  if (rows * (cols / 128) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
-  if (debug_checks_enabled() && (st = check_finite(x, dt, rows, cols, ldx, stream)) != BFP8_OK)
-    return st;
-  return launch_quantize_act(x, dt, rows, cols, ldx, 0, 128, q, ldq, s, stream);
+  return quant_act(x, dt, rows, cols, ldx, 0, 128, q, ldq, s, false, stream);
+}
+
+bfp8_status bfp8_quantize_act_kmajor(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
+                                     int64_t ldx, uint8_t* q, int64_t ldq, float* s,
+                                     hipStream_t stream) {
+  return quant_act(x, dt, rows, cols, ldx, 0, 128, q, ldq, s, true, stream);
 }
 
 bfp8_status bfp8_quantize_act_transposed(const void* x, bfp8_in_dtype dt, int64_t rows,
                                          int64_t cols, int64_t ldx, uint8_t* qt,
                                          int64_t ldqt, float* st_, hipStream_t stream) {
-  if (rows % 128 != 0 && rows > 0) return valid_dtype(dt) ? BFP8_ERR_SHAPE : BFP8_ERR_DTYPE;
-  bfp8_status st = check_quant_common(x, dt, rows, cols, ldx, qt, ldqt, st_);
-  if (st != BFP8_OK || rows == 0 || cols == 0) return st;
-  if (ldqt < rows) return BFP8_ERR_SHAPE;
-  if (rows / 128 > kMaxGridY || cdiv(cols, 64) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
-  if (debug_checks_enabled() && (st = check_finite(x, dt, rows, cols, ldx, stream)) != BFP8_OK)
-    return st;
-  return launch_quantize_act_transposed(x, dt, rows, cols, ldx, 0, 128, qt, ldqt, st_, stream);
+  return quant_act_t(x, dt, rows, cols, ldx, 0, 128, qt, ldqt, st_, false, stream);
+}
+
+bfp8_status bfp8_quantize_act_transposed_kmajor(const void* x, bfp8_in_dtype dt, int64_t rows,
+                                                int64_t cols, int64_t ldx, uint8_t* qt,
+                                                int64_t ldqt, float* st_, hipStream_t stream) {
+  return quant_act_t(x, dt, rows, cols, ldx, 0, 128, qt, ldqt, st_, true, stream);
 }
 
 bfp8_status bfp8_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
-                                  int64_t ldx, uint8_t* q, int64_t ldq, float* s, uint8_t* qt,
-                                  int64_t ldqt, float* st_, hipStream_t stream) {
-  if (((rows % 128 != 0 && rows > 0) || (cols % 128 != 0 && cols > 0)))
-    return valid_dtype(dt) ? BFP8_ERR_SHAPE : BFP8_ERR_DTYPE;
-  bfp8_status st = check_quant_common(x, dt, rows, cols, ldx, q, ldq, s);
-  if (st != BFP8_OK || rows == 0 || cols == 0) return st;
-  if (qt == nullptr || st_ == nullptr) return BFP8_ERR_NULL;
-  if (!aligned16(qt) || !aligned16(st_)) return BFP8_ERR_ALIGN;
-  if (ldq < cols || ldqt < rows) return BFP8_ERR_SHAPE;
-  if (ldqt % 16 != 0) return BFP8_ERR_ALIGN;
-  if (rows / 128 > kMaxGridY || cols / 128 >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
-  if (debug_checks_enabled() && (st = check_finite(x, dt, rows, cols, ldx, stream)) != BFP8_OK)
-    return st;
-  return launch_quantize_act_dual(x, dt, rows, cols, ldx, 0, 128, q, ldq, s, qt, ldqt, st_,
-                                  stream);
+                                   int64_t ldx, uint8_t* q, int64_t ldq, float* s, uint8_t* qt,
+                                   int64_t ldqt, float* st_, hipStream_t stream) {
+  return quant_dual(x, dt, rows, cols, ldx, 0, 128, q, ldq, s, qt, ldqt, st_, false, stream);
+}
+
+bfp8_status bfp8_quantize_act_dual_kmajor(const void* x, bfp8_in_dtype dt, int64_t rows,
+                                          int64_t cols, int64_t ldx, uint8_t* q, int64_t ldq,
+                                          float* s, uint8_t* qt, int64_t ldqt, float* st_,
+                                          hipStream_t stream) {
+  return quant_dual(x, dt, rows, cols, ldx, 0, 128, q, ldq, s, qt, ldqt, st_, true, stream);
 }
 
 bfp8_status bfp8_quantize_weight(const void* w, bfp8_in_dtype dt, int64_t rows, int64_t cols,
@@ -232,49 +287,27 @@ bfp8_status bfp8_quantize_weight_batch(const bfp8_weight_job* jobs, int n, bfp8_
 bfp8_status bfp8_quantize_mx_act(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
                                  int64_t ldx, int group, uint8_t* q, int64_t ldq, uint8_t* s,
                                  hipStream_t stream) {
-  if (group != 32 && group != 128) return BFP8_ERR_SCALE_MODE;
-  if (cols % 128 != 0 && cols > 0) return valid_dtype(dt) ? BFP8_ERR_SHAPE : BFP8_ERR_DTYPE;
-  bfp8_status st = check_quant_common(x, dt, rows, cols, ldx, q, ldq, s);
-  if (st != BFP8_OK || rows == 0 || cols == 0) return st;
-  if (ldq < cols) return BFP8_ERR_SHAPE;
-  if (rows * (cols / 128) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
-  if (debug_checks_enabled() && (st = check_finite(x, dt, rows, cols, ldx, stream)) != BFP8_OK)
-    return st;
-  return launch_quantize_act(x, dt, rows, cols, ldx, 1, group, q, ldq, s, stream);
+  return quant_act(x, dt, rows, cols, ldx, 1, group, q, ldq, s, false, stream);
 }
 
 bfp8_status bfp8_quantize_mx_act_transposed(const void* x, bfp8_in_dtype dt, int64_t rows,
                                             int64_t cols, int64_t ldx, int group, uint8_t* qt,
                                             int64_t ldqt, uint8_t* st_, hipStream_t stream) {
-  if (group != 32 && group != 128) return BFP8_ERR_SCALE_MODE;
-  if (rows % 128 != 0 && rows > 0) return valid_dtype(dt) ? BFP8_ERR_SHAPE : BFP8_ERR_DTYPE;
-  bfp8_status st = check_quant_common(x, dt, rows, cols, ldx, qt, ldqt, st_);
-  if (st != BFP8_OK || rows == 0 || cols == 0) return st;
-  if (ldqt < rows) return BFP8_ERR_SHAPE;
-  if (rows / 128 > kMaxGridY || cdiv(cols, 64) >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
-  if (debug_checks_enabled() && (st = check_finite(x, dt, rows, cols, ldx, stream)) != BFP8_OK)
-    return st;
-  return launch_quantize_act_transposed(x, dt, rows, cols, ldx, 1, group, qt, ldqt, st_, stream);
+  return quant_act_t(x, dt, rows, cols, ldx, 1, group, qt, ldqt, st_, false, stream);
 }
 
 bfp8_status bfp8_quantize_mx_act_dual(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
                                       int64_t ldx, int group, uint8_t* q, int64_t ldq, uint8_t* s,
                                       uint8_t* qt, int64_t ldqt, uint8_t* st_,
                                       hipStream_t stream) {
-  if (group != 32 && group != 128) return BFP8_ERR_SCALE_MODE;
-  if (((rows % 128 != 0 && rows > 0) || (cols % 128 != 0 && cols > 0)))
-    return valid_dtype(dt) ? BFP8_ERR_SHAPE : BFP8_ERR_DTYPE;
-  bfp8_status st = check_quant_common(x, dt, rows, cols, ldx, q, ldq, s);
-  if (st != BFP8_OK || rows == 0 || cols == 0) return st;
-  if (qt == nullptr || st_ == nullptr) return BFP8_ERR_NULL;
-  if (!aligned16(qt) || !aligned16(st_)) return BFP8_ERR_ALIGN;
-  if (ldq < cols || ldqt < rows) return BFP8_ERR_SHAPE;
-  if (ldqt % 16 != 0) return BFP8_ERR_ALIGN;
-  if (rows / 128 > kMaxGridY || cols / 128 >= (int64_t(1) << 31)) return BFP8_ERR_SHAPE;
-  if (debug_checks_enabled() && (st = check_finite(x, dt, rows, cols, ldx, stream)) != BFP8_OK)
-    return st;
-  return launch_quantize_act_dual(x, dt, rows, cols, ldx, 1, group, q, ldq, s, qt, ldqt, st_,
-                                  stream);
+  return quant_dual(x, dt, rows, cols, ldx, 1, group, q, ldq, s, qt, ldqt, st_, false, stream);
+}
+
+bfp8_status bfp8_quantize_mx_act_dual_kmajor(const void* x, bfp8_in_dtype dt, int64_t rows,
+                                             int64_t cols, int64_t ldx, uint8_t* q, int64_t ldq,
+                                             uint8_t* s, uint8_t* qt, int64_t ldqt, uint8_t* st_,
+                                             hipStream_t stream) {
+  return quant_dual(x, dt, rows, cols, ldx, 1, 128, q, ldq, s, qt, ldqt, st_, true, stream);
 }
 
 bfp8_status bfp8_quantize_mx_weight(const void* w, bfp8_in_dtype dt, int64_t rows, int64_t cols,
@@ -297,8 +330,8 @@ bfp8_status bfp8_quantize_mx_weight_batch(const bfp8_mx_weight_job* jobs, int n,
 size_t bfp8_gemm_workspace_bytes(bfp8_layout layout, bfp8_scale_mode modeA,
                                  bfp8_scale_mode modeB, int64_t M, int64_t N, int64_t K) {
   if (layout != BFP8_NN && layout != BFP8_NT && layout != BFP8_TN) return static_cast<size_t>(-1);
-  if ((modeA != BFP8_SCALE_1x128 && modeA != BFP8_SCALE_128x128 && modeA != BFP8_SCALE_1x32) ||
-      (modeB != BFP8_SCALE_1x128 && modeB != BFP8_SCALE_128x128 && modeB != BFP8_SCALE_1x32))
+  if ((!fp32_mode(modeA) && modeA != BFP8_SCALE_1x32) ||
+      (!fp32_mode(modeB) && modeB != BFP8_SCALE_1x32))
     return static_cast<size_t>(-1);
   if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return static_cast<size_t>(-1);
   return gemm_workspace(layout, modeA, modeB, M, N, K);
@@ -310,9 +343,7 @@ bfp8_status bfp8_gemm(bfp8_layout layout, int64_t M, int64_t N, int64_t K, const
                       int64_t ldc, void* workspace, size_t workspace_bytes,
                       hipStream_t stream) {
   if (layout != BFP8_NN && layout != BFP8_NT && layout != BFP8_TN) return BFP8_ERR_LAYOUT;
-  if ((modeA != BFP8_SCALE_1x128 && modeA != BFP8_SCALE_128x128) ||
-      (modeB != BFP8_SCALE_1x128 && modeB != BFP8_SCALE_128x128))
-    return BFP8_ERR_SCALE_MODE;
+  if (!fp32_mode(modeA) || !fp32_mode(modeB)) return BFP8_ERR_SCALE_MODE;
   return gemm_common(layout, M, N, K, A, lda, sA, modeA, B, ldb, sB, modeB, C, ldc, workspace,
                      workspace_bytes, false, stream);
 }
@@ -323,9 +354,7 @@ bfp8_status bfp8_gemm_static_scratch(bfp8_layout layout, int64_t M, int64_t N, i
                                      const float* sB, bfp8_scale_mode modeB, void* C, int64_t ldc,
                                      hipStream_t stream) {
   if (layout != BFP8_NN && layout != BFP8_NT && layout != BFP8_TN) return BFP8_ERR_LAYOUT;
-  if ((modeA != BFP8_SCALE_1x128 && modeA != BFP8_SCALE_128x128) ||
-      (modeB != BFP8_SCALE_1x128 && modeB != BFP8_SCALE_128x128))
-    return BFP8_ERR_SCALE_MODE;
+  if (!fp32_mode(modeA) || !fp32_mode(modeB)) return BFP8_ERR_SCALE_MODE;
   return gemm_common(layout, M, N, K, A, lda, sA, modeA, B, ldb, sB, modeB, C, ldc, nullptr, 0,
                      false, stream, true);
 }
@@ -336,9 +365,7 @@ bfp8_status bfp8_gemm_mx(bfp8_layout layout, int64_t M, int64_t N, int64_t K, co
                          int64_t ldc, void* workspace, size_t workspace_bytes,
                          hipStream_t stream) {
   if (layout != BFP8_NN && layout != BFP8_NT && layout != BFP8_TN) return BFP8_ERR_LAYOUT;
-  auto valid = [](bfp8_scale_mode m) {
-    return m == BFP8_SCALE_1x128 || m == BFP8_SCALE_128x128 || m == BFP8_SCALE_1x32;
-  };
+  auto valid = [](bfp8_scale_mode m) { return fp32_mode(m) || m == BFP8_SCALE_1x32; };
   if (!valid(modeA) || !valid(modeB)) return BFP8_ERR_SCALE_MODE;
   // 1x32 scales only for K-contiguous operands (A of NN/NT, B of NT)
   if ((modeA == BFP8_SCALE_1x32 && layout == BFP8_TN) ||

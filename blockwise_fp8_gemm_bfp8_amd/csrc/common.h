@@ -161,17 +161,19 @@ bfp8_status check_finite(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t 
 // Host-side launch helpers (defined in the .hip files).  `rule` selects the
 // scale rule (0: float32 amax/448, 1: power-of-two E8M0 byte) and `s` points
 // to float or uint8_t scales accordingly; `group` is the group length along
-// the grouped axis (128, or 32 for the power-of-two rule).
+// the grouped axis (128, or 32 for the power-of-two rule).  `km` (group 128
+// only) stores the scale tensors K-block major: [groups][rows] instead of
+// [rows][groups].
 bfp8_status launch_quantize_act(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
                                 int64_t ldx, int rule, int group, uint8_t* q, int64_t ldq,
-                                void* s, hipStream_t stream);
+                                void* s, bool km, hipStream_t stream);
 bfp8_status launch_quantize_act_transposed(const void* x, bfp8_in_dtype dt, int64_t rows,
                                            int64_t cols, int64_t ldx, int rule, int group,
-                                           uint8_t* qt, int64_t ldqt, void* st,
+                                           uint8_t* qt, int64_t ldqt, void* st, bool km,
                                            hipStream_t stream);
 bfp8_status launch_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
                                      int64_t ldx, int rule, int group, uint8_t* q, int64_t ldq,
-                                     void* s, uint8_t* qt, int64_t ldqt, void* st,
+                                     void* s, uint8_t* qt, int64_t ldqt, void* st, bool km,
                                      hipStream_t stream);
 bfp8_status launch_quantize_weight(const void* w, bfp8_in_dtype dt, int64_t rows, int64_t cols,
                                    int64_t ldw, int rule, uint8_t* q, int64_t ldq, void* s,

@@ -302,6 +302,10 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
             int tiles_n, float* __restrict__ part, int64_t ldp) {
   const float* __restrict__ sA = static_cast<const float*>(sA_);
   const float* __restrict__ sB = static_cast<const float*>(sB_);
+  // MODE 3: 1x128 groups like MODE 0, with the scale tensor stored K-block
+  // major ([K/128][rows]) whatever the code orientation
+  constexpr int MA = MODE_A == 3 ? 0 : MODE_A, MB = MODE_B == 3 ? 0 : MODE_B;
+  constexpr bool SKA = A_KM || MODE_A == 3, SKB = B_KM || MODE_B == 3;
   // Two pipeline stages; block kb lives in stage kb % 2.
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
@@ -350,8 +354,8 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
   {
     const bool b_side = wave >= 4;
     const int sub = wave & 3;
-    const int mode = b_side ? MODE_B : MODE_A;
-    const bool km = b_side ? B_KM : A_KM;
+    const int mode = b_side ? MB : MA;
+    const bool km = b_side ? SKB : SKA;
     const float* sp = b_side ? sB : sA;
     const int64_t r0 = b_side ? n0 : m0, rows = b_side ? N : M, nblk = b_side ? NBk : MBk;
     sc_lds = (b_side ? 1024u : 0u) + (mode == 0 ? static_cast<uint32_t>(sub) * 256u : 0u);
@@ -413,8 +417,8 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
   // comes from the K block's LDS stage, copied with its codes
   auto row_mults = [&](const uint8_t* st, float (&ra)[TM]) {
     const float* s_lds = reinterpret_cast<const float*>(st + kTileABytes + kTileBBytes);
-    const float sb = MODE_B == 1 ? s_lds[BM + wn] : 1.0f;
-    if (MODE_A == 0) {
+    const float sb = MB == 1 ? s_lds[BM + wn] : 1.0f;
+    if (MA == 0) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) ra[i] = s_lds[wm * WM + 16 * i + r16] * sb;
     } else {
@@ -424,7 +428,7 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
     }
   };
   auto col_mults = [&](const uint8_t* st, int j, float (&cb)[4]) {
-    if (MODE_B == 0) {
+    if (MB == 0) {
       const float* s_lds = reinterpret_cast<const float*>(st + kTileABytes + kTileBBytes);
       const float4 v = *reinterpret_cast<const float4*>(s_lds + BM + wn * WN + 16 * j + 4 * g);
       cb[0] = v.x; cb[1] = v.y; cb[2] = v.z; cb[3] = v.w;
@@ -448,7 +452,7 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float x = a[r];
-      x = fmaf(p[r], MODE_B == 0 ? rmul * cm[r] : rmul, x);
+      x = fmaf(p[r], MB == 0 ? rmul * cm[r] : rmul, x);
       asm volatile("" : "+v"(x));
       a[r] = x;
     }
@@ -656,6 +660,9 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
                 int tiles_n, float* __restrict__ part, int64_t ldp) {
   const uint8_t* __restrict__ eA = static_cast<const uint8_t*>(sA_);
   const uint8_t* __restrict__ eB = static_cast<const uint8_t*>(sB_);
+  // MODE 3: 1x128 groups, scale bytes stored K-block major ([K/128][rows])
+  constexpr int MA = MODE_A == 3 ? 0 : MODE_A, MB = MODE_B == 3 ? 0 : MODE_B;
+  constexpr bool SKA = A_KM || MODE_A == 3, SKB = B_KM || MODE_B == 3;
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
 
@@ -694,17 +701,17 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
       // every wave copies (for 128x128 blocks the copies of waves 1-3 land
       // beside wave 0's and are never read): no wave-dependent branch
       if (piece == 16)
-        load_mx_scales<A_KM, MODE_A>(eA, m0, M, MBk, KB, kb, sdst, wave, lane);
+        load_mx_scales<SKA, MA>(eA, m0, M, MBk, KB, kb, sdst, wave, lane);
       else
-        load_mx_scales<B_KM, MODE_B>(eB, n0, N, NBk, KB, kb, sdst + 1024, wave, lane);
+        load_mx_scales<SKB, MB>(eB, n0, N, NBk, KB, kb, sdst + 1024, wave, lane);
     }
   };
 
   // E8M0 bytes, as in gemm_kernel: per-lane byte offsets packed 2 bits per
   // subtile, plus a K-block term
   auto byte_base = [&](bool b_side, int rt) -> uint32_t {
-    const int mode = b_side ? MODE_B : MODE_A;
-    const bool km = b_side ? B_KM : A_KM;
+    const int mode = b_side ? MB : MA;
+    const bool km = b_side ? SKB : SKA;
     const int64_t r0 = b_side ? n0 : m0, rows = b_side ? N : M, nblk = b_side ? NBk : MBk;
     if (mode == 2) return 0;
     if (mode == 1) {
@@ -729,20 +736,20 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
   // before the bytes are extracted, so the LDS latency hides under MFMAs
   auto word_a = [&](const uint8_t* st, int i) -> uint32_t {
     const uint32_t* w = reinterpret_cast<const uint32_t*>(st + kTileABytes + kTileBBytes);
-    return MODE_A == 1 ? w[(wm * W4M) / 128] : w[wm * W4M + 16 * i + r16];
+    return MA == 1 ? w[(wm * W4M) / 128] : w[wm * W4M + 16 * i + r16];
   };
   auto byte_a = [&](uint32_t word, int64_t kb, int i) -> int {
-    const uint32_t ka = kterm(MODE_A, A_KM, M, MBk, kb);
-    const uint32_t sh = MODE_A == 2 ? 8u * g : 8u * (((pack_a >> (2 * i)) + ka) & 3u);
+    const uint32_t ka = kterm(MA, SKA, M, MBk, kb);
+    const uint32_t sh = MA == 2 ? 8u * g : 8u * (((pack_a >> (2 * i)) + ka) & 3u);
     return static_cast<int>((word >> sh) & 0xFFu);
   };
   auto word_b = [&](const uint8_t* st, int j) -> uint32_t {
     const uint32_t* w = reinterpret_cast<const uint32_t*>(st + kTileABytes + kTileBBytes) + BM;
-    return MODE_B == 1 ? w[(wn * W4N) / 128] : w[wn * W4N + 16 * j + r16];
+    return MB == 1 ? w[(wn * W4N) / 128] : w[wn * W4N + 16 * j + r16];
   };
   auto byte_b = [&](uint32_t word, int64_t kb, int j) -> int {
-    const uint32_t kbb = kterm(MODE_B, B_KM, N, NBk, kb);
-    const uint32_t sh = MODE_B == 2 ? 8u * g : 8u * (((pack_b >> (2 * j)) + kbb) & 3u);
+    const uint32_t kbb = kterm(MB, SKB, N, NBk, kb);
+    const uint32_t sh = MB == 2 ? 8u * g : 8u * (((pack_b >> (2 * j)) + kbb) & 3u);
     return static_cast<int>((word >> sh) & 0xFFu);
   };
 
@@ -956,21 +963,33 @@ static bfp8_status launch_layout(const GemmArgs& a, dim3 grid, int tm, int tn, f
                     a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K, tm, tn, part,   \
                     ldp);                                                                     \
   } while (0)
-  if (a.modeA == 0 && a.modeB == 1) BFP8_LAUNCH(0, 1);
-  else if (a.modeA == 0 && a.modeB == 0) BFP8_LAUNCH(0, 0);
-  else if (a.modeA == 1 && a.modeB == 0) BFP8_LAUNCH(1, 0);
-  else if (a.modeA == 1 && a.modeB == 1) BFP8_LAUNCH(1, 1);
-  else if constexpr (MX) {
+  // mode 3 (K-block-major act scales) is mode 0 for a K-major operand
+  const int ma = (A_KM && a.modeA == 3) ? 0 : a.modeA;
+  const int mb = (B_KM && a.modeB == 3) ? 0 : a.modeB;
+  if (ma == 0 && mb == 1) BFP8_LAUNCH(0, 1);
+  else if (ma == 0 && mb == 0) BFP8_LAUNCH(0, 0);
+  else if (ma == 1 && mb == 0) BFP8_LAUNCH(1, 0);
+  else if (ma == 1 && mb == 1) BFP8_LAUNCH(1, 1);
+  if constexpr (!A_KM) {
+    if (ma == 3 && mb == 1) BFP8_LAUNCH(3, 1);
+    else if (ma == 3 && mb == 0) BFP8_LAUNCH(3, 0);
+    if constexpr (!B_KM) {
+      if (ma == 3 && mb == 3) BFP8_LAUNCH(3, 3);
+      else if (ma == 0 && mb == 3) BFP8_LAUNCH(0, 3);
+      else if (ma == 1 && mb == 3) BFP8_LAUNCH(1, 3);
+    }
+  }
+  if constexpr (MX) {
     // 1x32 groups (mode 2) exist only with E8M0 scales and K-contiguous storage
     if constexpr (!A_KM && !B_KM) {
-      if (a.modeA == 2 && a.modeB == 2) BFP8_LAUNCH(2, 2);
-      else if (a.modeA == 2 && a.modeB == 0) BFP8_LAUNCH(2, 0);
-      else if (a.modeA == 2 && a.modeB == 1) BFP8_LAUNCH(2, 1);
-      else if (a.modeA == 0 && a.modeB == 2) BFP8_LAUNCH(0, 2);
-      else if (a.modeA == 1 && a.modeB == 2) BFP8_LAUNCH(1, 2);
+      if (ma == 2 && mb == 2) BFP8_LAUNCH(2, 2);
+      else if (ma == 2 && mb == 0) BFP8_LAUNCH(2, 0);
+      else if (ma == 2 && mb == 1) BFP8_LAUNCH(2, 1);
+      else if (ma == 0 && mb == 2) BFP8_LAUNCH(0, 2);
+      else if (ma == 1 && mb == 2) BFP8_LAUNCH(1, 2);
     } else if constexpr (!A_KM) {
-      if (a.modeA == 2 && a.modeB == 0) BFP8_LAUNCH(2, 0);
-      else if (a.modeA == 2 && a.modeB == 1) BFP8_LAUNCH(2, 1);
+      if (ma == 2 && mb == 0) BFP8_LAUNCH(2, 0);
+      else if (ma == 2 && mb == 1) BFP8_LAUNCH(2, 1);
     }
   }
 #undef BFP8_LAUNCH

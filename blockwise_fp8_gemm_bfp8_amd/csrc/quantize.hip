@@ -88,12 +88,15 @@ __device__ __forceinline__ float group_lanes_max(float v) {
 // ---------------------------------------------------------------------------
 constexpr int kActUnroll = 4;
 
-template <typename T, int RULE, int GROUP>
+template <typename T, int RULE, int GROUP, bool KM>
 __global__ __launch_bounds__(256) void quantize_act_kernel(
     const T* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
-    typename ScaleRule<RULE>::type* __restrict__ s, uint32_t gpr, uint32_t n_groups) {
+    typename ScaleRule<RULE>::type* __restrict__ s, uint32_t gpr, uint32_t n_groups,
+    uint32_t rows) {
   // gpr / n_groups count 128-element chunks; s holds gpr * (128 / GROUP)
-  // scales per row.
+  // scales per row ([rows][gpr]), or, with KM (GROUP 128), one row of
+  // `rows` scales per chunk ([gpr][rows]): then consecutive slots take
+  // consecutive rows of one chunk, so a step's scales land side by side.
   const uint32_t lane16 = threadIdx.x & 15u;
   const uint32_t slot = threadIdx.x >> 4;  // 0..15: group within a step
   const uint32_t per_block = 16u * kActUnroll;
@@ -104,8 +107,13 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(
     for (int u = 0; u < kActUnroll; ++u) {
       const uint32_t g = base + u * 16u + slot;
       const bool ok = g < n_groups;
-      row[u] = ok ? g / gpr : 0u;
-      gc[u] = ok ? g - row[u] * gpr : 0u;
+      if (KM) {
+        gc[u] = ok ? g / rows : 0u;
+        row[u] = ok ? g - gc[u] * rows : 0u;
+      } else {
+        row[u] = ok ? g / gpr : 0u;
+        gc[u] = ok ? g - row[u] * gpr : 0u;
+      }
       const T* p = x + static_cast<int64_t>(row[u]) * ldx + gc[u] * kGroup + lane16 * 8u;
       Load8<T>::run(p, v[u], ok ? 8 : 0);
     }
@@ -121,8 +129,11 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(
                                   lane16 * 8u) = codes;
         constexpr uint32_t kLanes = GROUP / 8;  // lanes per group
         constexpr uint32_t kSub = kGroup / GROUP;
-        if (lane16 % kLanes == 0)
+        if (KM) {
+          if (lane16 == 0) s[static_cast<int64_t>(gc[u]) * rows + row[u]] = sc;
+        } else if (lane16 % kLanes == 0) {
           s[static_cast<int64_t>(row[u]) * gpr * kSub + gc[u] * kSub + lane16 / kLanes] = sc;
+        }
       }
     }
   }
@@ -140,12 +151,13 @@ constexpr int kTrTok = 128;
 constexpr int kTrCh = 64;
 constexpr int kTrLd = kTrCh + 4;  // padded fp32 row stride (16-byte aligned)
 
-template <typename T, int RULE, int GROUP>
+template <typename T, int RULE, int GROUP, bool KM>
 __global__ __launch_bounds__(256) void quantize_act_t_kernel(
     const T* __restrict__ x, int64_t ldx, int64_t cols, uint8_t* __restrict__ qt, int64_t ldqt,
     typename ScaleRule<RULE>::type* __restrict__ st, int64_t n_tok_blocks) {
   // n_tok_blocks counts 128-token blocks; st rows hold n_tok_blocks *
-  // (128 / GROUP) scales.
+  // (128 / GROUP) scales ([cols][n_tok_blocks]), or, with KM (GROUP 128),
+  // one row of `cols` scales per token block ([n_tok_blocks][cols]).
   __shared__ __attribute__((aligned(16))) float tile[kTrTok * kTrLd];
   __shared__ float part[4][kTrCh];
   const int tid = threadIdx.x;
@@ -196,7 +208,10 @@ __global__ __launch_bounds__(256) void quantize_act_t_kernel(
     dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
     dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
     if (GROUP == 128) {
-      if (p == 0) st[(c0 + c) * n_tok_blocks + tb] = sc;
+      if (p == 0) {
+        if (KM) st[tb * cols + c0 + c] = sc;
+        else st[(c0 + c) * n_tok_blocks + tb] = sc;
+      }
     } else {
       st[(c0 + c) * n_tok_blocks * 4 + tb * 4 + p] = sc;
     }
@@ -306,16 +321,30 @@ struct DualTile<float> {
   static constexpr int kLd = 128 + 4;
 };
 
-template <typename T, int RULE, int GROUP, int CB>
+// Two adjacent scales in one store (the index of the first is even).
+__device__ __forceinline__ void store_scale_pair(float* p, float a, float b) {
+  *reinterpret_cast<float2*>(p) = make_float2(a, b);
+}
+__device__ __forceinline__ void store_scale_pair(uint8_t* p, uint8_t a, uint8_t b) {
+  *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(a | (b << 8));
+}
+
+template <typename T, int RULE, int GROUP, int CB, bool KM>
 __global__ __launch_bounds__(256 * CB) void quantize_dual_kernel(
     const T* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
     typename ScaleRule<RULE>::type* __restrict__ s, uint8_t* __restrict__ qt, int64_t ldqt,
     typename ScaleRule<RULE>::type* __restrict__ st, int64_t n_ch_blocks, int64_t n_tok_blocks) {
+  // KM (GROUP 128): both scale tensors K-block major -- row scales
+  // [n_ch_blocks][rows], token scales [n_tok_blocks][cols] -- so a tile's
+  // 128 row scales per channel block and its 128 * CB token scales each
+  // leave as one contiguous run.
+  typedef typename ScaleRule<RULE>::type S;
   constexpr int kSub = kGroup / GROUP;  // groups per 128 along either axis
   constexpr int kLd = DualTile<T>::kLd + 128 * (CB - 1);
   constexpr int kCh = 128 * CB;         // channels per tile
   __shared__ __attribute__((aligned(16))) T tile[128 * kLd];
   __shared__ float part[4][kCh];
+  __shared__ __attribute__((aligned(16))) S rsc[KM ? CB : 1][128];  // KM: row scales of the tile
   const int tid = threadIdx.x;
   const int64_t cb = static_cast<int64_t>(blockIdx.x) * CB, tb = blockIdx.y;
   const int64_t m0 = tb * 128, c0 = cb * 128;
@@ -337,7 +366,9 @@ __global__ __launch_bounds__(256 * CB) void quantize_dual_kernel(
     float inv;
     const auto sc = ScaleRule<RULE>::make(amax, inv);
     *reinterpret_cast<uint2*>(q + (m0 + r) * ldq + c0 + cofs) = encode8(v[u], inv);
-    if (CB == 2 && GROUP == 128 && RULE == 0) {
+    if (KM) {
+      if (lane16 == 0) rsc[KM ? gsub : 0][r] = sc;
+    } else if (CB == 2 && GROUP == 128 && RULE == 0) {
       // the row's two scales are adjacent: one 8-byte store from group 0
       const float sc1 = __shfl_down(static_cast<float>(sc), 16, 32);
       if (tid % 32 == 0)
@@ -403,7 +434,15 @@ __global__ __launch_bounds__(256 * CB) void quantize_dual_kernel(
   da[1] = make_uint4(wa[4], wa[5], wa[6], wa[7]);
   db[0] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
   db[1] = make_uint4(wb[4], wb[5], wb[6], wb[7]);
-  if (GROUP == 128) {
+  if (KM) {
+    const int64_t cols = n_ch_blocks * 128;
+    if (p == 0) store_scale_pair(st + tb * cols + c0 + 2 * cp, sa, sb);
+    if (p == 1) {
+      // row scales of channel block cb + cp / 64, rows 2 (cp % 64) and one more
+      const int gs = cp / 64, rr = 2 * (cp % 64);
+      store_scale_pair(s + (cb + gs) * (n_tok_blocks * 128) + m0 + rr, rsc[gs][rr], rsc[gs][rr + 1]);
+    }
+  } else if (GROUP == 128) {
     if (p == 0) {
       st[(c0 + 2 * cp) * n_tok_blocks + tb] = sa;
       st[(c0 + 2 * cp + 1) * n_tok_blocks + tb] = sb;
@@ -464,9 +503,16 @@ __global__ __launch_bounds__(256) void find_nonfinite_kernel(const T* __restrict
     }                                                                        \
   } while (0)
 
+// As BFP8_DISPATCH, and the scale-layout flag: KMV = km (group 128 only).
+#define BFP8_DISPATCH_KM(KERNEL_CALL)                                      \
+  BFP8_DISPATCH(if constexpr (G == 128) {                                  \
+    if (km) { constexpr bool KMV = true; KERNEL_CALL; }                    \
+    else { constexpr bool KMV = false; KERNEL_CALL; }                      \
+  } else { constexpr bool KMV = false; KERNEL_CALL; })
+
 bfp8_status launch_quantize_act(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
                                 int64_t ldx, int rule, int group, uint8_t* q, int64_t ldq,
-                                void* s, hipStream_t stream) {
+                                void* s, bool km, hipStream_t stream) {
   const int64_t gpr = cols / kGroup;
   const int64_t n_groups = rows * gpr;
   if (n_groups == 0) return BFP8_OK;
@@ -474,30 +520,32 @@ bfp8_status launch_quantize_act(const void* x, bfp8_in_dtype dt, int64_t rows, i
   int64_t blocks = (n_groups + per_block - 1) / per_block;
   if (blocks > 16384) blocks = 16384;
   bfp8_status st = BFP8_OK;
-  BFP8_DISPATCH((st = launch(&quantize_act_kernel<T, R, G>, dim3(static_cast<unsigned>(blocks)),
-                             dim3(256), stream, static_cast<const T*>(x), ldx, q, ldq,
-                             static_cast<typename ScaleRule<R>::type*>(s),
-                             static_cast<uint32_t>(gpr), static_cast<uint32_t>(n_groups))));
+  BFP8_DISPATCH_KM((st = launch(&quantize_act_kernel<T, R, G, KMV>,
+                                dim3(static_cast<unsigned>(blocks)), dim3(256), stream,
+                                static_cast<const T*>(x), ldx, q, ldq,
+                                static_cast<typename ScaleRule<R>::type*>(s),
+                                static_cast<uint32_t>(gpr), static_cast<uint32_t>(n_groups),
+                                static_cast<uint32_t>(rows))));
   return st;
 }
 
 bfp8_status launch_quantize_act_transposed(const void* x, bfp8_in_dtype dt, int64_t rows,
                                            int64_t cols, int64_t ldx, int rule, int group,
-                                           uint8_t* qt, int64_t ldqt, void* st,
+                                           uint8_t* qt, int64_t ldqt, void* st, bool km,
                                            hipStream_t stream) {
   if (rows == 0 || cols == 0) return BFP8_OK;
   const int64_t tok_blocks = rows / kTrTok;
   dim3 grid(static_cast<unsigned>((cols + kTrCh - 1) / kTrCh), static_cast<unsigned>(tok_blocks));
   bfp8_status status = BFP8_OK;
-  BFP8_DISPATCH((status = launch(&quantize_act_t_kernel<T, R, G>, grid, dim3(256), stream,
-                                 static_cast<const T*>(x), ldx, cols, qt, ldqt,
-                                 static_cast<typename ScaleRule<R>::type*>(st), tok_blocks)));
+  BFP8_DISPATCH_KM((status = launch(&quantize_act_t_kernel<T, R, G, KMV>, grid, dim3(256),
+                                    stream, static_cast<const T*>(x), ldx, cols, qt, ldqt,
+                                    static_cast<typename ScaleRule<R>::type*>(st), tok_blocks)));
   return status;
 }
 
 bfp8_status launch_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
                                      int64_t ldx, int rule, int group, uint8_t* q, int64_t ldq,
-                                     void* s, uint8_t* qt, int64_t ldqt, void* st,
+                                     void* s, uint8_t* qt, int64_t ldqt, void* st, bool km,
                                      hipStream_t stream) {
   if (rows == 0 || cols == 0) return BFP8_OK;
   const int64_t ch_blocks = cols / kGroup, tok_blocks = rows / kGroup;
@@ -507,7 +555,7 @@ bfp8_status launch_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t ro
   if (dt == BFP8_IN_BF16 && ch_blocks % 2 == 0 && ch_blocks >= 48) {
     dim3 grid2(static_cast<unsigned>(ch_blocks / 2), static_cast<unsigned>(tok_blocks));
     bfp8_status status = BFP8_OK;
-    BFP8_DISPATCH((status = launch(&quantize_dual_kernel<uint16_t, R, G, 2>, grid2, dim3(512),
+    BFP8_DISPATCH_KM((status = launch(&quantize_dual_kernel<uint16_t, R, G, 2, KMV>, grid2, dim3(512),
                                    stream, static_cast<const uint16_t*>(x), ldx, q, ldq,
                                    static_cast<typename ScaleRule<R>::type*>(s), qt, ldqt,
                                    static_cast<typename ScaleRule<R>::type*>(st), ch_blocks,
@@ -516,7 +564,7 @@ bfp8_status launch_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t ro
   }
   dim3 grid(static_cast<unsigned>(ch_blocks), static_cast<unsigned>(tok_blocks));
   bfp8_status status = BFP8_OK;
-  BFP8_DISPATCH((status = launch(&quantize_dual_kernel<T, R, G, 1>, grid, dim3(256), stream,
+  BFP8_DISPATCH_KM((status = launch(&quantize_dual_kernel<T, R, G, 1, KMV>, grid, dim3(256), stream,
                                  static_cast<const T*>(x), ldx, q, ldq,
                                  static_cast<typename ScaleRule<R>::type*>(s), qt, ldqt,
                                  static_cast<typename ScaleRule<R>::type*>(st), ch_blocks,
@@ -553,6 +601,7 @@ bfp8_status launch_quantize_weight(const void* w, bfp8_in_dtype dt, int64_t rows
   return status;
 }
 
+#undef BFP8_DISPATCH_KM
 #undef BFP8_DISPATCH
 
 bool debug_checks_enabled() {

@@ -6,8 +6,10 @@ the Puro-2B paper translation (papers.lianghsun.dev), section 3.2:
   dgrad:  quantize_act(dy), gemm NN with W's codes as stored -> dx [M][in]
   wgrad:  quantize_act_transposed(dy), quantize_act_transposed(x),
           gemm NT on the two token-grouped operands          -> dW [out][in]
-where a tensor needed in both layouts is read once (quantize_act_dual), and
-all the weights are quantised in one launch (quantize_weight_batch).
+where a tensor needed in both layouts is read once (quantize_act_dual), all
+the weights are quantised in one launch (quantize_weight_batch), and the
+activation / gradient scales are kept K-block major (the _kmajor quantisers,
+GEMM scale mode 'act_km'; the 1x32 groups keep their one layout).
 All buffers (codes, scales, outputs, split-K workspaces) are allocated once, so a
 pass only enqueues kernels on the current stream.  The pass is kept as a list of
 kernel calls with the work each does (flops, algorithmic bytes), which is what
@@ -32,9 +34,10 @@ from typing import Callable, Dict, List, Optional, Tuple
 
 import torch
 
-from . import (MAX_WEIGHT_JOBS, _scale_bytes, gemm, gemm_mx, gemm_workspace_bytes, quantize_act,
-               quantize_act_dual, quantize_act_transposed, quantize_mx_act_dual,
-               quantize_mx_weight_batch, quantize_weight_batch)
+from . import (MAX_WEIGHT_JOBS, _scale_bytes, gemm, gemm_mx, gemm_workspace_bytes,
+               quantize_act_dual_kmajor, quantize_act_kmajor, quantize_act_transposed_kmajor,
+               quantize_mx_act_dual, quantize_mx_act_dual_kmajor, quantize_mx_weight_batch,
+               quantize_weight_batch)
 
 SCALE_FORMATS = ("fp32", "mx128", "mx32")
 
@@ -172,21 +175,24 @@ class HotPath:
         b = L.buf
         b["wq"] = torch.empty((dout, din), dtype=u8, device=dev)
         b["ws"] = torch.empty(((dout + 127) // 128, din // 128), dtype=f32, device=dev)
+        # activation / gradient scales K-block major ([K/128][rows]): each
+        # quantiser tile writes its scales as one run, each GEMM K block
+        # reads them as a few cache lines
         if "fprop" in self.roles:
             b["xq"] = torch.empty((M, din), dtype=u8, device=dev)
-            b["xs"] = torch.empty((M, din // 128), dtype=f32, device=dev)
+            b["xs"] = torch.empty((din // 128, M), dtype=f32, device=dev)
             b["y"] = torch.empty((M, dout), dtype=bf, device=dev)
         if "dgrad" in self.roles:
             b["dyq"] = torch.empty((M, dout), dtype=u8, device=dev)
-            b["dys"] = torch.empty((M, dout // 128), dtype=f32, device=dev)
+            b["dys"] = torch.empty((dout // 128, M), dtype=f32, device=dev)
             b["dx"] = torch.empty((M, din), dtype=bf, device=dev)
         if "wgrad" in self.roles:
             b["dyqt"] = torch.empty((dout, M), dtype=u8, device=dev)
-            b["dyst"] = torch.empty((dout, M // 128), dtype=f32, device=dev)
+            b["dyst"] = torch.empty((M // 128, dout), dtype=f32, device=dev)
             b["xqt"] = torch.empty((din, M), dtype=u8, device=dev)
-            b["xst"] = torch.empty((din, M // 128), dtype=f32, device=dev)
+            b["xst"] = torch.empty((M // 128, din), dtype=f32, device=dev)
             b["dw"] = torch.empty((dout, din), dtype=bf, device=dev)
-            nb = gemm_workspace_bytes("NT", "act", "act", dout, din, M)
+            nb = gemm_workspace_bytes("NT", "act_km", "act_km", dout, din, M)
             b["ws_wgrad"] = torch.empty((max(nb, 16),), dtype=u8, device=dev)
 
     def _alloc_mx(self, L: LinearState):
@@ -204,18 +210,21 @@ class HotPath:
             b["wst"] = _scale_bytes(din, dout // 32, dev)
         else:
             b["ws"] = _scale_bytes((dout + 127) // 128, (din + 127) // 128, dev)
+        # group 128: scale bytes K-block major ([K/128][rows]); group 32 keeps
+        # [rows][K/32] (the only layout of mode mx32)
+        km = grp == 128
         b["xq"] = torch.empty((M, din), dtype=u8, device=dev)
-        b["xs"] = _scale_bytes(M, din // grp, dev)
+        b["xs"] = _scale_bytes(din // grp, M, dev) if km else _scale_bytes(M, din // grp, dev)
         b["xqt"] = torch.empty((din, M), dtype=u8, device=dev)
-        b["xst"] = _scale_bytes(din, M // grp, dev)
+        b["xst"] = _scale_bytes(M // grp, din, dev) if km else _scale_bytes(din, M // grp, dev)
         b["y"] = torch.empty((M, dout), dtype=bf, device=dev)
         b["dyq"] = torch.empty((M, dout), dtype=u8, device=dev)
-        b["dys"] = _scale_bytes(M, dout // grp, dev)
+        b["dys"] = _scale_bytes(dout // grp, M, dev) if km else _scale_bytes(M, dout // grp, dev)
         b["dyqt"] = torch.empty((dout, M), dtype=u8, device=dev)
-        b["dyst"] = _scale_bytes(dout, M // grp, dev)
+        b["dyst"] = _scale_bytes(M // grp, dout, dev) if km else _scale_bytes(dout, M // grp, dev)
         b["dx"] = torch.empty((M, din), dtype=bf, device=dev)
         b["dw"] = torch.empty((dout, din), dtype=bf, device=dev)
-        mode = "mx32" if grp == 32 else "act"
+        mode = "mx32" if grp == 32 else "act_km"
         nb = gemm_workspace_bytes("NT", mode, mode, dout, din, M)
         b["ws_wgrad"] = torch.empty((max(nb, 16),), dtype=u8, device=dev)
 
@@ -255,16 +264,16 @@ class HotPath:
             if "fprop" in roles:
                 if both_x:
                     ops.append(Op(f"{L.name}.x dual", "quant",
-                                  lambda L=L, b=b: quantize_act_dual(L.x, b["xq"], b["xs"],
-                                                                     b["xqt"], b["xst"]),
+                                  lambda L=L, b=b: quantize_act_dual_kmajor(
+                                      L.x, b["xq"], b["xs"], b["xqt"], b["xst"]),
                                   bytes=M * din * (e + 2) + 4 * (b["xs"].numel() + b["xst"].numel()),
                                   feeds=[(f"{L.name}.fprop", 0.5), (f"{L.name}.wgrad", 0.5)]))
                 else:
                     ops.append(Op(f"{L.name}.x act", "quant",
-                                  lambda L=L, b=b: quantize_act(L.x, b["xq"], b["xs"]),
+                                  lambda L=L, b=b: quantize_act_kmajor(L.x, b["xq"], b["xs"]),
                                   bytes=M * din * (e + 1) + 4 * b["xs"].numel(),
                                   feeds=[(f"{L.name}.fprop", 1.0)]))
-                ops.append(gemm_op(L, "fprop", "NT", b["xq"], b["xs"], b["wq"], b["ws"], "act",
+                ops.append(gemm_op(L, "fprop", "NT", b["xq"], b["xs"], b["wq"], b["ws"], "act_km",
                                    "block", b["y"], M, dout, din))
         for L in self.layers:
             b = L.buf
@@ -273,31 +282,34 @@ class HotPath:
             e = _esize(L.x)
             if both_dy:
                 ops.append(Op(f"{L.name}.dy dual", "quant",
-                              lambda L=L, b=b: quantize_act_dual(L.dy, b["dyq"], b["dys"],
-                                                                 b["dyqt"], b["dyst"]),
+                              lambda L=L, b=b: quantize_act_dual_kmajor(
+                                  L.dy, b["dyq"], b["dys"], b["dyqt"], b["dyst"]),
                               bytes=M * dout * (e + 2) + 4 * (b["dys"].numel() + b["dyst"].numel()),
                               feeds=[(f"{L.name}.dgrad", 0.5), (f"{L.name}.wgrad", 0.5)]))
             elif "dgrad" in roles:
                 ops.append(Op(f"{L.name}.dy act", "quant",
-                              lambda L=L, b=b: quantize_act(L.dy, b["dyq"], b["dys"]),
+                              lambda L=L, b=b: quantize_act_kmajor(L.dy, b["dyq"], b["dys"]),
                               bytes=M * dout * (e + 1) + 4 * b["dys"].numel(),
                               feeds=[(f"{L.name}.dgrad", 1.0)]))
             elif "wgrad" in roles:
                 ops.append(Op(f"{L.name}.dy transposed", "quant",
-                              lambda L=L, b=b: quantize_act_transposed(L.dy, b["dyqt"], b["dyst"]),
+                              lambda L=L, b=b: quantize_act_transposed_kmajor(
+                                  L.dy, b["dyqt"], b["dyst"]),
                               bytes=M * dout * (e + 1) + 4 * b["dyst"].numel(),
                               feeds=[(f"{L.name}.wgrad", 1.0)]))
             if "dgrad" in roles:
-                ops.append(gemm_op(L, "dgrad", "NN", b["dyq"], b["dys"], b["wq"], b["ws"], "act",
-                                   "block", b["dx"], M, din, dout))
+                ops.append(gemm_op(L, "dgrad", "NN", b["dyq"], b["dys"], b["wq"], b["ws"],
+                                   "act_km", "block", b["dx"], M, din, dout))
             if "wgrad" in roles:
                 if not both_x:
                     ops.append(Op(f"{L.name}.x transposed", "quant",
-                                  lambda L=L, b=b: quantize_act_transposed(L.x, b["xqt"], b["xst"]),
+                                  lambda L=L, b=b: quantize_act_transposed_kmajor(
+                                      L.x, b["xqt"], b["xst"]),
                                   bytes=M * din * (e + 1) + 4 * b["xst"].numel(),
                                   feeds=[(f"{L.name}.wgrad", 1.0)]))
                 ops.append(gemm_op(L, "wgrad", "NT", b["dyqt"], b["dyst"], b["xqt"], b["xst"],
-                                   "act", "act", b["dw"], dout, din, M, ws=b["ws_wgrad"]))
+                                   "act_km", "act_km", b["dw"], dout, din, M,
+                                   ws=b["ws_wgrad"]))
         return ops
 
     def _build_ops_mx(self) -> List[Op]:
@@ -306,7 +318,7 @@ class HotPath:
         groups the weight is too (in-features groups for fprop, out-features
         groups for dgrad), otherwise its 128x128 blocks serve both GEMMs."""
         grp = 32 if self.scales == "mx32" else 128
-        mode = "mx32" if grp == 32 else "act"
+        mode = "mx32" if grp == 32 else "act_km"
         ops: List[Op] = []
 
         def gemm_op(L, role, layout, a, sa, b, sb, ma, mb, out, M, N, K, ws=None):
@@ -338,8 +350,10 @@ class HotPath:
             else:
                 wmode = "block"
             ops.append(Op(f"{L.name}.x dual", "quant",
-                          lambda L=L, b=b: quantize_mx_act_dual(L.x, grp, b["xq"], b["xs"],
-                                                                b["xqt"], b["xst"]),
+                          (lambda L=L, b=b: quantize_mx_act_dual_kmajor(
+                              L.x, b["xq"], b["xs"], b["xqt"], b["xst"])) if grp == 128 else
+                          (lambda L=L, b=b: quantize_mx_act_dual(L.x, grp, b["xq"], b["xs"],
+                                                                 b["xqt"], b["xst"])),
                           bytes=M * din * (e + 2) + b["xs"].numel() + b["xst"].numel(),
                           feeds=[(f"{L.name}.fprop", 0.5), (f"{L.name}.wgrad", 0.5)]))
             ops.append(gemm_op(L, "fprop", "NT", b["xq"], b["xs"], b["wq"], b["ws"], mode, wmode,
@@ -350,8 +364,10 @@ class HotPath:
             dout = L.w.shape[0]
             e = _esize(L.x)
             ops.append(Op(f"{L.name}.dy dual", "quant",
-                          lambda L=L, b=b: quantize_mx_act_dual(L.dy, grp, b["dyq"], b["dys"],
-                                                                b["dyqt"], b["dyst"]),
+                          (lambda L=L, b=b: quantize_mx_act_dual_kmajor(
+                              L.dy, b["dyq"], b["dys"], b["dyqt"], b["dyst"])) if grp == 128 else
+                          (lambda L=L, b=b: quantize_mx_act_dual(L.dy, grp, b["dyq"], b["dys"],
+                                                                 b["dyqt"], b["dyst"])),
                           bytes=M * dout * (e + 2) + b["dys"].numel() + b["dyst"].numel(),
                           feeds=[(f"{L.name}.dgrad", 0.5), (f"{L.name}.wgrad", 0.5)]))
             if grp == 32:

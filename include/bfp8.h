@@ -44,6 +44,10 @@
  *                              B 'T' [N][K/128]   B 'N' [K/128][N]
  *   block mode (128x128):      A 'N' [ceil(M/128)][K/128]   A 'T' [K/128][ceil(M/128)]
  *                              B 'T' [ceil(N/128)][K/128]   B 'N' [K/128][ceil(N/128)]
+ *   act mode, K-block major (BFP8_SCALE_1x128_KMAJOR):  A [K/128][M]   B [K/128][N]
+ *     for either orientation of the codes: the scales of one K block are
+ *     contiguous, so each K block's scales are read as a few cache lines
+ *     (for a K-major operand this is the act-mode layout itself).
  *
  * Ownership and threading: the caller allocates every buffer (inputs,
  * codes, scales, outputs, workspace) in device memory.  The library keeps
@@ -86,7 +90,7 @@
 extern "C" {
 #endif
 
-#define BFP8_ABI_VERSION 4
+#define BFP8_ABI_VERSION 5
 
 typedef enum {
   BFP8_OK = 0,
@@ -104,9 +108,11 @@ typedef enum {
 typedef enum { BFP8_IN_BF16 = 0, BFP8_IN_F32 = 1 } bfp8_in_dtype;
 typedef enum { BFP8_NN = 0, BFP8_NT = 1, BFP8_TN = 2 } bfp8_layout;
 typedef enum {
-  BFP8_SCALE_1x128 = 0,   /* 1 x 128 groups along K                          */
-  BFP8_SCALE_128x128 = 1, /* 128 x 128 blocks                                */
-  BFP8_SCALE_1x32 = 2     /* 1 x 32 groups along K (E8M0 scales only: MXFP8) */
+  BFP8_SCALE_1x128 = 0,        /* 1 x 128 groups along K                          */
+  BFP8_SCALE_128x128 = 1,      /* 128 x 128 blocks                                */
+  BFP8_SCALE_1x32 = 2,         /* 1 x 32 groups along K (E8M0 scales only: MXFP8) */
+  BFP8_SCALE_1x128_KMAJOR = 3  /* 1 x 128 groups along K, scale tensor stored
+                                  [K/128][rows] whatever the code orientation */
 } bfp8_scale_mode;
 
 /*
@@ -153,6 +159,31 @@ bfp8_status bfp8_quantize_act_transposed(const void* x, bfp8_in_dtype dt, int64_
 bfp8_status bfp8_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
                                    int64_t ldx, uint8_t* q, int64_t ldq, float* s, uint8_t* qt,
                                    int64_t ldqt, float* st, hipStream_t stream);
+
+/*
+ * The same three quantisers with their scale tensors stored K-block major,
+ * the layout of BFP8_SCALE_1x128_KMAJOR: the tensor's rows are the groups
+ * along the grouped axis, its columns the other axis.  Codes are those of
+ * the calls above, byte for byte; every scale is the same value, transposed:
+ *   bfp8_quantize_act_kmajor             s  [cols/128][rows]
+ *   bfp8_quantize_act_transposed_kmajor  st [rows/128][cols]
+ *   bfp8_quantize_act_dual_kmajor        s  [cols/128][rows], st [rows/128][cols]
+ * (Puro-2B translation, section 3.2: the same groups along the reduction
+ * dimension.)  A quantiser then writes each tile's scales as one contiguous
+ * run, and the GEMM reads each K block's scales as a few cache lines, where
+ * [rows][groups] spreads them over one cache line per row.  Arguments and
+ * errors as for the calls above.
+ */
+bfp8_status bfp8_quantize_act_kmajor(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
+                                     int64_t ldx, uint8_t* q, int64_t ldq, float* s,
+                                     hipStream_t stream);
+bfp8_status bfp8_quantize_act_transposed_kmajor(const void* x, bfp8_in_dtype dt, int64_t rows,
+                                                int64_t cols, int64_t ldx, uint8_t* qt,
+                                                int64_t ldqt, float* st, hipStream_t stream);
+bfp8_status bfp8_quantize_act_dual_kmajor(const void* x, bfp8_in_dtype dt, int64_t rows,
+                                          int64_t cols, int64_t ldx, uint8_t* q, int64_t ldq,
+                                          float* s, uint8_t* qt, int64_t ldqt, float* st,
+                                          hipStream_t stream);
 
 /*
  * Weight quantiser: one scale per 128x128 block.
@@ -252,6 +283,14 @@ bfp8_status bfp8_quantize_mx_act_transposed(const void* x, bfp8_in_dtype dt, int
 bfp8_status bfp8_quantize_mx_act_dual(const void* x, bfp8_in_dtype dt, int64_t rows, int64_t cols,
                                       int64_t ldx, int group, uint8_t* q, int64_t ldq, uint8_t* s,
                                       uint8_t* qt, int64_t ldqt, uint8_t* st, hipStream_t stream);
+
+/* bfp8_quantize_mx_act_dual with group 128 and both scale tensors stored
+ * K-block major (s [cols/128][rows], st [rows/128][cols] E8M0 bytes), the
+ * layout of BFP8_SCALE_1x128_KMAJOR. */
+bfp8_status bfp8_quantize_mx_act_dual_kmajor(const void* x, bfp8_in_dtype dt, int64_t rows,
+                                             int64_t cols, int64_t ldx, uint8_t* q, int64_t ldq,
+                                             uint8_t* s, uint8_t* qt, int64_t ldqt, uint8_t* st,
+                                             hipStream_t stream);
 
 /* 128x128 weight blocks: q [rows][ldq], s [ceil(rows/128)][ceil(cols/128)]. */
 bfp8_status bfp8_quantize_mx_weight(const void* w, bfp8_in_dtype dt, int64_t rows, int64_t cols,

@@ -41,6 +41,8 @@ def test_header_declares_the_boundary():
                             "bfp8_quantize_mx_act_dual", "bfp8_quantize_mx_weight",
                             "bfp8_quantize_mx_weight_batch",
                             "bfp8_gemm_mx", "bfp8_gemm_static_scratch",
+                            "bfp8_quantize_act_kmajor", "bfp8_quantize_act_transposed_kmajor",
+                            "bfp8_quantize_act_dual_kmajor", "bfp8_quantize_mx_act_dual_kmajor",
                             "bfp8_status_str", "bfp8_abi_version"])
 
 
@@ -50,7 +52,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.bfp8_abi_version() == 4
+    assert L.bfp8_abi_version() == 5
     for code in range(10):
         assert len(L.bfp8_status_str(code)) > 0
     assert b"Inf or NaN" in L.bfp8_status_str(9)
@@ -174,7 +176,7 @@ def gemm(L, layout=1, M=256, N=384, K=512, A=P, lda=512, sA=P, ma=0, B=P, ldb=51
 def test_gemm_errors(L):
     assert gemm(L, layout=3) == LAYOUT
     assert gemm(L, ma=2) == SMODE                 # 1x32 needs E8M0 scales (bfp8_gemm_mx)
-    assert gemm(L, ma=3) == SMODE
+    assert gemm(L, ma=4) == SMODE
     assert gemm(L, mb=-1) == SMODE
     assert gemm(L, K=500) == SHAPE
     assert gemm(L, M=-1) == SHAPE
@@ -252,7 +254,7 @@ def gemm_mx(L, layout=1, M=256, N=384, K=512, A=P, lda=512, sA=P, ma=0, B=P, ldb
 
 def test_gemm_mx_errors(L):
     assert gemm_mx(L, layout=4) == LAYOUT
-    assert gemm_mx(L, ma=3) == SMODE
+    assert gemm_mx(L, ma=4) == SMODE
     assert gemm_mx(L, layout=2, ma=2, lda=256) == SMODE   # 1x32 A must be K-contiguous
     assert gemm_mx(L, layout=0, mb=2, ldb=384) == SMODE   # 1x32 B must be K-contiguous
     assert gemm_mx(L, K=200) == SHAPE
@@ -276,3 +278,23 @@ def test_static_scratch_gemm_rejects_before_any_launch(L):
     assert call() == WS
     assert "BFP8_STATIC_SCRATCH_BYTES (64u << 20)" in open(HEADER).read()
     assert bfp8.STATIC_SCRATCH_BYTES == 64 << 20
+
+
+def test_kmajor_scale_mode_and_quantisers_validate(L):
+    """BFP8_SCALE_1x128_KMAJOR (3) is a float32 and an E8M0 mode; the
+    K-block-major quantisers reject what the default ones reject."""
+    assert "BFP8_SCALE_1x128_KMAJOR = 3" in open(HEADER).read() and bfp8.MODES["act_km"] == 3
+    assert bfp8.gemm_workspace_bytes("NT", "act_km", "act_km", 2048, 2048, 16384) == \
+        bfp8.gemm_workspace_bytes("NT", "act", "act", 2048, 2048, 16384)
+    assert L.bfp8_gemm_workspace_bytes(1, 4, 0, 256, 256, 256) == ctypes.c_size_t(-1).value
+    # bfp8_gemm / bfp8_gemm_mx: mode 4 unknown
+    args = (1, 256, 256, 256, P, 256, P, 4, P, 256, P, 0, P, 256, None, 0, None)
+    assert L.bfp8_gemm(*args) == SMODE and L.bfp8_gemm_mx(*args) == SMODE
+    for fn in (L.bfp8_quantize_act_kmajor, L.bfp8_quantize_act_transposed_kmajor):
+        assert fn(P, 0, 256, 256, 256, P, 256, None, None) == NULL
+        assert fn(P, 7, 256, 256, 256, P, 256, P, None) == DTYPE
+    assert L.bfp8_quantize_act_kmajor(P, 0, 256, 100, 256, P, 256, P, None) == SHAPE
+    assert L.bfp8_quantize_act_transposed_kmajor(P, 0, 100, 256, 256, P, 256, P, None) == SHAPE
+    for fn in (L.bfp8_quantize_act_dual_kmajor, L.bfp8_quantize_mx_act_dual_kmajor):
+        assert fn(P, 0, 256, 256, 256, P, 256, P, None, 256, P, None) == NULL
+        assert fn(P, 0, 256, 100, 256, P, 256, P, P, 256, P, None) == SHAPE

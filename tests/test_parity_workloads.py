@@ -6,7 +6,8 @@ For every GEMM the oracle quantises only the rows/channels it needs (1x128
 groups are independent across rows, token groups across channels; weights are
 quantised whole).  The GPU's codes and scales for those rows / channels must
 match the oracle's bit for bit (codes byte for byte, float32 scales as uint32
-bits, E8M0 scales byte for byte), and every sampled GEMM output must pass the
+bits, E8M0 scales byte for byte; the pass keeps activation and gradient
+scales K-block major, the oracle's transposed), and every sampled GEMM output must pass the
 gate of tests/gate.py against the float64 product of the oracle's dequantised
 operands.  The survey's O6 figure (1e-2 * rms floor) is printed for each GEMM.
 """
@@ -27,6 +28,12 @@ def sample(n, k, rng):
     if n <= k:
         return np.arange(n)
     return np.sort(rng.choice(n, k, replace=False))
+
+
+def km(buf, idx):
+    """Rows `idx` of a K-block-major scale tensor ([groups][rows]), in the
+    oracle's [rows][groups] orientation."""
+    return buf[:, idx].t()
 
 
 def same_bits(got, exp, what):
@@ -62,7 +69,7 @@ def test_workload_hot_path(name):
             cols = sample(L.out_features, 256, rng)
             xq, xs = oracle.quantize_act(x[rows])
             same_bits(b["xq"][rows], xq, "xq")
-            same_bits(b["xs"][rows], xs, "xs")
+            same_bits(km(b["xs"], rows), xs, "xs")
             ac, asc = oracle.logical_operand(xq, xs, "A", "N", "act")
             C = b["y"].float().cpu().numpy()[np.ix_(rows, cols)]
             gate.check(C, ac, asc, wc_f[:, cols], ws_f[:, cols], (name, L.name, "fprop"))
@@ -72,7 +79,7 @@ def test_workload_hot_path(name):
             cols = sample(L.in_features, 256, rng)
             dq, ds = oracle.quantize_act(dy[rows])
             same_bits(b["dyq"][rows], dq, "dyq")
-            same_bits(b["dys"][rows], ds, "dys")
+            same_bits(km(b["dys"], rows), ds, "dys")
             ac, asc = oracle.logical_operand(dq, ds, "A", "N", "act")
             C = b["dx"].float().cpu().numpy()[np.ix_(rows, cols)]
             gate.check(C, ac, asc, wc_d[:, cols], ws_d[:, cols], (name, L.name, "dgrad"))
@@ -83,9 +90,9 @@ def test_workload_hot_path(name):
             aq, as_ = oracle.quantize_act_transposed(np.ascontiguousarray(dy[:, rows]))
             bq, bs = oracle.quantize_act_transposed(np.ascontiguousarray(x[:, cols]))
             same_bits(b["dyqt"][rows], aq, "dyqt")
-            same_bits(b["dyst"][rows], as_, "dyst")
+            same_bits(km(b["dyst"], rows), as_, "dyst")
             same_bits(b["xqt"][cols], bq, "xqt")
-            same_bits(b["xst"][cols], bs, "xst")
+            same_bits(km(b["xst"], cols), bs, "xst")
             parts = gate.operand_parts("NT", aq, as_, "act", bq, bs, "act")
             C = b["dw"].float().cpu().numpy()[np.ix_(rows, cols)]
             gate.check(C, *parts, (name, L.name, "wgrad"))
@@ -130,15 +137,16 @@ def test_layer_hot_path_power_of_two(scales):
         rows = sample(M, 160, rng)
         cols = sample(L.out_features, 192, rng)
         xq, xs = oracle.quantize_mx_act(x[rows], grp)
+        sc = (lambda buf, idx: km(buf, idx)) if grp == 128 else (lambda buf, idx: buf[idx])
         same_bits(b["xq"][rows], xq, "xq")
-        same_bits(b["xs"][rows], xs, "xs")
+        same_bits(sc(b["xs"], rows), xs, "xs")
         ac, asc = oracle.logical_mx_operand(xq, xs, "A", "N", mode)
         C = b["y"].float().cpu().numpy()[np.ix_(rows, cols)]
         gate.check(C, ac, asc, wf[0][:, cols], wf[1][:, cols], (scales, L.name, "fprop"))
         cols = sample(L.in_features, 192, rng)
         dq, ds = oracle.quantize_mx_act(dy[rows], grp)
         same_bits(b["dyq"][rows], dq, "dyq")
-        same_bits(b["dys"][rows], ds, "dys")
+        same_bits(sc(b["dys"], rows), ds, "dys")
         ac, asc = oracle.logical_mx_operand(dq, ds, "A", "N", mode)
         C = b["dx"].float().cpu().numpy()[np.ix_(rows, cols)]
         gate.check(C, ac, asc, wd[0][:, cols], wd[1][:, cols], (scales, L.name, "dgrad"))
@@ -147,9 +155,9 @@ def test_layer_hot_path_power_of_two(scales):
         aq, as_ = oracle.quantize_mx_act_transposed(np.ascontiguousarray(dy[:, orow]), grp)
         bq, bs = oracle.quantize_mx_act_transposed(np.ascontiguousarray(x[:, icol]), grp)
         same_bits(b["dyqt"][orow], aq, "dyqt")
-        same_bits(b["dyst"][orow], as_, "dyst")
+        same_bits(sc(b["dyst"], orow), as_, "dyst")
         same_bits(b["xqt"][icol], bq, "xqt")
-        same_bits(b["xst"][icol], bs, "xst")
+        same_bits(sc(b["xst"], icol), bs, "xst")
         parts = gate.operand_parts("NT", aq, as_, mode, bq, bs, mode, mx=True)
         C = b["dw"].float().cpu().numpy()[np.ix_(orow, icol)]
         gate.check(C, *parts, (scales, L.name, "wgrad"))
