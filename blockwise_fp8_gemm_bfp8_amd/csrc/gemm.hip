@@ -148,6 +148,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
+// 16 bytes from an LDS address that is only 8-byte aligned (an epilogue row
+// of a padded staging slot), as two 8-byte reads: a 16-byte read from such
+// an address stalls the LDS for extra cycles.
+__device__ __forceinline__ v4u lds_read16_a8(const uint8_t* p) {
+  const uint2 lo = *reinterpret_cast<const uint2*>(p);
+  const uint2 hi = *reinterpret_cast<const uint2*>(p + 8);
+  return v4u{lo.x, lo.y, hi.x, hi.y};
+}
+
 // 16-byte chunk swizzle of a K-major LDS tile row k (256 B per row): the
 // low three bits spread the 8 rows one tr8 read touches over 8 chunks, the
 // fourth bit moves lane groups g and g+1 (k differs by 16) to different
@@ -482,9 +491,9 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
   float ra_last[TM];
 
   // One K block computed from `cur` while the copy of block kb+1 into `nxt`
-  // (free since the previous barrier) is issued piecewise between the first
-  // MFMAs; then, once every wave's copies have landed, the fragments of
-  // block kb+1 are read from `nxt`.
+  // (free since the previous barrier) is issued piecewise between the MFMAs
+  // of the block's first half; then, once every wave's copies have landed,
+  // the fragments of block kb+1 are read from `nxt`.
   auto kblock = [&](int64_t kb, const uint8_t* cur, uint8_t* nxt) {
     const bool more = kb + 1 < kb_end;
     // The copies are issued unconditionally (no branch per piece): after the
@@ -516,7 +525,10 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
           promote(acc[i2][j2], pend[t % kLag], ra[i2], j2 == j ? cm_cur : cm_prev);
         }
         pend[t % kLag] = pc;
-        if (t >= 1 && t <= kLoadPieces) issue_piece(kn, nxt, t - 1);
+        // one copy piece every second MFMA slot (t = 1, 3, ..., 17): denser
+        // issue bunches the copies' LDS writes, sparser issue leaves too
+        // little time before the end-of-block wait (both measured slower)
+        if (t >= 1 && (t - 1) % 2 == 0 && (t - 1) / 2 < kLoadPieces) issue_piece(kn, nxt, (t - 1) / 2);
         // one MFMA and the promotion of the partial kLag issues back per
         // scheduling region: the machine scheduler would otherwise pull each
         // promotion up against the MFMA that produces it and stall on it
@@ -610,7 +622,7 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
     v4u v[WM / 4];
 #pragma unroll
     for (int u = 0; u < WM / 4; ++u)
-      v[u] = *reinterpret_cast<const v4u*>(slot + (4 * u + (lane >> 4)) * kEpiRowBytes + chunk * 16);
+      v[u] = lds_read16_a8(slot + (4 * u + (lane >> 4)) * kEpiRowBytes + chunk * 16);
     uint16_t* dst = C + (mw + (lane >> 4)) * ldc + nw + chunk * 8;
 #pragma unroll
     for (int u = 0; u < WM / 4; ++u)
@@ -620,7 +632,7 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
 #pragma unroll
   for (int u = 0; u < WM / 4; ++u) {
     const int row = 4 * u + (lane >> 4);
-    const uint4 v = *reinterpret_cast<const uint4*>(slot + row * kEpiRowBytes + chunk * 16);
+    const v4u v = lds_read16_a8(slot + row * kEpiRowBytes + chunk * 16);
     const int64_t m = mw + row, n = nw + chunk * 8;
     if (m >= M) continue;
     uint16_t* dst = C + m * ldc + n;
@@ -776,7 +788,7 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
   uint32_t wb = word_b(stage0, 0);
 
   // One K block from `cur`; the copy of block kb+1 into `nxt` is issued
-  // between the first MFMAs.  The barrier sits before the last column: its
+  // between the MFMAs of the block's first half.  The barrier sits before the last column: its
   // MFMAs run from registers while the next block's B fragment and, one
   // subtile at a time, its A fragments are read from `nxt`.
   auto kblock = [&](int64_t kb, const uint8_t* cur, uint8_t* nxt) {
@@ -817,7 +829,8 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
         // no copy): without an anchor the MFMAs drift away from the copies
         // and fragment reads they are meant to cover
         if (t >= 3) asm volatile("" : "+a"(acc[(t - 3) % T4M][(t - 3) / T4M]));
-        if (t >= 1 && t <= kPieces) issue_piece(kn, nxt, t - 1);
+        // one copy piece every second MFMA slot (t = 1, 3, ..., 35)
+        if (t >= 1 && (t - 1) % 2 == 0 && (t - 1) / 2 < kPieces) issue_piece(kn, nxt, (t - 1) / 2);
         if (j == T4N - 1) {
           af[i] = opa.frag(nxt, wm * W4M + 16 * i, lane);
           wa[i] = word_a(nxt, i);
@@ -888,8 +901,7 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
       v4u v[W4M / 8];
 #pragma unroll
       for (int u = 0; u < W4M / 8; ++u)
-        v[u] = *reinterpret_cast<const v4u*>(slot + (64 * h + 4 * u + (lane >> 4)) * k4EpiRowBytes +
-                                             chunk * 16);
+        v[u] = lds_read16_a8(slot + (64 * h + 4 * u + (lane >> 4)) * k4EpiRowBytes + chunk * 16);
 #pragma unroll
       for (int u = 0; u < W4M / 8; ++u)
         __builtin_nontemporal_store(v[u], reinterpret_cast<v4u*>(dst + (64 * h + 4 * u) * ldc));
@@ -899,7 +911,7 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
 #pragma unroll
   for (int u = 0; u < W4M / 4; ++u) {
     const int row = 4 * u + (lane >> 4);
-    const uint4 v = *reinterpret_cast<const uint4*>(slot + row * k4EpiRowBytes + chunk * 16);
+    const v4u v = lds_read16_a8(slot + row * k4EpiRowBytes + chunk * 16);
     const int64_t m = mw + row, n = nw + chunk * 8;
     if (m >= M) continue;
     uint16_t* dst = C + m * ldc + n;

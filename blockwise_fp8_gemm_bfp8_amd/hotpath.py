@@ -88,9 +88,10 @@ class TimingEvent:
             raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
         return ms.value
 
-    def __del__(self):
-        # at interpreter exit the HIP runtime may already be torn down
-        if self.ev and not sys.is_finalizing():
+    def __del__(self, _finalizing=sys.is_finalizing):
+        # at interpreter exit the HIP runtime (and this module's globals) may
+        # already be torn down
+        if self.ev and not _finalizing():
             self._h.hipEventDestroy(self.ev)
         self.ev = ctypes.c_void_p()
 
