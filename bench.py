@@ -325,6 +325,184 @@ def sweep(hp, reps):
     return out
 
 
+def scaled_mm_baseline(hp, reps):
+    """hipBLASLt's per-tensor-scaled FP8 GEMM (torch._scaled_mm, unit scales,
+    bf16 output) on each GEMM's own E4M3 code operands, beside the same call
+    of this library, both timed cold as in the sweep (median of `reps`).  The
+    vendor kernel applies no per-block scales and no promotion: it is the
+    matrix-core rate of a tuned kernel on the same bytes."""
+    import torch
+
+    from blockwise_fp8_gemm_bfp8_amd.hotpath import TimingEvent
+
+    f8 = torch.float8_e4m3fn
+    one = torch.ones((), dtype=torch.float32, device="cuda")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def cold(fn):
+        evs = []
+        for _ in range(reps):
+            torch.sum(flush, dim=(0,), out=sink)
+            s, e = TimingEvent(), TimingEvent()
+            s.record()
+            fn()
+            e.record()
+            evs.append((s, e))
+        torch.cuda.synchronize()
+        return statistics.median([s.elapsed_time(e) * 1e3 for s, e in evs])
+
+    out = []
+    for op in hp.ops:
+        if op.kind != "gemm" or op.codes is None:
+            continue
+        a, b = op.codes
+        if op.layout == "NT":      # A [M][K], B [N][K]
+            A, Bt = a.view(f8), b.view(f8)
+        elif op.layout == "NN":    # A [M][K], B [K][N]: B^T materialised once
+            A, Bt = a.view(f8), b.t().contiguous().view(f8)
+        else:
+            continue
+
+        def vendor(A=A, Bt=Bt):
+            torch._scaled_mm(A, Bt.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+
+        vendor()
+        op.fn()
+        torch.cuda.synchronize()
+        tv, to = cold(vendor), cold(op.fn)
+        M, N, K = op.mnk
+        rec = {"gemm": op.label, "layout": op.layout, "mnk": [M, N, K],
+               "hipblaslt_tensorwise_us": round(tv, 2), "ours_us": round(to, 2),
+               "hipblaslt_tflops": round(op.flops / (tv * 1e-6) / 1e12, 1),
+               "ours_tflops": round(op.flops / (to * 1e-6) / 1e12, 1)}
+        out.append(rec)
+        log(f"[bench] vs hipBLASLt {op.label:15s} {rec['hipblaslt_tensorwise_us']:8.1f} us "
+            f"({rec['hipblaslt_tflops']:6.1f} TFLOP/s)   ours {rec['ours_us']:8.1f} us "
+            f"({rec['ours_tflops']:6.1f})")
+    del flush
+    tv = sum(r["hipblaslt_tensorwise_us"] for r in out)
+    to = sum(r["ours_us"] for r in out)
+    fl = sum(op.flops for op in hp.ops if op.kind == "gemm" and op.codes is not None
+             and op.layout in ("NT", "NN"))
+    return {"kind": "torch._scaled_mm (hipBLASLt), per-tensor unit scales, on the pass's own "
+                    "E4M3 codes; cold median per GEMM",
+            "hipblaslt_tflops": round(fl / (tv * 1e-6) / 1e12, 1) if tv else None,
+            "ours_tflops": round(fl / (to * 1e-6) / 1e12, 1) if to else None,
+            "per_gemm": out}
+
+
+XCDS = 8            # MI355X: GRBM_GUI_ACTIVE counts once per XCD
+SIMDS = 256 * 4     # 256 CUs x 4 SIMDs
+
+
+def summarize_pmc(dirs, write_traffic=False, workload=DEFAULT_WORKLOAD):
+    """Markdown summary of rocprofv3 --pmc runs of this script (the
+    *counter_collection.csv files under each directory), per kernel: mean
+    duration, and whichever of these the counters allow -- graphics clock
+    (GRBM_GUI_ACTIVE over the 8 XCDs), MFMA busy fraction
+    (SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs), FP8 rate from the MFMA op
+    count, LDS issue stalls, bank conflicts and unaligned stalls, and HBM
+    bytes from FETCH_SIZE / WRITE_SIZE (KiB) scaled by what the same counter
+    reads for the 1 GiB copy of --copy-calibration.  With write_traffic, the
+    mean GEMM-kernel bytes per launch go to profiles/gemm_traffic.json,
+    stamped with the GEMM source hash."""
+    import csv
+    import glob
+
+    per = {}
+    copy = {}
+    for d in dirs:
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            disp = {}
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    e = disp.setdefault(r["Dispatch_Id"], [r["Kernel_Name"], int(r["End_Timestamp"])
+                                                           - int(r["Start_Timestamp"]), {}])
+                    e[2][r["Counter_Name"]] = float(r["Counter_Value"])
+            for name, dur, cs in disp.values():
+                if "copy" in name.lower():
+                    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+                        if c in cs:
+                            copy[c] = max(copy.get(c, 0.0), cs[c])
+                    continue
+                k = per.setdefault(_short_kernel_name(name), {"_dur": [], "_n": {}})
+                k["_dur"].append(dur)
+                for c, v in cs.items():
+                    k.setdefault(c, []).append(v)
+                k["_n"][f] = k["_n"].get(f, 0) + 1
+    gib_kib = float(1 << 20)
+    factor = {c: gib_kib / copy[c] for c in copy if copy[c] > 0}
+
+    def m(k, c):
+        v = k.get(c)
+        return sum(v) / len(v) if v else None
+
+    rows = []
+    traffic = []
+    for name, k in sorted(per.items(), key=lambda kv: -sum(kv[1]["_dur"])):
+        dur = sum(k["_dur"]) / len(k["_dur"])  # ns
+        launches = max(k["_n"].values())
+        r = {"kernel": name, "launches": launches, "us": dur / 1e3}
+        g = m(k, "GRBM_GUI_ACTIVE")
+        if g:
+            r["ghz"] = g / XCDS / dur
+            b = m(k, "SQ_VALU_MFMA_BUSY_CYCLES")
+            if b is not None:
+                r["mfma_busy"] = b / (SIMDS * g / XCDS)
+        mops = m(k, "SQ_INSTS_VALU_MFMA_MOPS_F8")
+        if mops:
+            r["fp8_tflops"] = mops * 512 / (dur * 1e-9) / 1e12
+        wc = m(k, "SQ_WAVE_CYCLES")
+        if wc:
+            for c, key in (("SQ_WAIT_INST_LDS", "wait_lds_issue"), ("SQ_WAIT_ANY", "wait_any")):
+                if m(k, c) is not None:
+                    r[key] = m(k, c) / wc
+        act = m(k, "SQ_LDS_IDX_ACTIVE")
+        if act:
+            if m(k, "SQ_LDS_BANK_CONFLICT") is not None:
+                r["lds_bank_conflict"] = m(k, "SQ_LDS_BANK_CONFLICT") / act
+            if m(k, "SQ_LDS_UNALIGNED_STALL") is not None:
+                r["lds_unaligned"] = m(k, "SQ_LDS_UNALIGNED_STALL") / act
+        nbytes = 0.0
+        for c, key in (("FETCH_SIZE", "fetch_mb"), ("WRITE_SIZE", "write_mb")):
+            if m(k, c) is not None and c in factor:
+                r[key] = m(k, c) * 1024 * factor[c] / 1e6
+                nbytes += r[key] * 1e6
+        if "fetch_mb" in r and "write_mb" in r:
+            r["hbm_gbs"] = nbytes / (dur * 1e-9) / 1e9
+            if name.startswith("gemm_kernel") or name.startswith("gemm_mx4_kernel"):
+                traffic += [nbytes] * launches
+        rows.append(r)
+    cols = [("launches", "launches", "{:d}"), ("us", "mean us", "{:.1f}"), ("ghz", "GHz", "{:.2f}"),
+            ("mfma_busy", "MFMA busy", "{:.1%}"), ("fp8_tflops", "FP8 TFLOP/s", "{:.0f}"),
+            ("wait_lds_issue", "LDS issue wait", "{:.1%}"), ("wait_any", "waitcnt/barrier", "{:.1%}"),
+            ("lds_bank_conflict", "bank confl.", "{:.1%}"), ("lds_unaligned", "unaligned", "{:.1%}"),
+            ("fetch_mb", "fetch MB", "{:.1f}"), ("write_mb", "write MB", "{:.1f}"),
+            ("hbm_gbs", "HBM GB/s", "{:.0f}")]
+    used = [c for c in cols if any(c[0] in r for r in rows)]
+    out = ["| kernel | " + " | ".join(c[1] for c in used) + " |",
+           "|---|" + "---|" * len(used)]
+    for r in rows:
+        out.append(f"| `{r['kernel']}` | " + " | ".join(
+            (c[2].format(r[c[0]]) if c[0] in r else "") for c in used) + " |")
+    if factor:
+        out += ["", "Copy calibration (1 GiB torch copy): " + ", ".join(
+            f"{c} reads {copy[c] / 1024:.1f} MiB -> factor {factor[c]:.3f}" for c in sorted(factor))]
+    if traffic:
+        mean = sum(traffic) / len(traffic)
+        out += ["", f"GEMM kernels: {mean / 1e6:.1f} MB of HBM-side traffic per launch (mean over "
+                    f"{len(traffic)} launches); GEMM source sha256[:16] = {gemm_source_hash()}."]
+        if write_traffic:
+            with open(TRAFFIC_FILE, "w") as fh:
+                json.dump({"gemm_source_sha256_16": gemm_source_hash(),
+                           "hbm_bytes_per_launch": int(mean),
+                           "fetch_factor": factor.get("FETCH_SIZE"),
+                           "write_factor": factor.get("WRITE_SIZE"), "workload": workload,
+                           "summary": f"profiles/gemm_hbm_traffic_{workload}.md"}, fh, indent=1)
+    return "\n".join(out)
+
+
 def _short_kernel_name(name):
     """'void ns::(anonymous namespace)::gemm_kernel<false, true, 0, 1>(args)' ->
     'gemm_kernel<false, true, 0, 1>'."""
@@ -409,10 +587,19 @@ def main():
                          "and exit; --steps / --warmup must match the traced run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+    ap.add_argument("--summarize-pmc", metavar="DIR", nargs="+",
+                    help="summarise rocprofv3 --pmc runs of this script (no GPU needed) and exit")
+    ap.add_argument("--write-traffic", action="store_true",
+                    help="with --summarize-pmc: record the GEMM bytes per launch for the line")
+    ap.add_argument("--scaled-mm-baseline", action="store_true",
+                    help="also time hipBLASLt's per-tensor FP8 GEMM on the pass's own codes")
     args = ap.parse_args()
 
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace, args.warmup, args.steps))
+        return
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc, args.write_traffic, args.workload))
         return
 
     if args.gpus != 1:
@@ -548,19 +735,21 @@ def main():
         if qroof is not None:
             qroof["cold_per_call"] = quant_cold
     # ---- phase 5: clock window ------------------------------------------------
-    clocks = ClockSampler()
-    torch.cuda.synchronize()
-    clocks.start()
-    t_c0 = time.perf_counter()
-    n_win = 0
-    while time.perf_counter() - t_c0 < args.clock_window:
-        for _ in range(10):
-            hp.run()
+    clock = None
+    if args.clock_window > 0:
+        clocks = ClockSampler()
         torch.cuda.synchronize()
-        n_win += 10
-    t_c1 = time.perf_counter()
-    clocks.stop()
-    clock = clocks.summary(t_c0, t_c1)
+        clocks.start()
+        t_c0 = time.perf_counter()
+        n_win = 0
+        while time.perf_counter() - t_c0 < args.clock_window:
+            for _ in range(10):
+                hp.run()
+            torch.cuda.synchronize()
+            n_win += 10
+        t_c1 = time.perf_counter()
+        clocks.stop()
+        clock = clocks.summary(t_c0, t_c1)
     if clock is not None:
         clock["window_s"] = round(t_c1 - t_c0, 2)
         clock["window_tflops"] = round(flops_step * n_win / (t_c1 - t_c0) / 1e12, 1)
@@ -577,6 +766,10 @@ def main():
     bf16 = None
     if not args.no_bf16_baseline:
         bf16 = bf16_baseline(tensors, wl, max(args.steps // 3, 3), value)
+
+    smm = None
+    if args.scaled_mm_baseline:
+        smm = scaled_mm_baseline(hp, min(args.reps, 20))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -628,6 +821,8 @@ def main():
         "cpu_baseline": cpu,
         "bf16_baseline": bf16,
     }
+    if smm is not None:
+        line["scaled_mm_baseline"] = smm
     print(json.dumps(line), flush=True)
 
 

@@ -114,7 +114,9 @@ class Op:
     -- inputs read once, codes and scales written once (for a GEMM: both code
     operands, their scales and the bf16 output).  feeds: for a quantiser, the
     GEMMs whose operands it writes, with the share of its time charged to
-    each (a dual quantiser serves two GEMMs, half each)."""
+    each (a dual quantiser serves two GEMMs, half each).  codes: for a GEMM,
+    its two code operands as passed (A, B), for comparisons on the same
+    bytes."""
 
     label: str
     kind: str
@@ -124,6 +126,7 @@ class Op:
     layout: str = ""
     mnk: Tuple[int, int, int] = (0, 0, 0)
     feeds: List[Tuple[str, float]] = field(default_factory=list)
+    codes: Optional[Tuple[torch.Tensor, torch.Tensor]] = None
 
 
 def _esize(t: torch.Tensor) -> int:
@@ -255,7 +258,7 @@ class HotPath:
             fn = (lambda: gemm(layout, a, sa, b, sb, ma, mb, out=out, workspace=ws)) if ws is not None \
                 else (lambda: gemm(layout, a, sa, b, sb, ma, mb, out=out))
             return Op(f"{L.name}.{role}", "gemm", fn, flops=2 * M * N * K, bytes=nbytes,
-                      layout=layout, mnk=(M, N, K))
+                      layout=layout, mnk=(M, N, K), codes=(a, b))
 
         for L in self.layers:
             b = L.buf
@@ -327,7 +330,7 @@ class HotPath:
             fn = (lambda: gemm_mx(layout, a, sa, b, sb, ma, mb, out=out, workspace=ws)) \
                 if ws is not None else (lambda: gemm_mx(layout, a, sa, b, sb, ma, mb, out=out))
             return Op(f"{L.name}.{role}", "gemm", fn, flops=2 * M * N * K, bytes=nbytes,
-                      layout=layout, mnk=(M, N, K))
+                      layout=layout, mnk=(M, N, K), codes=(a, b))
 
         if grp == 128:
             for i in range(0, len(self.layers), MAX_WEIGHT_JOBS):

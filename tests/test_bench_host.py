@@ -59,3 +59,43 @@ def test_family_roofline_is_mean_work_over_mean_time():
     q = bench.family_roofline(HP, mean_us, ("quant", "weight_quant"), "bytes")
     # 3e9 bytes per launch over 750 us
     assert q["achieved"] == 4000.0 and q["frac"] == 0.5 and q["unit"] == "GB/s"
+
+
+def test_pmc_summary_derives_busy_clock_and_calibrated_bytes(tmp_path, monkeypatch):
+    """Two counter runs of the same program (one per directory): the MFMA
+    busy fraction is busy cycles over 1024 SIMDs x (GRBM cycles / 8 XCDs),
+    and HBM bytes are the KiB counters scaled by the 1 GiB copy's reading."""
+    hdr = ('"Correlation_Id","Dispatch_Id","Agent_Id","Queue_Id","Process_Id","Thread_Id",'
+           '"Grid_Size","Kernel_Id","Kernel_Name","Workgroup_Size","LDS_Block_Size",'
+           '"Scratch_Size","VGPR_Count","Accum_VGPR_Count","SGPR_Count","Counter_Name",'
+           '"Counter_Value","Start_Timestamp","End_Timestamp"\n')
+
+    def row(d, name, c, v, t0, t1):
+        return f'{d},{d},"Agent 1",1,1,1,256,1,"{name}",256,0,0,8,0,16,"{c}",{v},{t0},{t1}\n'
+
+    g = "void ns::(anonymous namespace)::gemm_kernel<false, false, 3, 1>(unsigned char const*)"
+    cp = "void at::native::elementwise_kernel<copy_functor>(int)"
+    a = tmp_path / "a" / "x"
+    a.mkdir(parents=True)
+    # 100 us at 2 GHz: GRBM counts 8 x 200000 cycles; MFMA busy 40 % of 1024 SIMDs
+    (a / "p_counter_collection.csv").write_text(
+        hdr + row(1, g, "GRBM_GUI_ACTIVE", 1600000, 0, 100000)
+        + row(1, g, "SQ_VALU_MFMA_BUSY_CYCLES", 0.4 * 1024 * 200000, 0, 100000))
+    b = tmp_path / "b"
+    b.mkdir()
+    # the copy reads half of what moved (factor 2); the GEMM fetches 100 MiB as counted
+    (b / "q_counter_collection.csv").write_text(
+        hdr + row(1, cp, "FETCH_SIZE", 512 * 1024, 0, 10) + row(2, g, "FETCH_SIZE", 100 * 1024, 0, 100000))
+    c = tmp_path / "c"
+    c.mkdir()
+    (c / "q_counter_collection.csv").write_text(
+        hdr + row(1, cp, "WRITE_SIZE", 1024 * 1024, 0, 10) + row(2, g, "WRITE_SIZE", 50 * 1024, 0, 100000))
+    out_json = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out_json))
+    md = bench.summarize_pmc([str(tmp_path / "a"), str(b), str(c)], write_traffic=True)
+    line = [x for x in md.splitlines() if "gemm_kernel<false, false, 3, 1>" in x][0]
+    assert "| 2.00 |" in line and "| 40.0% |" in line
+    rec = json.loads(out_json.read_text())
+    assert rec["fetch_factor"] == 2.0 and rec["write_factor"] == 1.0
+    assert rec["hbm_bytes_per_launch"] == int((200 + 50) * 1024 * 1024)
+    assert rec["gemm_source_sha256_16"] == bench.gemm_source_hash()
