@@ -392,6 +392,44 @@ def scaled_mm_baseline(hp, reps):
             "per_gemm": out}
 
 
+def copy_ceiling(hp, reps):
+    """For each quantiser call: a plain device copy (torch copy_) of a
+    contiguous buffer with as many elements, of the same dtype, as the call
+    reads, timed cold like the sweep.  The copy reads and writes every
+    byte once with no arithmetic and one launch: the access-volume ceiling
+    for a kernel of that size (it moves at least the quantiser's bytes --
+    exactly them for the dual quantiser, whose two E4M3 outputs equal the
+    bf16 input in size).  Returns {op index: (median us, bytes moved)}."""
+    import torch
+
+    from blockwise_fp8_gemm_bfp8_amd.hotpath import TimingEvent
+
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    out = {}
+    for i, op in enumerate(hp.ops):
+        if op.kind == "gemm" or not op.src:
+            continue
+        n = sum(t.numel() for t in op.src)
+        a = torch.ones(n, dtype=op.src[0].dtype, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        evs = []
+        for _ in range(reps):
+            torch.sum(flush, dim=(0,), out=sink)
+            s, e = TimingEvent(), TimingEvent()
+            s.record()
+            b.copy_(a)
+            e.record()
+            evs.append((s, e))
+        torch.cuda.synchronize()
+        out[i] = (statistics.median([s.elapsed_time(e) * 1e3 for s, e in evs]),
+                  2 * n * a.element_size())
+        del a, b
+    del flush
+    return out
+
+
 XCDS = 8            # MI355X: GRBM_GUI_ACTIVE counts once per XCD
 SIMDS = 256 * 4     # 256 CUs x 4 SIMDs
 
@@ -593,6 +631,8 @@ def main():
                     help="with --summarize-pmc: record the GEMM bytes per launch for the line")
     ap.add_argument("--scaled-mm-baseline", action="store_true",
                     help="also time hipBLASLt's per-tensor FP8 GEMM on the pass's own codes")
+    ap.add_argument("--quant-ceiling", action="store_true",
+                    help="with the sweep: time a plain copy of each quantiser's input volume")
     args = ap.parse_args()
 
     if args.summarize_trace:
@@ -721,15 +761,24 @@ def main():
                 f"{per_gemm[-1]['gemm_tflops']:7.1f} TFLOP/s; incl. quant "
                 f"{per_gemm[-1]['incl_quant_tflops']:7.1f}")
         quant_cold = []
-        for op, st in zip(hp.ops, sw):
+        ceil = copy_ceiling(hp, args.reps) if args.quant_ceiling else {}
+        for i, (op, st) in enumerate(zip(hp.ops, sw)):
             if op.kind == "gemm":
                 continue
             gbs = op.bytes / (st["median"] * 1e-6) / 1e9
             quant_cold.append({"call": op.label, "median_us": round(st["median"], 2),
                                "p10_us": round(st["p10"], 2), "p90_us": round(st["p90"], 2),
                                "gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)})
+            extra = ""
+            if i in ceil:
+                cu, cb = ceil[i]
+                quant_cold[-1].update({"copy_same_input_us": round(cu, 2),
+                                       "copy_gbs": round(cb / (cu * 1e-6) / 1e9, 1),
+                                       "copy_time_over_quant_time": round(cu / st["median"], 3)})
+                extra = (f"; copy of the input volume {cu:6.1f} us "
+                         f"({cb / (cu * 1e-6) / 1e9:6.0f} GB/s)")
             log(f"[bench] {op.label:22s} median {st['median']:7.1f} us  {gbs:7.1f} GB/s "
-                f"({100 * gbs / HBM_PEAK_GBS:.1f} % of HBM)")
+                f"({100 * gbs / HBM_PEAK_GBS:.1f} % of HBM){extra}")
             if op.kind == "weight_quant":
                 weight_quant = (weight_quant or 0.0) + st["median"]
         if qroof is not None:

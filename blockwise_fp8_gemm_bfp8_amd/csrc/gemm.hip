@@ -825,22 +825,18 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
         const int t = j * T4M + i;
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
             bq, af[i], acc[i][j], 0, 0, 0, mxb, 0, mxa[i]);
-        // pin the accumulator of the MFMA three issues back (AGPR operand,
-        // no copy): without an anchor the MFMAs drift away from the copies
-        // and fragment reads they are meant to cover
-        if (t >= 3) asm volatile("" : "+a"(acc[(t - 3) % T4M][(t - 3) / T4M]));
         // one copy piece every second MFMA slot (t = 1, 3, ..., 35)
         if (t >= 1 && (t - 1) % 2 == 0 && (t - 1) / 2 < kPieces) issue_piece(kn, nxt, (t - 1) / 2);
         if (j == T4N - 1) {
           af[i] = opa.frag(nxt, wm * W4M + 16 * i, lane);
           wa[i] = word_a(nxt, i);
         }
+        // one MFMA per scheduling region (left to the scheduler, the
+        // instruction order it picks runs 10 % slower)
         __builtin_amdgcn_sched_barrier(0);
       }
       bq = bn;
     }
-#pragma unroll
-    for (int q = 0; q < 3; ++q) asm volatile("" : "+a"(acc[(T4M * T4N - 3 + q) % T4M][T4N - 1]));
   };
   // one copy of the block body with the stages picked at run time
   for (int kb = kb_begin; kb < kb_end; ++kb) {

@@ -17,6 +17,8 @@
 
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include "common.h"
 
 namespace bfp8 {
@@ -280,22 +282,164 @@ __global__ __launch_bounds__(256) void quantize_weight_kernel(
                                  blockIdx.x, red);
 }
 
-// Several weights in one launch: the flat block index walks the weights in
+constexpr int kWeightWgsPerCu = 4;  // two raw blocks per thread: ~130 VGPRs, 4 waves per SIMD
+
+// Several weights in one launch: a flat block index walks the weights in
 // order (first_block holds each weight's first index, kMaxWeightJobs + 1
-// entries), so the blocks of every weight run side by side and a weight
-// too small to fill the GPU on its own no longer leaves it idle.
-template <typename T, int RULE>
-__global__ __launch_bounds__(256) void quantize_weight_batch_kernel(WeightBatch b) {
-  __shared__ float red[4];
-  const int64_t blk = blockIdx.x;
+// entries), so the blocks of every weight run side by side and a weight too
+// small to fill the GPU on its own no longer leaves it idle.  The grid is a
+// fixed number of workgroups (a few per CU) that stride over the blocks;
+// each loads its next block into registers (raw input words) before it
+// reduces, encodes and stores the current one, so every workgroup keeps two
+// blocks of loads in flight and the whole batch runs as one round.  The
+// per-block arithmetic is that of quantize_weight_block.
+template <typename T>
+struct RawBlock;  // this thread's 64 input elements of one 128x128 block, as loaded
+template <>
+struct RawBlock<uint16_t> {
+  uint4 v[8];
+};
+template <>
+struct RawBlock<float> {
+  float4 v[16];
+};
+
+struct BlockRef {
+  int j;        // weight index
+  int64_t bm;   // block row
+  int64_t bk;   // block column
+};
+
+__device__ __forceinline__ BlockRef block_ref(const WeightBatch& b, int64_t blk) {
   int j = 0;
   while (j + 1 < b.n && blk >= b.first_block[j + 1]) ++j;
   const int64_t local = blk - b.first_block[j];
   const int64_t cb = b.col_blocks[j];
-  quantize_weight_block<T, RULE>(static_cast<const T*>(b.w[j]), b.ldw[j], b.rows[j], b.cols[j],
-                                 b.q[j], b.ldq[j],
-                                 static_cast<typename ScaleRule<RULE>::type*>(b.s[j]), cb,
-                                 local / cb, local % cb, red);
+  return BlockRef{j, local / cb, local % cb};
+}
+
+// Row r and first column c of this thread's vector u (0..7) of a block, and
+// how many of its 8 elements are inside the weight.
+__device__ __forceinline__ int vec_extent(const WeightBatch& b, const BlockRef& br, int u,
+                                          int64_t& r, int64_t& c) {
+  const int e = threadIdx.x + 256 * u;
+  r = br.bm * kGroup + (e >> 4);
+  c = br.bk * kGroup + (e & 15) * 8;
+  const int64_t left = b.cols[br.j] - c;
+  int n = left >= 8 ? 8 : (left > 0 ? static_cast<int>(left) : 0);
+  if (r >= b.rows[br.j]) n = 0;
+  return n;
+}
+
+template <typename T>
+__device__ __forceinline__ void load_raw(const WeightBatch& b, const BlockRef& br,
+                                         RawBlock<T>& raw) {
+  const T* w = static_cast<const T*>(b.w[br.j]);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    int64_t r, c;
+    const int n = vec_extent(b, br, u, r, c);
+    const T* p = w + r * b.ldw[br.j] + c;
+    if constexpr (sizeof(T) == 2) {
+      if (n == 8) {
+        raw.v[u] = *reinterpret_cast<const uint4*>(p);
+      } else {
+        uint32_t h[8];
+        for (int e = 0; e < 8; ++e) h[e] = e < n ? p[e] : 0u;
+        raw.v[u] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                              h[6] | (h[7] << 16));
+      }
+    } else {
+      if (n == 8) {
+        raw.v[2 * u] = reinterpret_cast<const float4*>(p)[0];
+        raw.v[2 * u + 1] = reinterpret_cast<const float4*>(p)[1];
+      } else {
+        float f[8];
+        for (int e = 0; e < 8; ++e) f[e] = e < n ? p[e] : 0.0f;
+        raw.v[2 * u] = make_float4(f[0], f[1], f[2], f[3]);
+        raw.v[2 * u + 1] = make_float4(f[4], f[5], f[6], f[7]);
+      }
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void unpack8(const RawBlock<T>& raw, int u, float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t w[4] = {raw.v[u].x, raw.v[u].y, raw.v[u].z, raw.v[u].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+      v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+    }
+  } else {
+    const float4 a = raw.v[2 * u], c = raw.v[2 * u + 1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
+  }
+}
+
+// Block amax (elements outside the weight were loaded as +0), scale, codes.
+template <typename T, int RULE>
+__device__ __forceinline__ void quantize_raw_block(const WeightBatch& b, const BlockRef& br,
+                                                   const RawBlock<T>& raw, float* red) {
+  float m = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    float v[8];
+    unpack8<T>(raw, u, v);
+    m = fmaxf(m, absmax8(v));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float inv;
+  const auto sc = ScaleRule<RULE>::make(amax, inv);
+  if (threadIdx.x == 0)
+    static_cast<typename ScaleRule<RULE>::type*>(b.s[br.j])[br.bm * b.col_blocks[br.j] + br.bk] = sc;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    int64_t r, c;
+    const int n = vec_extent(b, br, u, r, c);
+    if (n == 0) continue;
+    float v[8];
+    unpack8<T>(raw, u, v);
+    const uint2 codes = encode8(v, inv);
+    uint8_t* dst = b.q[br.j] + r * b.ldq[br.j] + c;
+    if (n == 8) {
+      *reinterpret_cast<uint2*>(dst) = codes;
+    } else {
+      for (int e = 0; e < n; ++e)
+        dst[e] = static_cast<uint8_t>((e < 4 ? codes.x >> (8 * e) : codes.y >> (8 * (e - 4))) & 0xFFu);
+    }
+  }
+}
+
+template <typename T, int RULE>
+__global__ __launch_bounds__(256) void quantize_weight_batch_kernel(WeightBatch b) {
+  // two reduction buffers, used alternately: a block's buffer is rewritten
+  // two blocks later, after the barrier of the block in between, which no
+  // thread passes before every thread has read the first
+  __shared__ float red[2][4];
+  const int64_t nblk = b.first_block[b.n];
+  int64_t blk = blockIdx.x;
+  if (blk >= nblk) return;  // uniform per workgroup
+  RawBlock<T> cur;
+  BlockRef cref = block_ref(b, blk);
+  load_raw<T>(b, cref, cur);
+  for (int ph = 0; blk < nblk; blk += gridDim.x, ph ^= 1) {
+    const int64_t nb = blk + gridDim.x;
+    RawBlock<T> nxt;
+    BlockRef nref = cref;
+    if (nb < nblk) {
+      nref = block_ref(b, nb);
+      load_raw<T>(b, nref, nxt);
+    }
+    quantize_raw_block<T, RULE>(b, cref, cur, red[ph]);
+    cur = nxt;
+    cref = nref;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -576,7 +720,15 @@ bfp8_status launch_quantize_weight_batch(const WeightBatch& b, bfp8_in_dtype dt,
                                          hipStream_t stream) {
   const int64_t blocks = b.first_block[b.n];
   if (blocks == 0) return BFP8_OK;
-  const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  // kWeightWgsPerCu workgroups per CU (the register-limited residency of
+  // the two-block form), never more than there are blocks
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return BFP8_ERR_HIP;
+  const int64_t wgs = std::min<int64_t>(blocks, static_cast<int64_t>(cus) * kWeightWgsPerCu);
+  const dim3 grid(static_cast<unsigned>(wgs)), block(256);
   if (dt == BFP8_IN_BF16) {
     if (rule == 0) return launch(&quantize_weight_batch_kernel<uint16_t, 0>, grid, block, stream, b);
     return launch(&quantize_weight_batch_kernel<uint16_t, 1>, grid, block, stream, b);

@@ -116,7 +116,7 @@ class Op:
     GEMMs whose operands it writes, with the share of its time charged to
     each (a dual quantiser serves two GEMMs, half each).  codes: for a GEMM,
     its two code operands as passed (A, B), for comparisons on the same
-    bytes."""
+    bytes.  src: for a quantiser, the tensors it reads."""
 
     label: str
     kind: str
@@ -127,6 +127,7 @@ class Op:
     mnk: Tuple[int, int, int] = (0, 0, 0)
     feeds: List[Tuple[str, float]] = field(default_factory=list)
     codes: Optional[Tuple[torch.Tensor, torch.Tensor]] = None
+    src: Tuple[torch.Tensor, ...] = ()
 
 
 def _esize(t: torch.Tensor) -> int:
@@ -251,7 +252,8 @@ class HotPath:
             ops.append(Op("weights", "weight_quant",
                           lambda g=group: quantize_weight_batch(
                               [L.w for L in g], [L.buf["wq"] for L in g],
-                              [L.buf["ws"] for L in g]), bytes=nbytes))
+                              [L.buf["ws"] for L in g]), bytes=nbytes,
+                          src=tuple(L.w for L in group)))
 
         def gemm_op(L, role, layout, a, sa, b, sb, ma, mb, out, M, N, K, ws=None):
             nbytes = a.numel() + b.numel() + 4 * (sa.numel() + sb.numel()) + 2 * M * N
@@ -271,12 +273,13 @@ class HotPath:
                                   lambda L=L, b=b: quantize_act_dual_kmajor(
                                       L.x, b["xq"], b["xs"], b["xqt"], b["xst"]),
                                   bytes=M * din * (e + 2) + 4 * (b["xs"].numel() + b["xst"].numel()),
-                                  feeds=[(f"{L.name}.fprop", 0.5), (f"{L.name}.wgrad", 0.5)]))
+                                  feeds=[(f"{L.name}.fprop", 0.5), (f"{L.name}.wgrad", 0.5)],
+                                  src=(L.x,)))
                 else:
                     ops.append(Op(f"{L.name}.x act", "quant",
                                   lambda L=L, b=b: quantize_act_kmajor(L.x, b["xq"], b["xs"]),
                                   bytes=M * din * (e + 1) + 4 * b["xs"].numel(),
-                                  feeds=[(f"{L.name}.fprop", 1.0)]))
+                                  feeds=[(f"{L.name}.fprop", 1.0)], src=(L.x,)))
                 ops.append(gemm_op(L, "fprop", "NT", b["xq"], b["xs"], b["wq"], b["ws"], "act_km",
                                    "block", b["y"], M, dout, din))
         for L in self.layers:
@@ -289,18 +292,19 @@ class HotPath:
                               lambda L=L, b=b: quantize_act_dual_kmajor(
                                   L.dy, b["dyq"], b["dys"], b["dyqt"], b["dyst"]),
                               bytes=M * dout * (e + 2) + 4 * (b["dys"].numel() + b["dyst"].numel()),
-                              feeds=[(f"{L.name}.dgrad", 0.5), (f"{L.name}.wgrad", 0.5)]))
+                              feeds=[(f"{L.name}.dgrad", 0.5), (f"{L.name}.wgrad", 0.5)],
+                              src=(L.dy,)))
             elif "dgrad" in roles:
                 ops.append(Op(f"{L.name}.dy act", "quant",
                               lambda L=L, b=b: quantize_act_kmajor(L.dy, b["dyq"], b["dys"]),
                               bytes=M * dout * (e + 1) + 4 * b["dys"].numel(),
-                              feeds=[(f"{L.name}.dgrad", 1.0)]))
+                              feeds=[(f"{L.name}.dgrad", 1.0)], src=(L.dy,)))
             elif "wgrad" in roles:
                 ops.append(Op(f"{L.name}.dy transposed", "quant",
                               lambda L=L, b=b: quantize_act_transposed_kmajor(
                                   L.dy, b["dyqt"], b["dyst"]),
                               bytes=M * dout * (e + 1) + 4 * b["dyst"].numel(),
-                              feeds=[(f"{L.name}.wgrad", 1.0)]))
+                              feeds=[(f"{L.name}.wgrad", 1.0)], src=(L.dy,)))
             if "dgrad" in roles:
                 ops.append(gemm_op(L, "dgrad", "NN", b["dyq"], b["dys"], b["wq"], b["ws"],
                                    "act_km", "block", b["dx"], M, din, dout))
@@ -310,7 +314,7 @@ class HotPath:
                                   lambda L=L, b=b: quantize_act_transposed_kmajor(
                                       L.x, b["xqt"], b["xst"]),
                                   bytes=M * din * (e + 1) + 4 * b["xst"].numel(),
-                                  feeds=[(f"{L.name}.wgrad", 1.0)]))
+                                  feeds=[(f"{L.name}.wgrad", 1.0)], src=(L.x,)))
                 ops.append(gemm_op(L, "wgrad", "NT", b["dyqt"], b["dyst"], b["xqt"], b["xst"],
                                    "act_km", "act_km", b["dw"], dout, din, M,
                                    ws=b["ws_wgrad"]))
@@ -339,7 +343,8 @@ class HotPath:
                 ops.append(Op("weights", "weight_quant",
                               lambda g=group: quantize_mx_weight_batch(
                                   [L.w for L in g], [L.buf["wq"] for L in g],
-                                  [L.buf["ws"] for L in g]), bytes=nbytes))
+                                  [L.buf["ws"] for L in g]), bytes=nbytes,
+                          src=tuple(L.w for L in group)))
         for L in self.layers:
             b = L.buf
             M, din = L.x.shape
@@ -349,7 +354,8 @@ class HotPath:
                 ops.append(Op(f"{L.name}.w dual", "weight_quant",
                               lambda L=L, b=b: quantize_mx_act_dual(L.w, 32, b["wq"], b["ws"],
                                                                     b["wqt"], b["wst"]),
-                              bytes=L.w.numel() * (e + 2) + b["ws"].numel() + b["wst"].numel()))
+                              bytes=L.w.numel() * (e + 2) + b["ws"].numel() + b["wst"].numel(),
+                              src=(L.w,)))
                 wmode = "mx32"
             else:
                 wmode = "block"
@@ -359,7 +365,7 @@ class HotPath:
                           (lambda L=L, b=b: quantize_mx_act_dual(L.x, grp, b["xq"], b["xs"],
                                                                  b["xqt"], b["xst"])),
                           bytes=M * din * (e + 2) + b["xs"].numel() + b["xst"].numel(),
-                          feeds=[(f"{L.name}.fprop", 0.5), (f"{L.name}.wgrad", 0.5)]))
+                          feeds=[(f"{L.name}.fprop", 0.5), (f"{L.name}.wgrad", 0.5)], src=(L.x,)))
             ops.append(gemm_op(L, "fprop", "NT", b["xq"], b["xs"], b["wq"], b["ws"], mode, wmode,
                                b["y"], M, dout, din))
         for L in self.layers:
@@ -373,7 +379,7 @@ class HotPath:
                           (lambda L=L, b=b: quantize_mx_act_dual(L.dy, grp, b["dyq"], b["dys"],
                                                                  b["dyqt"], b["dyst"])),
                           bytes=M * dout * (e + 2) + b["dys"].numel() + b["dyst"].numel(),
-                          feeds=[(f"{L.name}.dgrad", 0.5), (f"{L.name}.wgrad", 0.5)]))
+                          feeds=[(f"{L.name}.dgrad", 0.5), (f"{L.name}.wgrad", 0.5)], src=(L.dy,)))
             if grp == 32:
                 ops.append(gemm_op(L, "dgrad", "NT", b["dyq"], b["dys"], b["wqt"], b["wst"], mode,
                                    "mx32", b["dx"], M, din, dout))
