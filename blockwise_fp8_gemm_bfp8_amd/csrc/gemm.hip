@@ -302,6 +302,18 @@ __device__ __forceinline__ void load_mx_scales(const uint8_t* s, int64_t r0, int
                static_cast<uint32_t>(idx & ~int64_t(3)), make_rsrc(s, (bytes + 3) & ~int64_t(3)));
 }
 
+// K-block-major 1x128 scale bytes of 256 consecutive rows starting at byte
+// `first` of the `bytes`-byte tensor: wave `sub` copies words [64 sub,
+// 64 sub + 64) counted from the aligned word holding byte `first`, so the
+// tile's bytes sit at LDS offsets (first & 3) .. (first & 3) + 255 (words
+// past the tensor's end read as zero).
+__device__ __forceinline__ void load_mx_scale_bytes(const uint8_t* s, int64_t bytes, int64_t first,
+                                                    uint8_t* dst, int sub, int lane) {
+  const int64_t off = (first & ~int64_t(3)) + 4 * (64 * sub + lane);
+  copy4_to_lds(__builtin_amdgcn_readfirstlane(lds_addr(dst) + sub * 256), static_cast<uint32_t>(off),
+               make_rsrc(s, (bytes + 3) & ~int64_t(3)));
+}
+
 template <bool A_KM, bool B_KM, int MODE_A, int MODE_B>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(2, 2))) void
@@ -700,8 +712,13 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
   opb.init(B, ldb, n0, N, K, wave, lane);
 
   // The copy of one K block: 8 x 1 KiB of A, 8 x 1 KiB of B and the scale
-  // words of 64 rows of A and 64 columns of B per wave.
+  // words of 64 rows of A and 64 columns of B per wave.  K-block-major 1x128
+  // scales (kBytes*) are copied as the bytes themselves: the tile's 256
+  // consecutive bytes of block kb, from the aligned word at or before the
+  // first, so a lane reads its row's byte with one ds_read_u8 and passes it
+  // to the MFMA as is.
   constexpr int kPieces = 18;
+  constexpr bool kBytesA = SKA && MA == 0, kBytesB = SKB && MB == 0;
   i32x4 rsrc_a, rsrc_b;
   auto issue_piece = [&](int64_t kb, uint8_t* st, int piece) {
     if (piece < 8) {
@@ -712,10 +729,13 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
       uint8_t* sdst = st + kTileABytes + kTileBBytes;
       // every wave copies (for 128x128 blocks the copies of waves 1-3 land
       // beside wave 0's and are never read): no wave-dependent branch
-      if (piece == 16)
-        load_mx_scales<SKA, MA>(eA, m0, M, MBk, KB, kb, sdst, wave, lane);
-      else
-        load_mx_scales<SKB, MB>(eB, n0, N, NBk, KB, kb, sdst + 1024, wave, lane);
+      if (piece == 16) {
+        if constexpr (kBytesA) load_mx_scale_bytes(eA, M * KB, kb * M + m0, sdst, wave, lane);
+        else load_mx_scales<SKA, MA>(eA, m0, M, MBk, KB, kb, sdst, wave, lane);
+      } else {
+        if constexpr (kBytesB) load_mx_scale_bytes(eB, N * KB, kb * N + n0, sdst + 1024, wave, lane);
+        else load_mx_scales<SKB, MB>(eB, n0, N, NBk, KB, kb, sdst + 1024, wave, lane);
+      }
     }
   };
 
@@ -746,20 +766,33 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
   };
   // E8M0 scale words are read from LDS one column (B) or one block (A)
   // before the bytes are extracted, so the LDS latency hides under MFMAs
-  auto word_a = [&](const uint8_t* st, int i) -> uint32_t {
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(st + kTileABytes + kTileBBytes);
+  // (byte mode: the byte itself, read at the block's misalignment o)
+  auto word_a = [&](const uint8_t* st, int i, int64_t kbw) -> uint32_t {
+    const uint8_t* sb = st + kTileABytes + kTileBBytes;
+    if constexpr (kBytesA) {
+      const uint32_t o = static_cast<uint32_t>(kbw * M + m0) & 3u;
+      return sb[o + wm * W4M + 16 * i + r16];
+    }
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(sb);
     return MA == 1 ? w[(wm * W4M) / 128] : w[wm * W4M + 16 * i + r16];
   };
   auto byte_a = [&](uint32_t word, int64_t kb, int i) -> int {
+    if constexpr (kBytesA) return static_cast<int>(word);
     const uint32_t ka = kterm(MA, SKA, M, MBk, kb);
     const uint32_t sh = MA == 2 ? 8u * g : 8u * (((pack_a >> (2 * i)) + ka) & 3u);
     return static_cast<int>((word >> sh) & 0xFFu);
   };
-  auto word_b = [&](const uint8_t* st, int j) -> uint32_t {
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(st + kTileABytes + kTileBBytes) + BM;
+  auto word_b = [&](const uint8_t* st, int j, int64_t kbw) -> uint32_t {
+    const uint8_t* sb = st + kTileABytes + kTileBBytes + 4 * BM;
+    if constexpr (kBytesB) {
+      const uint32_t o = static_cast<uint32_t>(kbw * N + n0) & 3u;
+      return sb[o + wn * W4N + 16 * j + r16];
+    }
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(sb);
     return MB == 1 ? w[(wn * W4N) / 128] : w[wn * W4N + 16 * j + r16];
   };
   auto byte_b = [&](uint32_t word, int64_t kb, int j) -> int {
+    if constexpr (kBytesB) return static_cast<int>(word);
     const uint32_t kbb = kterm(MB, SKB, N, NBk, kb);
     const uint32_t sh = MB == 2 ? 8u * g : 8u * (((pack_b >> (2 * j)) + kbb) & 3u);
     return static_cast<int>((word >> sh) & 0xFFu);
@@ -784,8 +817,8 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
   for (int i = 0; i < T4M; ++i) af[i] = opa.frag(stage0, wm * W4M + 16 * i, lane);
   uint32_t wa[T4M];
 #pragma unroll
-  for (int i = 0; i < T4M; ++i) wa[i] = word_a(stage0, i);
-  uint32_t wb = word_b(stage0, 0);
+  for (int i = 0; i < T4M; ++i) wa[i] = word_a(stage0, i, kb_begin);
+  uint32_t wb = word_b(stage0, 0, kb_begin);
 
   // One K block from `cur`; the copy of block kb+1 into `nxt` is issued
   // between the MFMAs of the block's first half.  The barrier sits before the last column: its
@@ -803,13 +836,15 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
     int mxa[T4M];
 #pragma unroll
     for (int i = 0; i < T4M; ++i) mxa[i] = byte_a(wa[i], kb, i);
+    // 128x128 blocks: one B scale byte for the wave's whole 128 columns
+    const int mxb_blk = MB == 1 ? byte_b(wb, kb, 0) : 0;
 #pragma unroll
     for (int j = 0; j < T4N; ++j) {
-      const int mxb = byte_b(wb, kb, j);
+      const int mxb = MB == 1 ? mxb_blk : byte_b(wb, kb, j);
       v8i bn = bq;
       if (j + 1 < T4N) {
         bn = opb.frag(cur + kTileABytes, wn * W4N + 16 * (j + 1), lane);
-        wb = word_b(cur, j + 1);
+        if constexpr (MB != 1) wb = word_b(cur, j + 1, kb);
       }
       // (after the last K block this barrier and the reads below are
       // harmless: the copies read nothing and the fragments go unused;
@@ -818,7 +853,7 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
         __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's copies of block kb+1 landed
         __syncthreads();                     // everyone's did, and `cur` is free
         bn = opb.frag(nxt + kTileABytes, wn * W4N, lane);
-        wb = word_b(nxt, 0);
+        wb = word_b(nxt, 0, kn);
       }
 #pragma unroll
       for (int i = 0; i < T4M; ++i) {
@@ -829,7 +864,7 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
         if (t >= 1 && (t - 1) % 2 == 0 && (t - 1) / 2 < kPieces) issue_piece(kn, nxt, (t - 1) / 2);
         if (j == T4N - 1) {
           af[i] = opa.frag(nxt, wm * W4M + 16 * i, lane);
-          wa[i] = word_a(nxt, i);
+          wa[i] = word_a(nxt, i, kn);
         }
         // one MFMA per scheduling region (left to the scheduler, the
         // instruction order it picks runs 10 % slower)

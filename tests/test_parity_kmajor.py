@@ -110,3 +110,41 @@ def test_gemm_kmajor_scales_bitwise(layout, ma, mb, mx):
     got = fn(layout, qa, sak, qb, sbk, mak if ma != "block" else ma, mbk if mb != "block" else mb)
     torch.cuda.synchronize()
     assert torch.equal(ref.view(torch.int16), got.view(torch.int16))
+
+
+@pytest.mark.parametrize("shape", [(301, 270, 1024), (1, 130, 640), (259, 513, 1152)])
+@pytest.mark.parametrize("mb", ["block", "act"])
+@pytest.mark.parametrize("mx", [False, True])
+def test_gemm_kmajor_scales_unaligned_rows(shape, mb, mx):
+    """Row counts that are not multiples of 4: the K-block-major scale bytes
+    of a tile then start at a different offset within a word in every K
+    block (the power-of-two kernel stages them as bytes from the aligned
+    word before the first)."""
+    M, N, K = shape
+    KB = K // 128
+    g = torch.Generator(device="cuda").manual_seed(M + N + K)
+    qa, qb = codes((M, K), g), codes((N, K), g)
+
+    def act_scales(rows):
+        if mx:
+            s = torch.randint(118, 137, (rows, KB), dtype=torch.uint8, device="cuda", generator=g)
+            return bfp8._scale_bytes(rows, KB, "cuda").copy_(s), \
+                bfp8._scale_bytes(KB, rows, "cuda").copy_(s.t())
+        s = (torch.rand((rows, KB), device="cuda", generator=g) + 0.5).contiguous()
+        return s, s.t().contiguous()
+
+    sa, sak = act_scales(M)
+    if mb == "block":
+        shp = ((N + 127) // 128, KB)
+        sb = (bfp8._scale_bytes(*shp, "cuda").copy_(
+            torch.randint(118, 137, shp, dtype=torch.uint8, device="cuda", generator=g)) if mx
+              else (torch.rand(shp, device="cuda", generator=g) + 0.5).contiguous())
+        sbk, mbk = sb, "block"
+    else:
+        sb, sbk = act_scales(N)
+        mbk = "act_km"
+    fn = bfp8.gemm_mx if mx else bfp8.gemm
+    ref = fn("NT", qa, sa, qb, sb, "act", mb)
+    got = fn("NT", qa, sak, qb, sbk, "act_km", mbk)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.view(torch.int16), got.view(torch.int16))
