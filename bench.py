@@ -11,6 +11,8 @@ any timed region.  Prints ONE JSON line on stdout; details go to stderr.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--scales fp32|mx128|mx32] [--reps R] [--no-sweep]
                   [--no-cpu-baseline] [--no-bf16-baseline] [--copy-calibration]
+                  [--scaled-mm-baseline] [--quant-ceiling] [--graph]
+                  [--summarize-trace DB | --summarize-pmc DIR... [--write-traffic]]
 
 Phases, in order (each after a synchronisation):
   1. W warm-up passes;
@@ -18,6 +20,8 @@ Phases, in order (each after a synchronisation):
      the workload's flops per pass over the mean pass time.  Each pass is also
      bracketed by a pair of HIP events (fence-free, on the launch stream), which
      give the median and p10/p90 of the pass time;
+  2b. with --graph: the pass captured once into a HIP graph (no memset, no
+     allocation in it) and K replays timed the same way (`graph_replay`);
   3. an instrumented copy of the same K passes, every kernel call bracketed
      by its own pair of events: each call's median launch time over the K
      passes, from which `roofline` (the GEMM family: mean flops per launch
@@ -633,6 +637,8 @@ def main():
                     help="also time hipBLASLt's per-tensor FP8 GEMM on the pass's own codes")
     ap.add_argument("--quant-ceiling", action="store_true",
                     help="with the sweep: time a plain copy of each quantiser's input volume")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time K replays of the pass captured into one HIP graph")
     args = ap.parse_args()
 
     if args.summarize_trace:
@@ -695,6 +701,33 @@ def main():
     step_ms = [s.elapsed_time(e) for s, e in step_ev]
     log(f"[bench] {ms_per_step:.3f} ms per step (wall), events median "
         f"{statistics.median(step_ms):.3f} ms, {value:.1f} TFLOP/s")
+
+    # ---- phase 2b (--graph): the pass captured once, replayed K times --------
+    graph = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            hp.run()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            hp.run()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        tg0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        gdt = (time.perf_counter() - tg0) / args.steps
+        graph = {"ms_per_step": round(gdt * 1e3, 4),
+                 "value": round(flops_step / gdt / 1e12, 2),
+                 "kind": "the same pass captured once into a HIP graph, K replays timed the "
+                         "same way (launch cost off the host)"}
+        log(f"[bench] graph replay: {gdt * 1e3:.3f} ms per step, {graph['value']:.1f} TFLOP/s")
+        del g
 
     # ---- phase 3: the same passes with every kernel call bracketed -----------
     # (every event is created before the passes are enqueued; per call, the
@@ -872,6 +905,8 @@ def main():
     }
     if smm is not None:
         line["scaled_mm_baseline"] = smm
+    if graph is not None:
+        line["graph_replay"] = graph
     print(json.dumps(line), flush=True)
 
 
