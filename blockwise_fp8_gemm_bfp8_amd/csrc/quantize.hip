@@ -443,7 +443,9 @@ __global__ __launch_bounds__(256) void quantize_weight_batch_kernel(WeightBatch 
 }
 
 // ---------------------------------------------------------------------------
-// K1+K2 fused: one read of a 128-token x (128*CB)-channel tile emits both
+// K1+K2 fused (float32 inputs, 1x32 groups, and bf16 inputs of 6144 channels
+// or more; bf16 128-groups on narrower inputs take quantize_dual_narrow_kernel
+// below): one read of a 128-token x (128*CB)-channel tile emits both
 // the row-grouped codes (groups along channels: the fprop / dgrad operand)
 // and the token-grouped codes written transposed (groups along tokens: the
 // wgrad operand).  Phase 1 works from registers (16 lanes per row group, as
@@ -597,6 +599,128 @@ __global__ __launch_bounds__(256 * CB) void quantize_dual_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// K1+K2 fused, bf16 input, 128-groups, one 128 x 128 tile per 256-thread
+// workgroup, for inputs of fewer than 6144 channels: the same outputs as
+// quantize_dual_kernel, with the tile transposed through LDS as E4M3 codes
+// (16 KiB) instead of as bf16 values (34 KiB), so twice as many workgroups
+// fit on a CU and the 2048 tiles of a 16384 x 2048 input run as one round.
+// Thread (rsub, lane16) holds tokens 8 rsub .. 8 rsub + 7 of channels
+// 8 lane16 .. 8 lane16 + 7 as raw bf16 words.  Row groups are quantised
+// from them directly; the column maxima of the four waves meet in LDS; each
+// thread then encodes its 8 x 8 values with the column scales, and its 8
+// codes of one channel (consecutive tokens) go to that channel's LDS row as
+// one 8-byte write.  The rows of the code tile are finally copied to qt as
+// 128-byte runs.  The 16-byte chunks of a code row are XOR-swizzled by
+// (channel / 8) & 7 to spread the writes over the banks.
+// ---------------------------------------------------------------------------
+constexpr int kNarrowCh = 128;
+
+template <int RULE, bool KM>
+__global__ __launch_bounds__(256) void quantize_dual_narrow_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+    typename ScaleRule<RULE>::type* __restrict__ s, uint8_t* __restrict__ qt, int64_t ldqt,
+    typename ScaleRule<RULE>::type* __restrict__ st, int64_t n_ch_blocks, int64_t n_tok_blocks) {
+  typedef typename ScaleRule<RULE>::type S;
+  __shared__ __attribute__((aligned(16))) uint8_t ct[kNarrowCh * 128];  // [channel][token]
+  __shared__ float colmax[4][kNarrowCh];
+  __shared__ __attribute__((aligned(16))) S rsc[128];
+  const int tid = threadIdx.x;
+  const int lane16 = tid & 15, rsub = tid >> 4, wave = tid >> 6;
+  const int64_t cb = blockIdx.x, tb = blockIdx.y;
+  const int64_t m0 = tb * 128, c0 = cb * 128;
+
+  typedef uint32_t raw4 __attribute__((ext_vector_type(4)));
+  raw4 raw[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    raw[u] = *reinterpret_cast<const raw4*>(x + (m0 + 8 * rsub + u) * ldx + c0 + lane16 * 8);
+  auto elem = [&](int u, int k) -> float {
+    const uint32_t w = k < 2 ? raw[u].x : (k < 4 ? raw[u].y : (k < 6 ? raw[u].z : raw[u].w));
+    return bf16_bits_to_f32((k & 1) ? (w >> 16) : (w & 0xFFFFu));
+  };
+
+  // ---- row groups ---------------------------------------------------------
+  float cm[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) cm[k] = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      v[k] = elem(u, k);
+      cm[k] = fmaxf(cm[k], fabsf(v[k]));
+    }
+    const float amax = row16_max(absmax8(v));
+    float inv;
+    const S sc = ScaleRule<RULE>::make(amax, inv);
+    const int64_t r = m0 + 8 * rsub + u;
+    *reinterpret_cast<uint2*>(q + r * ldq + c0 + lane16 * 8) = encode8(v, inv);
+    if (lane16 == 0) {
+      if (KM) rsc[8 * rsub + u] = sc;
+      else s[r * n_ch_blocks + cb] = sc;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // the column pass re-reads the raw words (keeps the unpacked values from
+  // living across both passes, which would halve the resident workgroups)
+#pragma unroll
+  for (int u = 0; u < 8; ++u) asm volatile("" : "+v"(raw[u]));
+
+  // ---- column maxima: the wave's four token octets, then the four waves ----
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    cm[k] = fmaxf(cm[k], __shfl_xor(cm[k], 16));
+    cm[k] = fmaxf(cm[k], __shfl_xor(cm[k], 32));
+  }
+  if ((tid & 48) == 0) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) colmax[wave][lane16 * 8 + k] = cm[k];
+  }
+  __syncthreads();
+
+  // ---- token groups: encode with the column scales, transpose via LDS ----
+  // (one channel at a time, its scale stored at once, so that only the raw
+  // words stay live across the loop)
+  const int chunk_w = (rsub >> 1) ^ (lane16 & 7);  // tokens 8 rsub .. +7: chunk rsub / 2
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int c = lane16 * 8 + k;
+    const float amax = fmaxf(fmaxf(colmax[0][c], colmax[1][c]), fmaxf(colmax[2][c], colmax[3][c]));
+    float inv;
+    const S sc = ScaleRule<RULE>::make(amax, inv);
+    const uint32_t lo = encode4(elem(0, k) * inv, elem(1, k) * inv, elem(2, k) * inv, elem(3, k) * inv);
+    const uint32_t hi = encode4(elem(4, k) * inv, elem(5, k) * inv, elem(6, k) * inv, elem(7, k) * inv);
+    *reinterpret_cast<uint2*>(&ct[c * 128 + chunk_w * 16 + (rsub & 1) * 8]) = make_uint2(lo, hi);
+    if (rsub == 0) {
+      if (KM) st[tb * (n_ch_blocks * 128) + c0 + c] = sc;
+      else st[(c0 + c) * n_tok_blocks + tb] = sc;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();
+
+  // ---- code rows -> qt (8 lanes per channel, 16 bytes each) ----------------
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int c = pass * 32 + (tid >> 3), chunk = tid & 7;
+    const int phys = chunk ^ ((c >> 3) & 7);
+    const uint4 w = *reinterpret_cast<const uint4*>(&ct[c * 128 + phys * 16]);
+    *reinterpret_cast<uint4*>(qt + (c0 + c) * ldqt + m0 + chunk * 16) = w;
+  }
+  if (KM && tid < 32) {
+    // the tile's 128 row scales of channel block cb, one contiguous run
+    S* dst = s + cb * (n_tok_blocks * 128) + m0;
+    if constexpr (sizeof(S) == 4) {
+      reinterpret_cast<float4*>(dst)[tid] = reinterpret_cast<const float4*>(rsc)[tid];
+    } else {
+      reinterpret_cast<uint32_t*>(dst)[tid] = reinterpret_cast<const uint32_t*>(rsc)[tid];
+    }
+  }
+}
+
 // ---- opt-in input check (BFP8_DEBUG) ---------------------------------------
 // One flag word per GPU: set to 1 by any thread that finds a non-finite
 // input element.  Cleared by a kernel (not a memset) before each check.
@@ -708,6 +832,23 @@ bfp8_status launch_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t ro
   }
   dim3 grid(static_cast<unsigned>(ch_blocks), static_cast<unsigned>(tok_blocks));
   bfp8_status status = BFP8_OK;
+  // bf16 inputs of fewer channels, 128-groups: the code-transposing form
+  if (dt == BFP8_IN_BF16 && group == kGroup) {
+    if (rule == 0) {
+      if (km) return launch(&quantize_dual_narrow_kernel<0, true>, grid, dim3(256), stream,
+                            static_cast<const uint16_t*>(x), ldx, q, ldq, static_cast<float*>(s),
+                            qt, ldqt, static_cast<float*>(st), ch_blocks, tok_blocks);
+      return launch(&quantize_dual_narrow_kernel<0, false>, grid, dim3(256), stream,
+                    static_cast<const uint16_t*>(x), ldx, q, ldq, static_cast<float*>(s), qt, ldqt,
+                    static_cast<float*>(st), ch_blocks, tok_blocks);
+    }
+    if (km) return launch(&quantize_dual_narrow_kernel<1, true>, grid, dim3(256), stream,
+                          static_cast<const uint16_t*>(x), ldx, q, ldq, static_cast<uint8_t*>(s),
+                          qt, ldqt, static_cast<uint8_t*>(st), ch_blocks, tok_blocks);
+    return launch(&quantize_dual_narrow_kernel<1, false>, grid, dim3(256), stream,
+                  static_cast<const uint16_t*>(x), ldx, q, ldq, static_cast<uint8_t*>(s), qt, ldqt,
+                  static_cast<uint8_t*>(st), ch_blocks, tok_blocks);
+  }
   BFP8_DISPATCH_KM((status = launch(&quantize_dual_kernel<T, R, G, 1, KMV>, grid, dim3(256), stream,
                                  static_cast<const T*>(x), ldx, q, ldq,
                                  static_cast<typename ScaleRule<R>::type*>(s), qt, ldqt,

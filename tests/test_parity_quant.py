@@ -176,15 +176,20 @@ def test_quantize_act_dual_equals_both_quantisers(dtype, rows, cols):
     assert_same_codes(qt, st, eqt, est, f"dual cols {rows}x{cols} {dtype}")
 
 
-def test_quantize_act_dual_adversarial():
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_quantize_act_dual_adversarial(dtype):
+    # (bf16: the corner cases rounded to bf16 -- the input of the
+    # code-transposing kernel that bf16 inputs under 6144 channels take)
     base = adversarial_groups()  # 12 x 128 rows of corner cases
     x = np.concatenate([base] * 11)[:128]
     x = np.concatenate([x, x.T.copy()], axis=1)  # corner cases along both axes
-    q, s_, qt, st = bfp8.quantize_act_dual(torch.from_numpy(np.ascontiguousarray(x)).cuda())
-    eq, es = oracle.quantize_act(x)
-    eqt, est = oracle.quantize_act_transposed(x)
-    assert_same_codes(q, s_, eq, es, "dual adversarial rows")
-    assert_same_codes(qt, st, eqt, est, "dual adversarial cols")
+    xt = torch.from_numpy(np.ascontiguousarray(x)).to(dtype)
+    q, s_, qt, st = bfp8.quantize_act_dual(xt.cuda())
+    xn = to_numpy_input(xt)
+    eq, es = oracle.quantize_act(xn)
+    eqt, est = oracle.quantize_act_transposed(xn)
+    assert_same_codes(q, s_, eq, es, f"dual adversarial rows {dtype}")
+    assert_same_codes(qt, st, eqt, est, f"dual adversarial cols {dtype}")
 
 
 # ---------------------------------------------------------------- weight
