@@ -444,11 +444,11 @@ __global__ __launch_bounds__(256) void quantize_weight_batch_kernel(WeightBatch 
 
 // ---------------------------------------------------------------------------
 // K1+K2 fused (float32 inputs, 1x32 groups, and bf16 inputs of 6144 channels
-// or more; bf16 128-groups on narrower inputs take quantize_dual_narrow_kernel
-// below): one read of a 128-token x (128*CB)-channel tile emits both
-// the row-grouped codes (groups along channels: the fprop / dgrad operand)
-// and the token-grouped codes written transposed (groups along tokens: the
-// wgrad operand).  Phase 1 works from registers (16 lanes per row group, as
+// or more with row-major scales; other bf16 128-group inputs take
+// quantize_dual_ct_kernel below): one read of a 128-token x (128*CB)-channel
+// tile emits both the row-grouped codes (groups along channels: the fprop /
+// dgrad operand) and the token-grouped codes written transposed (groups along
+// tokens: the wgrad operand).  Phase 1 works from registers (16 lanes per row group, as
 // K1) and parks the raw tile in LDS; phase 2 walks columns of the LDS tile
 // (two channels per thread, a quarter of the tokens each) as K2 does.  Both
 // outputs are bit-identical to the two separate quantisers.  CB = 2 (512
@@ -601,10 +601,11 @@ __global__ __launch_bounds__(256 * CB) void quantize_dual_kernel(
 
 // ---------------------------------------------------------------------------
 // K1+K2 fused, bf16 input, 128-groups, one 128 x 128 tile per 256-thread
-// workgroup, for inputs of fewer than 6144 channels: the same outputs as
-// quantize_dual_kernel, with the tile transposed through LDS as E4M3 codes
-// (16 KiB) instead of as bf16 values (34 KiB), so twice as many workgroups
-// fit on a CU and the 2048 tiles of a 16384 x 2048 input run as one round.
+// workgroup: the same outputs as quantize_dual_kernel, with the tile
+// transposed through LDS as E4M3 codes (16 KiB) instead of as bf16 values
+// (34 KiB), so the LDS traffic per tile halves and one barrier fewer is
+// needed (10 % faster on 2048 channels, 0.9-1.0 of a plain device copy of
+// the input at every width).
 // Thread (rsub, lane16) holds tokens 8 rsub .. 8 rsub + 7 of channels
 // 8 lane16 .. 8 lane16 + 7 as raw bf16 words.  Row groups are quantised
 // from them directly; the column maxima of the four waves meet in LDS; each
@@ -614,16 +615,16 @@ __global__ __launch_bounds__(256 * CB) void quantize_dual_kernel(
 // 128-byte runs.  The 16-byte chunks of a code row are XOR-swizzled by
 // (channel / 8) & 7 to spread the writes over the banks.
 // ---------------------------------------------------------------------------
-constexpr int kNarrowCh = 128;
+constexpr int kCtCh = 128;
 
 template <int RULE, bool KM>
-__global__ __launch_bounds__(256) void quantize_dual_narrow_kernel(
+__global__ __launch_bounds__(256) void quantize_dual_ct_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
     typename ScaleRule<RULE>::type* __restrict__ s, uint8_t* __restrict__ qt, int64_t ldqt,
     typename ScaleRule<RULE>::type* __restrict__ st, int64_t n_ch_blocks, int64_t n_tok_blocks) {
   typedef typename ScaleRule<RULE>::type S;
-  __shared__ __attribute__((aligned(16))) uint8_t ct[kNarrowCh * 128];  // [channel][token]
-  __shared__ float colmax[4][kNarrowCh];
+  __shared__ __attribute__((aligned(16))) uint8_t ct[kCtCh * 128];  // [channel][token]
+  __shared__ float colmax[4][kCtCh];
   __shared__ __attribute__((aligned(16))) S rsc[128];
   const int tid = threadIdx.x;
   const int lane16 = tid & 15, rsub = tid >> 4, wave = tid >> 6;
@@ -817,10 +818,12 @@ bfp8_status launch_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t ro
                                      hipStream_t stream) {
   if (rows == 0 || cols == 0) return BFP8_OK;
   const int64_t ch_blocks = cols / kGroup, tok_blocks = rows / kGroup;
-  // bf16 inputs of 6144 channels or more: 128 x 256 tiles (512 threads),
-  // whose row scales go out as 8-byte pairs (measured 5-7 % faster there,
-  // slower on narrower inputs)
-  if (dt == BFP8_IN_BF16 && ch_blocks % 2 == 0 && ch_blocks >= 48) {
+  // bf16 inputs of 6144 channels or more with row-major scales: 128 x 256
+  // tiles (512 threads), whose row scales go out as 8-byte pairs (measured
+  // 5-7 % faster there, slower on narrower inputs); with K-block-major
+  // scales every tile's scales leave as contiguous runs anyway and the
+  // code-transposing kernel below is as fast or faster at every width
+  if (dt == BFP8_IN_BF16 && ch_blocks % 2 == 0 && ch_blocks >= 48 && !(group == kGroup && km)) {
     dim3 grid2(static_cast<unsigned>(ch_blocks / 2), static_cast<unsigned>(tok_blocks));
     bfp8_status status = BFP8_OK;
     BFP8_DISPATCH_KM((status = launch(&quantize_dual_kernel<uint16_t, R, G, 2, KMV>, grid2, dim3(512),
@@ -832,20 +835,21 @@ bfp8_status launch_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t ro
   }
   dim3 grid(static_cast<unsigned>(ch_blocks), static_cast<unsigned>(tok_blocks));
   bfp8_status status = BFP8_OK;
-  // bf16 inputs of fewer channels, 128-groups: the code-transposing form
+  // bf16 inputs, 128-groups (all widths with K-block-major scales, fewer
+  // than 6144 channels otherwise): the code-transposing form
   if (dt == BFP8_IN_BF16 && group == kGroup) {
     if (rule == 0) {
-      if (km) return launch(&quantize_dual_narrow_kernel<0, true>, grid, dim3(256), stream,
+      if (km) return launch(&quantize_dual_ct_kernel<0, true>, grid, dim3(256), stream,
                             static_cast<const uint16_t*>(x), ldx, q, ldq, static_cast<float*>(s),
                             qt, ldqt, static_cast<float*>(st), ch_blocks, tok_blocks);
-      return launch(&quantize_dual_narrow_kernel<0, false>, grid, dim3(256), stream,
+      return launch(&quantize_dual_ct_kernel<0, false>, grid, dim3(256), stream,
                     static_cast<const uint16_t*>(x), ldx, q, ldq, static_cast<float*>(s), qt, ldqt,
                     static_cast<float*>(st), ch_blocks, tok_blocks);
     }
-    if (km) return launch(&quantize_dual_narrow_kernel<1, true>, grid, dim3(256), stream,
+    if (km) return launch(&quantize_dual_ct_kernel<1, true>, grid, dim3(256), stream,
                           static_cast<const uint16_t*>(x), ldx, q, ldq, static_cast<uint8_t*>(s),
                           qt, ldqt, static_cast<uint8_t*>(st), ch_blocks, tok_blocks);
-    return launch(&quantize_dual_narrow_kernel<1, false>, grid, dim3(256), stream,
+    return launch(&quantize_dual_ct_kernel<1, false>, grid, dim3(256), stream,
                   static_cast<const uint16_t*>(x), ldx, q, ldq, static_cast<uint8_t*>(s), qt, ldqt,
                   static_cast<uint8_t*>(st), ch_blocks, tok_blocks);
   }
