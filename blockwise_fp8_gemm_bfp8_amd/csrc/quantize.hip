@@ -617,12 +617,13 @@ __global__ __launch_bounds__(256 * CB) void quantize_dual_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kCtCh = 128;
 
-template <int RULE, bool KM, bool ROWS>
+template <int RULE, int GROUP, bool KM, bool ROWS>
 __global__ __launch_bounds__(256) void quantize_dual_ct_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
     typename ScaleRule<RULE>::type* __restrict__ s, uint8_t* __restrict__ qt, int64_t ldqt,
     typename ScaleRule<RULE>::type* __restrict__ st, int64_t n_ch_blocks, int64_t n_tok_blocks) {
   typedef typename ScaleRule<RULE>::type S;
+  constexpr int kSub = kGroup / GROUP;  // groups per 128 along either axis
   __shared__ __attribute__((aligned(16))) uint8_t ct[kCtCh * 128];  // [channel][token]
   __shared__ float colmax[4][kCtCh];
   __shared__ __attribute__((aligned(16))) S rsc[128];
@@ -654,14 +655,14 @@ __global__ __launch_bounds__(256) void quantize_dual_ct_kernel(
       cm[k] = fmaxf(cm[k], fabsf(v[k]));
     }
     if constexpr (!ROWS) continue;
-    const float amax = row16_max(absmax8(v));
+    const float amax = group_lanes_max<GROUP>(absmax8(v));
     float inv;
     const S sc = ScaleRule<RULE>::make(amax, inv);
     const int64_t r = m0 + 8 * rsub + u;
     *reinterpret_cast<uint2*>(q + r * ldq + c0 + lane16 * 8) = encode8(v, inv);
-    if (lane16 == 0) {
+    if (lane16 % (GROUP / 8) == 0) {
       if (KM) rsc[8 * rsub + u] = sc;
-      else s[r * n_ch_blocks + cb] = sc;
+      else s[r * n_ch_blocks * kSub + cb * kSub + lane16 / (GROUP / 8)] = sc;
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -671,17 +672,20 @@ __global__ __launch_bounds__(256) void quantize_dual_ct_kernel(
 #pragma unroll
   for (int u = 0; u < 8; ++u) asm volatile("" : "+v"(raw[u]));
 
-  // ---- column maxima: the wave's four token octets, then the four waves ----
+  // ---- column maxima: the wave's four token octets (a 32-token group), then
+  // for 128-token groups the four waves ------------------------------------
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     cm[k] = fmaxf(cm[k], __shfl_xor(cm[k], 16));
     cm[k] = fmaxf(cm[k], __shfl_xor(cm[k], 32));
   }
-  if ((tid & 48) == 0) {
+  if (GROUP == 128) {
+    if ((tid & 48) == 0) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) colmax[wave][lane16 * 8 + k] = cm[k];
+      for (int k = 0; k < 8; ++k) colmax[wave][lane16 * 8 + k] = cm[k];
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // ---- token groups: encode with the column scales, transpose via LDS ----
   // (one channel at a time, its scale stored at once, so that only the raw
@@ -690,15 +694,19 @@ __global__ __launch_bounds__(256) void quantize_dual_ct_kernel(
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int c = lane16 * 8 + k;
-    const float amax = fmaxf(fmaxf(colmax[0][c], colmax[1][c]), fmaxf(colmax[2][c], colmax[3][c]));
+    const float amax = GROUP == 128 ? fmaxf(fmaxf(colmax[0][c], colmax[1][c]),
+                                            fmaxf(colmax[2][c], colmax[3][c]))
+                                    : cm[k];
     float inv;
     const S sc = ScaleRule<RULE>::make(amax, inv);
     const uint32_t lo = encode4(elem(0, k) * inv, elem(1, k) * inv, elem(2, k) * inv, elem(3, k) * inv);
     const uint32_t hi = encode4(elem(4, k) * inv, elem(5, k) * inv, elem(6, k) * inv, elem(7, k) * inv);
     *reinterpret_cast<uint2*>(&ct[c * 128 + chunk_w * 16 + (rsub & 1) * 8]) = make_uint2(lo, hi);
-    if (rsub == 0) {
+    if (GROUP == 128 && rsub == 0) {
       if (KM) st[tb * (n_ch_blocks * 128) + c0 + c] = sc;
       else st[(c0 + c) * n_tok_blocks + tb] = sc;
+    } else if (GROUP == 32 && (rsub & 3) == 0) {
+      st[(c0 + c) * n_tok_blocks * kSub + tb * kSub + wave] = sc;
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -805,25 +813,18 @@ bfp8_status launch_quantize_act_transposed(const void* x, bfp8_in_dtype dt, int6
                                            hipStream_t stream) {
   if (rows == 0 || cols == 0) return BFP8_OK;
   const int64_t tok_blocks = rows / kTrTok;
-  // bf16, 128-groups, whole 128-channel blocks: the code-transposing kernel
-  // without its row groups (24 % faster than the fp32-tile kernel below at
-  // 8192 x 6144, and faster than a plain copy of its input)
-  if (dt == BFP8_IN_BF16 && group == kGroup && cols % kGroup == 0) {
+  // bf16, whole 128-channel blocks: the code-transposing kernel without its
+  // row groups (24 % faster than the fp32-tile kernel below at 8192 x 6144,
+  // and faster than a plain copy of its input)
+  if (dt == BFP8_IN_BF16 && cols % kGroup == 0) {
     const dim3 g2(static_cast<unsigned>(cols / kGroup), static_cast<unsigned>(tok_blocks));
-    const int64_t cb = cols / kGroup;
-    const uint16_t* xb = static_cast<const uint16_t*>(x);
-    if (rule == 0) {
-      float* stf = static_cast<float*>(st);
-      if (km) return launch(&quantize_dual_ct_kernel<0, true, false>, g2, dim3(256), stream, xb,
-                            ldx, nullptr, int64_t(0), nullptr, qt, ldqt, stf, cb, tok_blocks);
-      return launch(&quantize_dual_ct_kernel<0, false, false>, g2, dim3(256), stream, xb, ldx,
-                    nullptr, int64_t(0), nullptr, qt, ldqt, stf, cb, tok_blocks);
-    }
-    uint8_t* stb = static_cast<uint8_t*>(st);
-    if (km) return launch(&quantize_dual_ct_kernel<1, true, false>, g2, dim3(256), stream, xb, ldx,
-                          nullptr, int64_t(0), nullptr, qt, ldqt, stb, cb, tok_blocks);
-    return launch(&quantize_dual_ct_kernel<1, false, false>, g2, dim3(256), stream, xb, ldx,
-                  nullptr, int64_t(0), nullptr, qt, ldqt, stb, cb, tok_blocks);
+    bfp8_status status = BFP8_OK;
+    BFP8_DISPATCH_KM((status = launch(&quantize_dual_ct_kernel<R, G, KMV, false>, g2, dim3(256),
+                                      stream, static_cast<const uint16_t*>(x), ldx, nullptr,
+                                      int64_t(0), nullptr, qt, ldqt,
+                                      static_cast<typename ScaleRule<R>::type*>(st),
+                                      cols / kGroup, tok_blocks)));
+    return status;
   }
   dim3 grid(static_cast<unsigned>((cols + kTrCh - 1) / kTrCh), static_cast<unsigned>(tok_blocks));
   bfp8_status status = BFP8_OK;
@@ -844,7 +845,7 @@ bfp8_status launch_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t ro
   // 5-7 % faster there, slower on narrower inputs); with K-block-major
   // scales every tile's scales leave as contiguous runs anyway and the
   // code-transposing kernel below is as fast or faster at every width
-  if (dt == BFP8_IN_BF16 && ch_blocks % 2 == 0 && ch_blocks >= 48 && !(group == kGroup && km)) {
+  if (dt == BFP8_IN_BF16 && ch_blocks % 2 == 0 && ch_blocks >= 48 && group == kGroup && !km) {
     dim3 grid2(static_cast<unsigned>(ch_blocks / 2), static_cast<unsigned>(tok_blocks));
     bfp8_status status = BFP8_OK;
     BFP8_DISPATCH_KM((status = launch(&quantize_dual_kernel<uint16_t, R, G, 2, KMV>, grid2, dim3(512),
@@ -856,23 +857,15 @@ bfp8_status launch_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t ro
   }
   dim3 grid(static_cast<unsigned>(ch_blocks), static_cast<unsigned>(tok_blocks));
   bfp8_status status = BFP8_OK;
-  // bf16 inputs, 128-groups (all widths with K-block-major scales, fewer
+  // bf16 inputs (all widths with K-block-major scales or 32-groups, fewer
   // than 6144 channels otherwise): the code-transposing form
-  if (dt == BFP8_IN_BF16 && group == kGroup) {
-    if (rule == 0) {
-      if (km) return launch(&quantize_dual_ct_kernel<0, true, true>, grid, dim3(256), stream,
-                            static_cast<const uint16_t*>(x), ldx, q, ldq, static_cast<float*>(s),
-                            qt, ldqt, static_cast<float*>(st), ch_blocks, tok_blocks);
-      return launch(&quantize_dual_ct_kernel<0, false, true>, grid, dim3(256), stream,
-                    static_cast<const uint16_t*>(x), ldx, q, ldq, static_cast<float*>(s), qt, ldqt,
-                    static_cast<float*>(st), ch_blocks, tok_blocks);
-    }
-    if (km) return launch(&quantize_dual_ct_kernel<1, true, true>, grid, dim3(256), stream,
-                          static_cast<const uint16_t*>(x), ldx, q, ldq, static_cast<uint8_t*>(s),
-                          qt, ldqt, static_cast<uint8_t*>(st), ch_blocks, tok_blocks);
-    return launch(&quantize_dual_ct_kernel<1, false, true>, grid, dim3(256), stream,
-                  static_cast<const uint16_t*>(x), ldx, q, ldq, static_cast<uint8_t*>(s), qt, ldqt,
-                  static_cast<uint8_t*>(st), ch_blocks, tok_blocks);
+  if (dt == BFP8_IN_BF16) {
+    BFP8_DISPATCH_KM((status = launch(&quantize_dual_ct_kernel<R, G, KMV, true>, grid, dim3(256),
+                                      stream, static_cast<const uint16_t*>(x), ldx, q, ldq,
+                                      static_cast<typename ScaleRule<R>::type*>(s), qt, ldqt,
+                                      static_cast<typename ScaleRule<R>::type*>(st), ch_blocks,
+                                      tok_blocks)));
+    return status;
   }
   BFP8_DISPATCH_KM((status = launch(&quantize_dual_kernel<T, R, G, 1, KMV>, grid, dim3(256), stream,
                                  static_cast<const T*>(x), ldx, q, ldq,
