@@ -32,7 +32,7 @@ def test_bench_line_on_tiny_workload_with_every_leg():
     if d["clock"] and d["clock"].get("gfx_mhz_median"):
         adj = roof["clock_adjusted"]
         assert adj["peak"] == pytest.approx(5000.0 * d["clock"]["gfx_mhz_median"] / 2400.0, rel=1e-3)
-        assert adj["frac"] == pytest.approx(roof["achieved"] / adj["peak"], rel=1e-3)
+        assert adj["frac"] == pytest.approx(roof["achieved"] / adj["peak"], abs=1e-4)
     q = d["quant_roofline"]
     assert q["bound"] == "hbm" and 0 < q["frac"] < 1
     calls = {c["call"] for c in q["cold_per_call"]}
