@@ -175,23 +175,8 @@ struct Operand {
   __device__ __forceinline__ void init(const uint8_t* p, int64_t ld_, int64_t r0, int64_t rows,
                                        int64_t K_, int wave, int lane) {
     (void)K_;
-    const int64_t rows_left = rows - r0;  // valid rows (or columns) from the tile start
-    base = reinterpret_cast<uint64_t>(KMAJOR ? p + r0 : p + r0 * ld_);
+    rebase(p, ld_, r0, rows);
     kstride = KMAJOR ? BK * ld_ : BK;
-    // Extent from the start of a K block.  K-contiguous: up to the end of
-    // that block's part of the last valid row, so every copy of a row past
-    // the valid ones (offset >= valid rows * ld) reads zeros.  K-major: the
-    // block's 128 k rows, a ragged last column chunk read up to the next
-    // 16-byte boundary, which the padded leading dimension covers.
-    int64_t e;
-    if (!KMAJOR) {
-      const int64_t rv = rows_left > 256 ? 256 : rows_left;
-      e = (rv - 1) * ld_ + BK;
-    } else {
-      const int64_t cols = rows_left > 256 ? 256 : ((rows_left + 15) & ~int64_t(15));
-      e = (BK - 1) * ld_ + cols;
-    }
-    ext = __builtin_amdgcn_readfirstlane(static_cast<int>(e > 0x7FFFFFFF ? 0x7FFFFFFF : e));
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
       if (!KMAJOR) {
@@ -206,6 +191,27 @@ struct Operand {
         voff[j] = static_cast<uint32_t>(k * ld_ + c * 16);
       }
     }
+  }
+
+  // The tile-dependent part: base and extent of the tile whose rows (or
+  // columns) start at r0 (the per-lane offsets do not depend on the tile).
+  // Extent from the start of a K block.  K-contiguous: up to the end of that
+  // block's part of the last valid row, so every copy of a row past the
+  // valid ones (offset >= valid rows * ld) reads zeros.  K-major: the
+  // block's 128 k rows, a ragged last column chunk read up to the next
+  // 16-byte boundary, which the padded leading dimension covers.
+  __device__ __forceinline__ void rebase(const uint8_t* p, int64_t ld_, int64_t r0, int64_t rows) {
+    const int64_t rows_left = rows - r0;  // valid rows (or columns) from the tile start
+    base = reinterpret_cast<uint64_t>(KMAJOR ? p + r0 : p + r0 * ld_);
+    int64_t e;
+    if (!KMAJOR) {
+      const int64_t rv = rows_left > 256 ? 256 : rows_left;
+      e = (rv - 1) * ld_ + BK;
+    } else {
+      const int64_t cols = rows_left > 256 ? 256 : ((rows_left + 15) & ~int64_t(15));
+      e = (BK - 1) * ld_ + cols;
+    }
+    ext = __builtin_amdgcn_readfirstlane(static_cast<int>(e > 0x7FFFFFFF ? 0x7FFFFFFF : e));
   }
 
   // Buffer descriptor of K block kb: its first byte and the constant
@@ -673,7 +679,7 @@ constexpr int k4Threads = 256;
 constexpr int W4M = 128, W4N = 128;  // wave tile, 2 x 2 waves
 constexpr int T4M = W4M / 16, T4N = W4N / 16;
 constexpr int k4EpiRowBytes = W4N * 2 + 8;  // padded bf16 row of a wave tile
-static_assert(2 * W4M * k4EpiRowBytes <= kStageBytes, "two epilogue slots per stage");
+static_assert(4 * (W4M / 2) * k4EpiRowBytes <= kStageBytes, "four half-tile epilogue slots per stage");
 
 template <bool A_KM, bool B_KM, int MODE_A, int MODE_B>
 __global__ __attribute__((amdgpu_flat_work_group_size(k4Threads, k4Threads),
@@ -681,7 +687,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(k4Threads, k4Threads),
 gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__ sA_,
                 const uint8_t* __restrict__ B, int64_t ldb, const void* __restrict__ sB_,
                 uint16_t* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K, int tiles_m,
-                int tiles_n, float* __restrict__ part, int64_t ldp) {
+                int tiles_n, int splits, float* __restrict__ part, int64_t ldp) {
   const uint8_t* __restrict__ eA = static_cast<const uint8_t*>(sA_);
   const uint8_t* __restrict__ eB = static_cast<const uint8_t*>(sB_);
   // MODE 3: 1x128 groups, scale bytes stored K-block major ([K/128][rows])
@@ -696,31 +702,71 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
   const int wm = wave & 1, wn = wave >> 1;
   const int g = lane >> 4, r16 = lane & 15;
 
-  int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = static_cast<int64_t>(tm) * BM;
-  const int64_t n0 = static_cast<int64_t>(tn) * BN;
   const int64_t KB = K / BK;
   const int64_t MBk = (M + 127) / 128, NBk = (N + 127) / 128;
-  const int splits = gridDim.y, split = blockIdx.y;
-  const int kb_begin = static_cast<int>((split * static_cast<int>(KB)) / splits);
-  const int kb_end = static_cast<int>(((split + 1) * static_cast<int>(KB)) / splits);
+  // Persistent: this workgroup runs the work units blockIdx.x, blockIdx.x +
+  // gridDim.x, ... (a unit: one 256x256 output tile and one split-K range of
+  // its K blocks; units tiles .. 2 tiles - 1 are split 1, and so on).  The
+  // last K block of a unit copies the next unit's first block, and the
+  // output of a unit is stored while those copies land, so neither the
+  // copy latency of a tile's first block nor a new workgroup's start sits
+  // between two tiles.  The grid is a multiple of the 8 XCDs, so every unit
+  // of a workgroup maps to the XCD it runs on.
+  const int tiles = tiles_m * tiles_n;
+  const int units = tiles * splits;
+  auto unit_tile = [&](int v, int64_t& um0, int64_t& un0, int& ukb0, int& ukb1) {
+    const int sp = v / tiles;
+    int tm, tn;
+    tile_coords(v - sp * tiles, tiles, tiles_m, tiles_n, tm, tn);
+    um0 = static_cast<int64_t>(tm) * BM;
+    un0 = static_cast<int64_t>(tn) * BN;
+    ukb0 = static_cast<int>((sp * static_cast<int>(KB)) / splits);
+    ukb1 = static_cast<int>(((sp + 1) * static_cast<int>(KB)) / splits);
+    return sp;
+  };
 
+  // ---- per-unit state ---------------------------------------------------------
+  int v = blockIdx.x;
+  int64_t m0, n0;
+  int kb_begin, kb_end;
+  int split = unit_tile(v, m0, n0, kb_begin, kb_end);
   Operand<A_KM, 8> opa;
   Operand<B_KM, 8> opb;
   opa.init(A, lda, m0, M, K, wave, lane);
   opb.init(B, ldb, n0, N, K, wave, lane);
+  // the unit whose first K block the current unit's last block copies
+  int64_t xm0 = 0, xn0 = 0;
+  int xkb0 = 0, xkb1 = 0;
+  bool has_next = false;
+  uint64_t xbase_a = 0, xbase_b = 0;
+  int xext_a = 0, xext_b = 0;
+  auto peek_next = [&]() {
+    const int vn = v + static_cast<int>(gridDim.x);
+    has_next = vn < units;
+    if (has_next) {
+      unit_tile(vn, xm0, xn0, xkb0, xkb1);
+      Operand<A_KM, 8> xa = opa;
+      Operand<B_KM, 8> xb = opb;
+      xa.rebase(A, lda, xm0, M);
+      xb.rebase(B, ldb, xn0, N);
+      xbase_a = xa.base;
+      xext_a = xa.ext;
+      xbase_b = xb.base;
+      xext_b = xb.ext;
+    }
+  };
+  peek_next();
 
   // The copy of one K block: 8 x 1 KiB of A, 8 x 1 KiB of B and the scale
   // words of 64 rows of A and 64 columns of B per wave.  K-block-major 1x128
   // scales (kBytes*) are copied as the bytes themselves: the tile's 256
   // consecutive bytes of block kb, from the aligned word at or before the
   // first, so a lane reads its row's byte with one ds_read_u8 and passes it
-  // to the MFMA as is.
+  // to the MFMA as is.  cm0 / cn0: the tile the block belongs to.
   constexpr int kPieces = 18;
   constexpr bool kBytesA = SKA && MA == 0, kBytesB = SKB && MB == 0;
   i32x4 rsrc_a, rsrc_b;
-  auto issue_piece = [&](int64_t kb, uint8_t* st, int piece) {
+  auto issue_piece = [&](int64_t kb, uint8_t* st, int piece, int64_t cm0, int64_t cn0) {
     if (piece < 8) {
       opa.load_piece(rsrc_a, st, wave, piece);
     } else if (piece < 16) {
@@ -730,11 +776,11 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
       // every wave copies (for 128x128 blocks the copies of waves 1-3 land
       // beside wave 0's and are never read): no wave-dependent branch
       if (piece == 16) {
-        if constexpr (kBytesA) load_mx_scale_bytes(eA, M * KB, kb * M + m0, sdst, wave, lane);
-        else load_mx_scales<SKA, MA>(eA, m0, M, MBk, KB, kb, sdst, wave, lane);
+        if constexpr (kBytesA) load_mx_scale_bytes(eA, M * KB, kb * M + cm0, sdst, wave, lane);
+        else load_mx_scales<SKA, MA>(eA, cm0, M, MBk, KB, kb, sdst, wave, lane);
       } else {
-        if constexpr (kBytesB) load_mx_scale_bytes(eB, N * KB, kb * N + n0, sdst + 1024, wave, lane);
-        else load_mx_scales<SKB, MB>(eB, n0, N, NBk, KB, kb, sdst + 1024, wave, lane);
+        if constexpr (kBytesB) load_mx_scale_bytes(eB, N * KB, kb * N + cn0, sdst + 1024, wave, lane);
+        else load_mx_scales<SKB, MB>(eB, cn0, N, NBk, KB, kb, sdst + 1024, wave, lane);
       }
     }
   };
@@ -756,21 +802,27 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
     return static_cast<uint32_t>(km ? r : r * KB) & 3u;
   };
   uint32_t pack_a = 0, pack_b = 0;
+  auto set_packs = [&]() {
+    pack_a = 0;
+    pack_b = 0;
 #pragma unroll
-  for (int i = 0; i < T4M; ++i) pack_a |= byte_base(false, wm * W4M + 16 * i + r16) << (2 * i);
+    for (int i = 0; i < T4M; ++i) pack_a |= byte_base(false, wm * W4M + 16 * i + r16) << (2 * i);
 #pragma unroll
-  for (int j = 0; j < T4N; ++j) pack_b |= byte_base(true, wn * W4N + 16 * j + r16) << (2 * j);
+    for (int j = 0; j < T4N; ++j) pack_b |= byte_base(true, wn * W4N + 16 * j + r16) << (2 * j);
+  };
+  set_packs();
   auto kterm = [&](int mode, bool km, int64_t rows, int64_t nblk, int64_t kb) -> uint32_t {
     if (mode == 2) return 0;
     return static_cast<uint32_t>(km ? kb * (mode == 1 ? nblk : rows) : kb) & 3u;
   };
   // E8M0 scale words are read from LDS one column (B) or one block (A)
   // before the bytes are extracted, so the LDS latency hides under MFMAs
-  // (byte mode: the byte itself, read at the block's misalignment o)
-  auto word_a = [&](const uint8_t* st, int i, int64_t kbw) -> uint32_t {
+  // (byte mode: the byte itself, read at the block's misalignment o, which
+  // depends on the tile cm0 / cn0 of the block)
+  auto word_a = [&](const uint8_t* st, int i, int64_t kbw, int64_t cm0) -> uint32_t {
     const uint8_t* sb = st + kTileABytes + kTileBBytes;
     if constexpr (kBytesA) {
-      const uint32_t o = static_cast<uint32_t>(kbw * M + m0) & 3u;
+      const uint32_t o = static_cast<uint32_t>(kbw * M + cm0) & 3u;
       return sb[o + wm * W4M + 16 * i + r16];
     }
     const uint32_t* w = reinterpret_cast<const uint32_t*>(sb);
@@ -782,10 +834,10 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
     const uint32_t sh = MA == 2 ? 8u * g : 8u * (((pack_a >> (2 * i)) + ka) & 3u);
     return static_cast<int>((word >> sh) & 0xFFu);
   };
-  auto word_b = [&](const uint8_t* st, int j, int64_t kbw) -> uint32_t {
+  auto word_b = [&](const uint8_t* st, int j, int64_t kbw, int64_t cn0) -> uint32_t {
     const uint8_t* sb = st + kTileABytes + kTileBBytes + 4 * BM;
     if constexpr (kBytesB) {
-      const uint32_t o = static_cast<uint32_t>(kbw * N + n0) & 3u;
+      const uint32_t o = static_cast<uint32_t>(kbw * N + cn0) & 3u;
       return sb[o + wn * W4N + 16 * j + r16];
     }
     const uint32_t* w = reinterpret_cast<const uint32_t*>(sb);
@@ -799,16 +851,12 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
   };
 
   v4f acc[T4M][T4N];
-#pragma unroll
-  for (int i = 0; i < T4M; ++i)
-#pragma unroll
-    for (int j = 0; j < T4N; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // ---- prologue -----------------------------------------------------------
+  // ---- prologue of the first unit -------------------------------------------
   rsrc_a = opa.block_rsrc(kb_begin);
   rsrc_b = opb.block_rsrc(kb_begin);
 #pragma unroll
-  for (int p = 0; p < kPieces; ++p) issue_piece(kb_begin, stage0, p);
+  for (int p = 0; p < kPieces; ++p) issue_piece(kb_begin, stage0, p, m0, n0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
   v8i af[T4M];
@@ -817,19 +865,22 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
   for (int i = 0; i < T4M; ++i) af[i] = opa.frag(stage0, wm * W4M + 16 * i, lane);
   uint32_t wa[T4M];
 #pragma unroll
-  for (int i = 0; i < T4M; ++i) wa[i] = word_a(stage0, i, kb_begin);
-  uint32_t wb = word_b(stage0, 0, kb_begin);
+  for (int i = 0; i < T4M; ++i) wa[i] = word_a(stage0, i, kb_begin, m0);
+  uint32_t wb = word_b(stage0, 0, kb_begin, n0);
 
-  // One K block from `cur`; the copy of block kb+1 into `nxt` is issued
-  // between the MFMAs of the block's first half.  The barrier sits before the last column: its
-  // MFMAs run from registers while the next block's B fragment and, one
-  // subtile at a time, its A fragments are read from `nxt`.
+  // One K block from `cur`; the copy of the next block (this unit's, or the
+  // next unit's first) into `nxt` is issued between the MFMAs of the
+  // block's first half.  The barrier sits before the last column: its MFMAs
+  // run from registers while the next block's B fragment and, one subtile at
+  // a time, its A fragments are read from `nxt`.
   auto kblock = [&](int64_t kb, const uint8_t* cur, uint8_t* nxt) {
     const bool more = kb + 1 < kb_end;
-    const int64_t kn = more ? kb + 1 : kb;
-    rsrc_a = opa.block_rsrc(kn);
-    rsrc_b = opb.block_rsrc(kn);
-    if (!more) {
+    const bool to_next = !more && has_next;  // the same for the whole workgroup
+    const int64_t kn = more ? kb + 1 : (to_next ? xkb0 : kb);
+    const int64_t cm0 = to_next ? xm0 : m0, cn0 = to_next ? xn0 : n0;
+    rsrc_a = advanced_rsrc(to_next ? xbase_a : opa.base, kn, opa.kstride, to_next ? xext_a : opa.ext);
+    rsrc_b = advanced_rsrc(to_next ? xbase_b : opb.base, kn, opb.kstride, to_next ? xext_b : opb.ext);
+    if (!more && !to_next) {  // after the last unit: the copies read nothing
       rsrc_a.z = 0;
       rsrc_b.z = 0;
     }
@@ -844,16 +895,17 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
       v8i bn = bq;
       if (j + 1 < T4N) {
         bn = opb.frag(cur + kTileABytes, wn * W4N + 16 * (j + 1), lane);
-        if constexpr (MB != 1) wb = word_b(cur, j + 1, kb);
+        if constexpr (MB != 1) wb = word_b(cur, j + 1, kb, n0);
       }
-      // (after the last K block this barrier and the reads below are
-      // harmless: the copies read nothing and the fragments go unused;
-      // keeping them unconditional keeps the block body one basic block)
+      // (after the last K block of the last unit this barrier and the reads
+      // below are harmless: the copies read nothing and the fragments go
+      // unused; keeping them unconditional keeps the block body one basic
+      // block)
       if (j == T4N - 1) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's copies of block kb+1 landed
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's copies of the next block landed
         __syncthreads();                     // everyone's did, and `cur` is free
         bn = opb.frag(nxt + kTileABytes, wn * W4N, lane);
-        wb = word_b(nxt, 0, kn);
+        wb = word_b(nxt, 0, kn, cn0);
       }
 #pragma unroll
       for (int i = 0; i < T4M; ++i) {
@@ -861,10 +913,11 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
             bq, af[i], acc[i][j], 0, 0, 0, mxb, 0, mxa[i]);
         // one copy piece every second MFMA slot (t = 1, 3, ..., 35)
-        if (t >= 1 && (t - 1) % 2 == 0 && (t - 1) / 2 < kPieces) issue_piece(kn, nxt, (t - 1) / 2);
+        if (t >= 1 && (t - 1) % 2 == 0 && (t - 1) / 2 < kPieces)
+          issue_piece(kn, nxt, (t - 1) / 2, cm0, cn0);
         if (j == T4N - 1) {
           af[i] = opa.frag(nxt, wm * W4M + 16 * i, lane);
-          wa[i] = word_a(nxt, i, kn);
+          wa[i] = word_a(nxt, i, kn, cm0);
         }
         // one MFMA per scheduling region (left to the scheduler, the
         // instruction order it picks runs 10 % slower)
@@ -873,14 +926,10 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
       bq = bn;
     }
   };
-  // one copy of the block body with the stages picked at run time
-  for (int kb = kb_begin; kb < kb_end; ++kb) {
-    const bool odd = ((kb - kb_begin) & 1) != 0;
-    kblock(kb, odd ? stage1 : stage0, odd ? stage0 : stage1);
-  }
 
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the last copies landed
-  if (part != nullptr) {
+  // ---- epilogue pieces ----------------------------------------------------------
+  // split-K partial: 4 consecutive fp32 columns per lane, 16-byte stores
+  auto store_partial = [&]() {
     float* pbase = part + static_cast<int64_t>(split) * M * ldp;
     if (m0 + wm * W4M + W4M <= M && n0 + wn * W4N + W4N <= N) {
       float* dst = pbase + (m0 + wm * W4M + r16) * ldp + n0 + wn * W4N + 4 * g;
@@ -905,54 +954,85 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
         }
       }
     }
-    return;
-  }
-
-  // ---- epilogue: bf16 through LDS (two padded 128 x 128 slots per stage),
-  // then 16 lanes store each 256-byte output row, non-temporal
-  __syncthreads();
-  uint8_t* slot = (wave < 2 ? stage0 : stage1) + (wave & 1) * (W4M * k4EpiRowBytes);
-#pragma unroll
-  for (int i = 0; i < T4M; ++i) {
-#pragma unroll
-    for (int j = 0; j < T4N; ++j) {
-      *reinterpret_cast<uint2*>(slot + (16 * i + r16) * k4EpiRowBytes + (16 * j + 4 * g) * 2) =
-          make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]),
-                     pack_bf16x2(acc[i][j][2], acc[i][j][3]));
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's slot is written
-  __builtin_amdgcn_wave_barrier();
-  const int64_t mw = m0 + wm * W4M, nw = n0 + wn * W4N;
-  const int chunk = lane & 15;
-  if (mw + W4M <= M && nw + W4N <= N) {
-    uint16_t* dst = C + (mw + (lane >> 4)) * ldc + nw + chunk * 8;
+  };
+  // bf16 through LDS: the stage of the unit's last K block (the other one
+  // holds the next unit's first block) takes each wave's tile in two halves
+  // of 64 padded rows; 16 lanes store each 256-byte output row, non-temporal
+  auto store_out = [&](uint8_t* stg) {
+    uint8_t* slot = stg + wave * (W4M / 2) * k4EpiRowBytes;
+    const int64_t mw = m0 + wm * W4M, nw = n0 + wn * W4N;
+    const bool whole = mw + W4M <= M && nw + W4N <= N;
+    const int chunk = lane & 15;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      v4u v[W4M / 8];
+      if (h == 1) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): first half read back
 #pragma unroll
-      for (int u = 0; u < W4M / 8; ++u)
-        v[u] = lds_read16_a8(slot + (64 * h + 4 * u + (lane >> 4)) * k4EpiRowBytes + chunk * 16);
+      for (int i = 0; i < T4M / 2; ++i) {
 #pragma unroll
-      for (int u = 0; u < W4M / 8; ++u)
-        __builtin_nontemporal_store(v[u], reinterpret_cast<v4u*>(dst + (64 * h + 4 * u) * ldc));
+        for (int j = 0; j < T4N; ++j) {
+          const v4f& x = acc[(T4M / 2) * h + i][j];
+          *reinterpret_cast<uint2*>(slot + (16 * i + r16) * k4EpiRowBytes + (16 * j + 4 * g) * 2) =
+              make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's half is written
+      __builtin_amdgcn_wave_barrier();
+      if (whole) {
+        v4u o[W4M / 8];
+#pragma unroll
+        for (int u = 0; u < W4M / 8; ++u)
+          o[u] = lds_read16_a8(slot + (4 * u + (lane >> 4)) * k4EpiRowBytes + chunk * 16);
+        uint16_t* dst = C + (mw + (W4M / 2) * h + (lane >> 4)) * ldc + nw + chunk * 8;
+#pragma unroll
+        for (int u = 0; u < W4M / 8; ++u)
+          __builtin_nontemporal_store(o[u], reinterpret_cast<v4u*>(dst + 4 * u * ldc));
+      } else {
+#pragma unroll
+        for (int u = 0; u < W4M / 8; ++u) {
+          const int row = 4 * u + (lane >> 4);
+          const v4u x = lds_read16_a8(slot + row * k4EpiRowBytes + chunk * 16);
+          const int64_t m = mw + (W4M / 2) * h + row, n = nw + chunk * 8;
+          if (m >= M) continue;
+          uint16_t* dst = C + m * ldc + n;
+          if (n + 7 < N) {
+            __builtin_nontemporal_store(x, reinterpret_cast<v4u*>(dst));
+          } else if (n < N) {
+            const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+            for (int e = 0; e < 8 && n + e < N; ++e)
+              dst[e] = static_cast<uint16_t>((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+          }
+        }
+      }
     }
-    return;
-  }
+  };
+
+  // ---- the units ------------------------------------------------------------------
+  bool odd0 = false;  // this unit's first K block is in stage1
+  while (true) {
 #pragma unroll
-  for (int u = 0; u < W4M / 4; ++u) {
-    const int row = 4 * u + (lane >> 4);
-    const v4u v = lds_read16_a8(slot + row * k4EpiRowBytes + chunk * 16);
-    const int64_t m = mw + row, n = nw + chunk * 8;
-    if (m >= M) continue;
-    uint16_t* dst = C + m * ldc + n;
-    if (n + 7 < N) {
-      __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(dst));
-    } else if (n < N) {
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      for (int e = 0; e < 8 && n + e < N; ++e)
-        dst[e] = static_cast<uint16_t>((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+    for (int i = 0; i < T4M; ++i)
+#pragma unroll
+      for (int j = 0; j < T4N; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int kb = kb_begin; kb < kb_end; ++kb) {
+      const bool odd = (((kb - kb_begin) & 1) != 0) != odd0;
+      kblock(kb, odd ? stage1 : stage0, odd ? stage0 : stage1);
     }
+    // the copies issued during the last block (the next unit's first block)
+    // have landed: the barrier before the last column waited for them
+    const bool last_odd = (((kb_end - 1 - kb_begin) & 1) != 0) != odd0;
+    if (part != nullptr) store_partial();
+    else store_out(last_odd ? stage1 : stage0);
+    if (!has_next) break;
+    __syncthreads();  // every wave's staging reads are done before that stage is refilled
+    // switch to the next unit; its first block's fragments and scale words
+    // are already in registers
+    v += static_cast<int>(gridDim.x);
+    split = unit_tile(v, m0, n0, kb_begin, kb_end);
+    opa.rebase(A, lda, m0, M);
+    opb.rebase(B, ldb, n0, N);
+    set_packs();
+    odd0 = !last_odd;
+    peek_next();
   }
 }
 
@@ -992,15 +1072,15 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }  // namespace
 
 template <bool A_KM, bool B_KM, bool MX>
-static bfp8_status launch_layout(const GemmArgs& a, dim3 grid, int tm, int tn, float* part,
-                                 int64_t ldp, hipStream_t stream) {
+static bfp8_status launch_layout(const GemmArgs& a, dim3 grid, dim3 pgrid, int tm, int tn, int S,
+                                 float* part, int64_t ldp, hipStream_t stream) {
 // float32 scales: the 8-wave kernel; E8M0 scales: the 4-wave kernel
 #define BFP8_LAUNCH(MA, MB)                                                                   \
   do {                                                                                        \
     if constexpr (MX)                                                                         \
-      return launch(&gemm_mx4_kernel<A_KM, B_KM, MA, MB>, grid, dim3(k4Threads), stream, a.A, \
-                    a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K, tm, tn, part,   \
-                    ldp);                                                                     \
+      return launch(&gemm_mx4_kernel<A_KM, B_KM, MA, MB>, pgrid, dim3(k4Threads), stream,    \
+                    a.A, a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K, tm, tn, S, \
+                    part, ldp);                                                               \
     else                                                                                      \
       return launch(&gemm_kernel<A_KM, B_KM, MA, MB>, grid, dim3(kThreads), stream, a.A,      \
                     a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K, tm, tn, part,   \
@@ -1089,17 +1169,28 @@ bfp8_status launch_gemm(const GemmArgs& a, void* workspace, size_t workspace_byt
   float* part = S > 1 ? static_cast<float*>(workspace) : nullptr;
   const int64_t ldp = split_ldp(a.N);
   const dim3 grid(static_cast<unsigned>(nblk), static_cast<unsigned>(S));
+  // the power-of-two kernel is persistent: one workgroup per compute unit
+  // (its LDS stages fill a CU), a multiple of the 8 XCDs, each running every
+  // gridDim-th tile-and-split unit
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return BFP8_ERR_HIP;
+  const int64_t units = nblk * S;
+  const int64_t wgs = cus >= kXcds ? (cus / kXcds) * kXcds : cus;
+  const dim3 pgrid(static_cast<unsigned>(units < wgs ? units : wgs));
   const int tm = static_cast<int>(tiles_m), tn = static_cast<int>(tiles_n);
   bfp8_status st;
   if (a.mx) {
-    if (!a.a_kmajor && !a.b_kmajor) st = launch_layout<false, false, true>(a, grid, tm, tn, part, ldp, stream);
-    else if (!a.a_kmajor && a.b_kmajor) st = launch_layout<false, true, true>(a, grid, tm, tn, part, ldp, stream);
-    else if (a.a_kmajor && a.b_kmajor) st = launch_layout<true, true, true>(a, grid, tm, tn, part, ldp, stream);
+    if (!a.a_kmajor && !a.b_kmajor) st = launch_layout<false, false, true>(a, grid, pgrid, tm, tn, S, part, ldp, stream);
+    else if (!a.a_kmajor && a.b_kmajor) st = launch_layout<false, true, true>(a, grid, pgrid, tm, tn, S, part, ldp, stream);
+    else if (a.a_kmajor && a.b_kmajor) st = launch_layout<true, true, true>(a, grid, pgrid, tm, tn, S, part, ldp, stream);
     else return BFP8_ERR_LAYOUT;
   } else {
-    if (!a.a_kmajor && !a.b_kmajor) st = launch_layout<false, false, false>(a, grid, tm, tn, part, ldp, stream);
-    else if (!a.a_kmajor && a.b_kmajor) st = launch_layout<false, true, false>(a, grid, tm, tn, part, ldp, stream);
-    else if (a.a_kmajor && a.b_kmajor) st = launch_layout<true, true, false>(a, grid, tm, tn, part, ldp, stream);
+    if (!a.a_kmajor && !a.b_kmajor) st = launch_layout<false, false, false>(a, grid, pgrid, tm, tn, S, part, ldp, stream);
+    else if (!a.a_kmajor && a.b_kmajor) st = launch_layout<false, true, false>(a, grid, pgrid, tm, tn, S, part, ldp, stream);
+    else if (a.a_kmajor && a.b_kmajor) st = launch_layout<true, true, false>(a, grid, pgrid, tm, tn, S, part, ldp, stream);
     else return BFP8_ERR_LAYOUT;
   }
   if (st != BFP8_OK || S == 1) return st;
