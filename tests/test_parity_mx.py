@@ -215,6 +215,27 @@ def test_gemm_mx_integer_exact_bitwise(layout, ma, mb):
     assert bad.numel() == 0, (layout, ma, mb, bad[:5].tolist())
 
 
+@pytest.mark.parametrize("layout,ma,mb", [("NT", "act", "block"), ("NN", "act", "block"),
+                                          ("TN", "act", "act"), ("NT", "mx32", "mx32")])
+@pytest.mark.parametrize("K", [384, 512])
+def test_gemm_mx_persistent_tiles_bitwise(layout, ma, mb, K):
+    """More 256x256 tiles than workgroups (272 for 256 CUs), so a workgroup
+    runs a second tile whose first K block its first tile's last block
+    copied; the second tiles include the ragged last row and column of
+    tiles; an odd K-block count (384) starts the second tile in the other
+    LDS stage.  Integer-valued codes and power-of-two scales make every fp32
+    step exact, so the bf16 output must match the float64 product bit for
+    bit."""
+    rng = np.random.default_rng(K + len(layout) + 5 * len(ma))
+    M, N = 16 * 256 + 4, 15 * 256 + 200
+    qa, sa, qb, sb = integer_mx_operands(rng, layout, ma, mb, M, N, K)
+    R = ref_mx(layout, qa, sa, ma, qb, sb, mb)
+    exp = torch.from_numpy(R).float().to(torch.bfloat16)
+    got = run_mx(layout, qa, sa, ma, qb, sb, mb).cpu()
+    bad = (got.view(torch.int16) != exp.view(torch.int16)).nonzero()
+    assert bad.numel() == 0, (layout, ma, mb, K, bad[:5].tolist())
+
+
 @pytest.mark.parametrize("M,N,K,ma,mb", [(512, 256, 16384, "act", "act"),
                                          (2048, 2048, 16384, "mx32", "mx32")])
 def test_gemm_mx_split_k(M, N, K, ma, mb):
