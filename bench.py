@@ -280,6 +280,104 @@ def bf16_baseline(tensors, wl, steps, fp8_value):
             "fp8_over_bf16": round(fp8_value / value, 3)}
 
 
+def rel_errors(C, R):
+    """Errors of C against the reference R (float64 arrays of one shape):
+    normwise ||C - R||_F / ||R||_F, and the largest |C - R| over rms(R)."""
+    import numpy as np
+
+    d = np.asarray(C, np.float64) - np.asarray(R, np.float64)
+    rn = float(np.linalg.norm(R))
+    rms = rn / (R.size ** 0.5) if R.size else 0.0
+    return {"normwise": round(float(np.linalg.norm(d)) / rn, 6) if rn > 0 else 0.0,
+            "max_over_rms": round(float(np.abs(d).max()) / rms, 5) if rms > 0 else 0.0}
+
+
+def accuracy_report(tensors, wl, hp_main, rows=128, seed=0):
+    """Accuracy of the scale formats (the f2 / f4 comparison): every GEMM of
+    one pass, run with float32 scales (1x128 / 128x128 groups), power-of-two
+    scales on the same groups (mx128) and 1x32 power-of-two groups (mx32),
+    and the same product in bf16 through hipBLASLt, each against the float64
+    product of the unquantised inputs, on `rows` sampled output rows (tokens
+    for fprop and dgrad, output features for wgrad)."""
+    import numpy as np
+    import torch
+
+    from blockwise_fp8_gemm_bfp8_amd.hotpath import HotPath
+
+    g = np.random.default_rng(seed)
+    names = [L.name for L in wl.linears]
+    f64 = lambda t: t.double().cpu().numpy()
+    pick = {}
+    ref = {}
+    for L in wl.linears:
+        x, w, dy = tensors["x." + L.name], tensors["w." + L.name], tensors.get("dy." + L.name)
+        M = x.shape[0]
+        tr = np.sort(g.choice(M, min(rows, M), replace=False))
+        fr = np.sort(g.choice(w.shape[0], min(rows, w.shape[0]), replace=False))
+        pick[L.name] = (tr, fr)
+        ti = torch.from_numpy(tr).to(x.device)
+        fi = torch.from_numpy(fr).to(x.device)
+        wd = f64(w)
+        if "fprop" in wl.roles:
+            ref[(L.name, "fprop")] = f64(x.index_select(0, ti)) @ wd.T
+        if dy is not None and "dgrad" in wl.roles:
+            ref[(L.name, "dgrad")] = f64(dy.index_select(0, ti)) @ wd
+        if dy is not None and "wgrad" in wl.roles:
+            ref[(L.name, "wgrad")] = f64(dy.index_select(1, fi)).T @ f64(x)
+    key = {"fprop": "y", "dgrad": "dx", "wgrad": "dw"}
+    out = {k: {} for k in ref}
+    formats = ["fp32", "mx128", "mx32"] if set(wl.roles) == {"fprop", "dgrad", "wgrad"} else ["fp32"]
+    for sc in formats:
+        hp = hp_main if hp_main.scales == sc else HotPath(tensors, names, wl.roles, scales=sc)
+        hp.run()
+        torch.cuda.synchronize()
+        for L in hp.layers:
+            tr, fr = pick[L.name]
+            for role in ("fprop", "dgrad", "wgrad"):
+                if (L.name, role) not in ref:
+                    continue
+                idx = torch.from_numpy(fr if role == "wgrad" else tr).to(L.x.device)
+                got = f64(L.buf[key[role]].index_select(0, idx))
+                out[(L.name, role)][sc] = rel_errors(got, ref[(L.name, role)])
+        if hp is not hp_main:
+            del hp
+            torch.cuda.empty_cache()
+    # the same products in bf16 (contiguous 2-D operands only)
+    for L in wl.linears:
+        x, w, dy = tensors["x." + L.name], tensors["w." + L.name], tensors.get("dy." + L.name)
+        tr, fr = pick[L.name]
+        ti = torch.from_numpy(tr).to(x.device)
+        fi = torch.from_numpy(fr).to(x.device)
+        xb, wb = x.to(torch.bfloat16), w.to(torch.bfloat16)
+        prods = {}
+        if (L.name, "fprop") in ref:
+            prods["fprop"] = torch.matmul(xb.index_select(0, ti), wb.t().contiguous())
+        if (L.name, "dgrad") in ref:
+            prods["dgrad"] = torch.matmul(dy.to(torch.bfloat16).index_select(0, ti), wb)
+        if (L.name, "wgrad") in ref:
+            prods["wgrad"] = torch.matmul(dy.to(torch.bfloat16).index_select(1, fi).t().contiguous(), xb)
+        for role, c in prods.items():
+            out[(L.name, role)]["bf16"] = rel_errors(f64(c), ref[(L.name, role)])
+    per = [{"gemm": f"{n}.{r}", **v} for (n, r), v in out.items()]
+    summary = {}
+    for f in formats + ["bf16"]:
+        vals = [p[f]["normwise"] for p in per if f in p]
+        if vals:
+            summary[f] = {"normwise_mean": round(sum(vals) / len(vals), 6),
+                          "normwise_max": round(max(vals), 6)}
+    for p in per:
+        log(f"[bench] accuracy {p['gemm']:15s} " + "  ".join(
+            f"{f} {p[f]['normwise']:.2e}" for f in formats + ["bf16"] if f in p))
+    return {"reference": "float64 product of the unquantised inputs (the workload's bf16 / fp32 "
+                         "tensors), sampled output rows", "rows_sampled": rows,
+            "metric": "normwise = ||C - R||_F / ||R||_F; max_over_rms = max |C - R| / rms(R)",
+            "formats": {"fp32": "float32 scales amax/448, 1x128 act / 128x128 weight groups",
+                        "mx128": "power-of-two (E8M0) scales on the same groups",
+                        "mx32": "MXFP8: 1x32 power-of-two groups on every operand",
+                        "bf16": "unquantised bf16 operands, hipBLASLt"},
+            "summary": summary, "per_gemm": per}
+
+
 def family_roofline(hp, mean_us, kind, fields):
     """Roofline of one kernel family from the instrumented passes: the mean
     algorithmic work per launch over the mean launch time (each call's time
@@ -638,6 +736,9 @@ def main():
                     help="also time hipBLASLt's per-tensor FP8 GEMM on the pass's own codes")
     ap.add_argument("--quant-ceiling", action="store_true",
                     help="with the sweep: time a plain copy of each quantiser's input volume")
+    ap.add_argument("--accuracy", action="store_true",
+                    help="also compare every GEMM in float32, mx128 and mx32 scales and in bf16 "
+                         "against the float64 product of the unquantised inputs (sampled rows)")
     ap.add_argument("--graph", action="store_true",
                     help="also time K replays of the pass captured into one HIP graph")
     args = ap.parse_args()
@@ -861,6 +962,10 @@ def main():
     if args.scaled_mm_baseline:
         smm = scaled_mm_baseline(hp, min(args.reps, 20))
 
+    accuracy = None
+    if args.accuracy:
+        accuracy = accuracy_report(tensors, wl, hp)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
@@ -913,6 +1018,8 @@ def main():
     }
     if smm is not None:
         line["scaled_mm_baseline"] = smm
+    if accuracy is not None:
+        line["accuracy"] = accuracy
     if graph is not None:
         line["graph_replay"] = graph
     print(json.dumps(line), flush=True)

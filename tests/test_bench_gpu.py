@@ -1,7 +1,8 @@
 """bench.py end to end on the tiny workload: every optional leg runs and the
 JSON line carries the fields its contract names (the headline, both
 rooflines, the cold sweep with the copy ceiling, the vendor comparison, the
-graph replay, the clock window and the oracle baseline)."""
+graph replay, the clock window, the scale-format accuracy and the oracle
+baseline)."""
 import json
 import os
 import subprocess
@@ -17,7 +18,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def test_bench_line_on_tiny_workload_with_every_leg():
     cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny_256x512x384",
            "--steps", "3", "--warmup", "1", "--reps", "5", "--clock-window", "0.3",
-           "--scaled-mm-baseline", "--quant-ceiling", "--graph"]
+           "--scaled-mm-baseline", "--quant-ceiling", "--graph", "--accuracy"]
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=600, cwd=ROOT)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [ln for ln in r.stdout.splitlines() if ln.strip()]
@@ -47,3 +48,8 @@ def test_bench_line_on_tiny_workload_with_every_leg():
     assert d["cpu_baseline"]["kind"] == "oracle" and d["cpu_baseline"]["value"] > 0
     assert d["cpu_baseline"]["host"]["os_cpu_count"] >= 1
     assert d["bf16_baseline"]["value"] > 0
+    acc = d["accuracy"]
+    (p,) = acc["per_gemm"]
+    assert p["gemm"] == "tiny.fprop" and set(p) == {"gemm", "fp32", "bf16"}
+    # E4M3 keeps 3 mantissa bits: a few per cent normwise; bf16 inputs are exact
+    assert 1e-3 < p["fp32"]["normwise"] < 0.1 and p["bf16"]["normwise"] < 1e-2

@@ -99,3 +99,15 @@ def test_pmc_summary_derives_busy_clock_and_calibrated_bytes(tmp_path, monkeypat
     assert rec["fetch_factor"] == 2.0 and rec["write_factor"] == 1.0
     assert rec["hbm_bytes_per_launch"] == int((200 + 50) * 1024 * 1024)
     assert rec["gemm_source_sha256_16"] == bench.gemm_source_hash()
+
+
+def test_rel_errors_normwise_and_worst_element():
+    import numpy as np
+
+    R = np.array([[3.0, 4.0], [0.0, 0.0]])
+    assert bench.rel_errors(R, R) == {"normwise": 0.0, "max_over_rms": 0.0}
+    C = R.copy()
+    C[1, 1] = 0.5  # ||R||_F = 5, rms = 2.5
+    e = bench.rel_errors(C, R)
+    assert e["normwise"] == 0.1 and e["max_over_rms"] == 0.2
+    assert bench.rel_errors(C.astype(np.float32), R)["normwise"] == 0.1

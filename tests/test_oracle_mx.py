@@ -146,3 +146,28 @@ def test_mx32_quantised_product_close_to_unquantised():
         got = oracle.gemm_mx_ref("NT", qx, sx, mode, qw, sw, mode)
         errs[g] = oracle.normwise_error(got, exact)
     assert errs[32] < 0.06 and errs[128] < 0.06
+
+
+def test_pow2_dequantised_value_does_not_depend_on_the_group_in_normal_range():
+    """With a power-of-two scale 2**e the quantised value x / 2**e has x's
+    own significand, so while it stays in E4M3's normal range its code
+    decodes to x rounded to 4 significant bits whatever e is: groups of 32
+    and of 128 give the same dequantised element except where one of the two
+    scaled values is below the smallest normal, 2**-6.  This is why 1x32 and
+    1x128 power-of-two scales quantise realistic data almost identically."""
+    r = rng(15)
+    x = r.standard_t(3, (256, 1024)).astype(np.float32)
+    dec = {}
+    sub = {}
+    for g in (32, 128):
+        q, s = oracle.quantize_mx_act(x, g)
+        scale = np.repeat(oracle.e8m0_decode(s), g, axis=1)
+        dec[g] = oracle.e4m3_decode(q).astype(np.float64) * scale
+        sub[g] = np.abs(x.astype(np.float64)) / scale < 2.0 ** -6
+    normal = ~(sub[32] | sub[128])
+    assert np.array_equal(dec[32][normal], dec[128][normal])
+    # the significand rounding itself: |x - dec| <= 2**-4 |x| in the normal range
+    xn = x.astype(np.float64)[normal]
+    assert np.all(np.abs(dec[128][normal] - xn) <= 2.0 ** -4 * np.abs(xn))
+    # and the elements that differ are few and tiny against their group
+    assert (~normal).mean() < 0.01
