@@ -37,7 +37,9 @@
 // the scales ride in the matrix-core instruction
 // (v_mfma_scale_f32_16x16x128_f8f6f4), the accumulators are the MFMA's C
 // operand in the AGPR file, and no VALU promotion is needed, which lets 4
-// waves of 128 x 128 replace 8 waves of 64 x 128.  The instruction takes one
+// waves of 128 x 128 replace 8 waves of 64 x 128.  That kernel is also
+// persistent: one workgroup per CU walks its tiles, and each tile's last K
+// block copies the next tile's first.  The instruction takes one
 // scale byte per row and 32-deep K chunk: the register of lane group j
 // (lane 16j + r) scales row r's K values [32j, 32j + 32) -- which the
 // fragment layout below spreads over lane groups 2j mod 4 and 2j + 1 mod 4
