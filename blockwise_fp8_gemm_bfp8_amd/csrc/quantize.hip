@@ -282,7 +282,7 @@ __global__ __launch_bounds__(256) void quantize_weight_kernel(
                                  blockIdx.x, red);
 }
 
-constexpr int kWeightWgsPerCu = 4;  // two raw blocks per thread: ~130 VGPRs, 4 waves per SIMD
+constexpr int kWeightWgsPerCu = 4;  // at most (two raw blocks per thread: ~130 VGPRs)
 
 // Several weights in one launch: a flat block index walks the weights in
 // order (first_block holds each weight's first index, kMaxWeightJobs + 1
@@ -879,21 +879,29 @@ bfp8_status launch_quantize_weight_batch(const WeightBatch& b, bfp8_in_dtype dt,
                                          hipStream_t stream) {
   const int64_t blocks = b.first_block[b.n];
   if (blocks == 0) return BFP8_OK;
-  // kWeightWgsPerCu workgroups per CU (the register-limited residency of
-  // the two-block form), never more than there are blocks
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     return BFP8_ERR_HIP;
-  const int64_t wgs = std::min<int64_t>(blocks, static_cast<int64_t>(cus) * kWeightWgsPerCu);
-  const dim3 grid(static_cast<unsigned>(wgs)), block(256);
+  // As many workgroups as are resident at once (the kernel is persistent: a
+  // workgroup that has to wait for a slot would run its whole share late),
+  // at most kWeightWgsPerCu per CU and never more than there are blocks.
+  // Residency is register-limited and differs between instantiations.
+  auto run = [&](auto kernel) -> bfp8_status {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess)
+      return BFP8_ERR_HIP;
+    per_cu = std::max(1, std::min(per_cu, kWeightWgsPerCu));
+    const int64_t wgs = std::min<int64_t>(blocks, static_cast<int64_t>(cus) * per_cu);
+    return launch(kernel, dim3(static_cast<unsigned>(wgs)), dim3(256), stream, b);
+  };
   if (dt == BFP8_IN_BF16) {
-    if (rule == 0) return launch(&quantize_weight_batch_kernel<uint16_t, 0>, grid, block, stream, b);
-    return launch(&quantize_weight_batch_kernel<uint16_t, 1>, grid, block, stream, b);
+    if (rule == 0) return run(&quantize_weight_batch_kernel<uint16_t, 0>);
+    return run(&quantize_weight_batch_kernel<uint16_t, 1>);
   }
-  if (rule == 0) return launch(&quantize_weight_batch_kernel<float, 0>, grid, block, stream, b);
-  return launch(&quantize_weight_batch_kernel<float, 1>, grid, block, stream, b);
+  if (rule == 0) return run(&quantize_weight_batch_kernel<float, 0>);
+  return run(&quantize_weight_batch_kernel<float, 1>);
 }
 
 bfp8_status launch_quantize_weight(const void* w, bfp8_in_dtype dt, int64_t rows, int64_t cols,
