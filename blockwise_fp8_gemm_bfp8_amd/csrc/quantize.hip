@@ -18,6 +18,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "common.h"
 
@@ -875,6 +876,22 @@ bfp8_status launch_quantize_act_dual(const void* x, bfp8_in_dtype dt, int64_t ro
   return status;
 }
 
+// Workgroups of quantize_weight_batch_kernel<T, RULE> resident per CU (at
+// most kWeightWgsPerCu), queried once: every GPU the library runs on is the
+// same gfx950 part.
+template <typename T, int RULE>
+static bfp8_status weight_batch_residency(int& per_cu) {
+  static std::atomic<int> cached{0};
+  per_cu = cached.load(std::memory_order_relaxed);
+  if (per_cu > 0) return BFP8_OK;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quantize_weight_batch_kernel<T, RULE>,
+                                                   256, 0) != hipSuccess)
+    return BFP8_ERR_HIP;
+  per_cu = std::max(1, std::min(per_cu, kWeightWgsPerCu));
+  cached.store(per_cu, std::memory_order_relaxed);
+  return BFP8_OK;
+}
+
 bfp8_status launch_quantize_weight_batch(const WeightBatch& b, bfp8_in_dtype dt, int rule,
                                          hipStream_t stream) {
   const int64_t blocks = b.first_block[b.n];
@@ -888,20 +905,23 @@ bfp8_status launch_quantize_weight_batch(const WeightBatch& b, bfp8_in_dtype dt,
   // workgroup that has to wait for a slot would run its whole share late),
   // at most kWeightWgsPerCu per CU and never more than there are blocks.
   // Residency is register-limited and differs between instantiations.
-  auto run = [&](auto kernel) -> bfp8_status {
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess)
-      return BFP8_ERR_HIP;
-    per_cu = std::max(1, std::min(per_cu, kWeightWgsPerCu));
-    const int64_t wgs = std::min<int64_t>(blocks, static_cast<int64_t>(cus) * per_cu);
-    return launch(kernel, dim3(static_cast<unsigned>(wgs)), dim3(256), stream, b);
-  };
+  int per_cu = 0;
+  bfp8_status st = BFP8_OK;
+  if (dt == BFP8_IN_BF16)
+    st = rule == 0 ? weight_batch_residency<uint16_t, 0>(per_cu)
+                   : weight_batch_residency<uint16_t, 1>(per_cu);
+  else
+    st = rule == 0 ? weight_batch_residency<float, 0>(per_cu)
+                   : weight_batch_residency<float, 1>(per_cu);
+  if (st != BFP8_OK) return st;
+  const int64_t wgs = std::min<int64_t>(blocks, static_cast<int64_t>(cus) * per_cu);
+  const dim3 grid(static_cast<unsigned>(wgs)), block(256);
   if (dt == BFP8_IN_BF16) {
-    if (rule == 0) return run(&quantize_weight_batch_kernel<uint16_t, 0>);
-    return run(&quantize_weight_batch_kernel<uint16_t, 1>);
+    if (rule == 0) return launch(&quantize_weight_batch_kernel<uint16_t, 0>, grid, block, stream, b);
+    return launch(&quantize_weight_batch_kernel<uint16_t, 1>, grid, block, stream, b);
   }
-  if (rule == 0) return run(&quantize_weight_batch_kernel<float, 0>);
-  return run(&quantize_weight_batch_kernel<float, 1>);
+  if (rule == 0) return launch(&quantize_weight_batch_kernel<float, 0>, grid, block, stream, b);
+  return launch(&quantize_weight_batch_kernel<float, 1>, grid, block, stream, b);
 }
 
 bfp8_status launch_quantize_weight(const void* w, bfp8_in_dtype dt, int64_t rows, int64_t cols,
