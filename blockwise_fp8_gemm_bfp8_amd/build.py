@@ -44,15 +44,21 @@ def build(verbose: bool = False) -> str:
     """Compile every HIP/C++ source and link libbfp8.so; returns its path."""
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="bfp8_build_") as tmp:
-        objs = []
+        objs, cmds = [], []
         for src in SOURCES:
             obj = os.path.join(tmp, src.replace(".", "_") + ".o")
             lang = ["-x", "hip"]
-            cmd = [cc, *compile_flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmds.append([cc, *compile_flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+            objs.append(obj)
+        # the sources compile independently: one hipcc process each, at once
+        procs = []
+        for cmd in cmds:
             if verbose:
                 print(" ".join(cmd), flush=True)
-            subprocess.run(cmd, check=True)
-            objs.append(obj)
+            procs.append((cmd, subprocess.Popen(cmd)))
+        failed = [cmd for cmd, pr in procs if pr.wait() != 0]
+        if failed:
+            raise subprocess.CalledProcessError(1, failed[0])
         tmp_lib = os.path.join(tmp, "libbfp8.so")
         cmd = [cc, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp_lib]
         if verbose:

@@ -24,12 +24,16 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 constexpr int64_t kMaxGridY = 65535;
 
 // Workspace: fp32 split-K partials for shapes whose output tiles under-fill
-// the chip (zero for all other shapes).  The GEMM runs unsplit when the
-// caller passes less.
-inline size_t gemm_workspace(bfp8_layout, bfp8_scale_mode, bfp8_scale_mode, int64_t M, int64_t N,
-                             int64_t K) {
+// the chip (zero for all other shapes), enough for whichever of bfp8_gemm
+// and bfp8_gemm_mx takes these modes (1x32 groups: only bfp8_gemm_mx).  The
+// GEMM runs unsplit when the caller passes less.
+inline size_t gemm_workspace(bfp8_layout, bfp8_scale_mode modeA, bfp8_scale_mode modeB, int64_t M,
+                             int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
-  return gemm_split_workspace(M, N, K);
+  const size_t mx = gemm_split_workspace(M, N, K, true);
+  if (modeA == BFP8_SCALE_1x32 || modeB == BFP8_SCALE_1x32) return mx;
+  const size_t f32 = gemm_split_workspace(M, N, K, false);
+  return f32 > mx ? f32 : mx;
 }
 
 // Largest leading dimension (bytes) the GEMM addresses with 32-bit offsets.

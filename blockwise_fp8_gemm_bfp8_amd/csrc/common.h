@@ -223,8 +223,18 @@ bfp8_status launch_gemm(const GemmArgs& a, void* workspace, size_t workspace_byt
 // bfp8_gemm with its split-K partials in the library's static device array:
 // BFP8_ERR_WORKSPACE (before any HIP call) if they would not fit.
 bfp8_status launch_gemm_static_scratch(const GemmArgs& a, hipStream_t stream);
-int gemm_splits(int64_t M, int64_t N, int64_t K);
-size_t gemm_split_workspace(int64_t M, int64_t N, int64_t K);
+// Split-K plan of an M x N x K GEMM: logical tiles [0, full) run unsplit,
+// the others in `splits` ranges of K blocks (splits == 1: nothing is split,
+// full == tiles); the split tiles cover output rows [row0, M).
+struct GemmPlan {
+  int64_t full;
+  int splits;
+  int64_t row0;
+};
+// mx: the plan of the power-of-two (E8M0) kernel, which splits all tiles alike.
+GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, bool mx);
+// fp32 partials of that plan: splits x (M - row0) rows x ceil4(N) floats
+size_t gemm_split_workspace(int64_t M, int64_t N, int64_t K, bool mx);
 bfp8_status launch_fill_bf16_zero(uint16_t* C, int64_t M, int64_t N, int64_t ldc,
                                   hipStream_t stream);
 

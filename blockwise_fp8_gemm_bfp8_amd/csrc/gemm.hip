@@ -76,14 +76,44 @@ typedef __attribute__((address_space(3))) v2i lds_v2i;
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
-// Map the hardware block id to a (tile_m, tile_n) pair: first undo the
-// round-robin XCD dealing so each XCD owns a contiguous range of logical
-// tiles, then walk tiles in column-major groups of kGroupM rows.
-__device__ __forceinline__ void tile_coords(int bid, int nblk, int tiles_m, int tiles_n, int& tm,
-                                            int& tn) {
-  const int q = nblk / kXcds, r = nblk % kXcds;
-  const int xcd = bid % kXcds, local = bid / kXcds;
-  const int logical = xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+// Work units of one launch.  Logical tiles [0, full) run over all of K and
+// store bf16; every remaining tile is split into `splits` contiguous ranges
+// of K blocks whose fp32 sums go to part[split][row - row0][ldp] (row0 =
+// 256 trow0, the first row of the split tiles; ldp = N rounded up to 4), summed in
+// split order by splitk_reduce_kernel.  Unit ids: [0, full) the whole
+// tiles, then one segment of (tiles - full) ids per split.  With full a
+// whole number of waves of workgroups, the split units are only the tiles
+// that would leave the last wave under-filled.  full is a multiple of the
+// tile walk's row groups, so the split tiles are whole rows of tiles.
+struct UnitPlan {
+  int tiles_m, tiles_n;
+  int full;     // whole tiles (logical order); the rest are split
+  int splits;   // K ranges per split tile (1: nothing is split), at most 8
+  int piece;    // K blocks per range (splits * piece = K / 128)
+  int trow0;    // first row of split tiles: full / tiles_n
+  float* part;  // fp32 partials of the split tiles
+};
+
+// Offset (elements) of output row m in split `sp`'s partials.
+__device__ __forceinline__ int64_t partial_row(const UnitPlan& p, int sp, int64_t m, int64_t M,
+                                               int64_t ldp) {
+  const int64_t row0 = static_cast<int64_t>(p.trow0) * BM;
+  return (sp * (M - row0) + (m - row0)) * ldp;
+}
+
+// Logical index of the j-th id of a segment of n consecutive block ids:
+// the hardware deals consecutive ids to the 8 XCDs round robin, so ids j
+// with the same j % 8 run on one XCD; this gives each of those classes a
+// contiguous range of logical indices.
+__device__ __forceinline__ int undeal(int j, int n) {
+  const int q = n / kXcds, r = n % kXcds;
+  const int rank = j % kXcds, local = j / kXcds;
+  return rank < r ? rank * (q + 1) + local : r * (q + 1) + (rank - r) * q + local;
+}
+
+// Tile of a logical index: tiles are walked in column-major groups of
+// kGroupM rows, so concurrent tiles of an XCD share A rows and B columns.
+__device__ __forceinline__ void tile_walk(int logical, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int per_group = kGroupM * tiles_n;
   const int group = logical / per_group;
   const int first_m = group * kGroupM;
@@ -91,6 +121,34 @@ __device__ __forceinline__ void tile_coords(int bid, int nblk, int tiles_m, int 
   const int in_group = logical - group * per_group;
   tm = first_m + in_group % gsize;
   tn = in_group / gsize;
+}
+
+// Tile and K-block range of unit u; returns its split (-1: a whole tile).
+__device__ __forceinline__ int plan_unit(const UnitPlan& p, int u, int KB, int& tm, int& tn,
+                                         int& kb0, int& kb1) {
+  int logical, sp;
+  if (u < p.full) {
+    logical = undeal(u, p.full);
+    sp = -1;
+    kb0 = 0;
+    kb1 = KB;
+  } else {
+    // split s is the id segment [full + s * rest, full + (s + 1) * rest)
+    const int rest = p.tiles_m * p.tiles_n - p.full;
+    int w = u - p.full;
+    sp = 0;
+#pragma unroll
+    for (int s = 1; s < 8; ++s)  // no integer division: at most 8 splits
+      if (w >= rest) {
+        w -= rest;
+        ++sp;
+      }
+    logical = p.full + undeal(w, rest);
+    kb0 = sp * p.piece;
+    kb1 = kb0 + p.piece;
+  }
+  tile_walk(logical, p.tiles_m, p.tiles_n, tm, tn);
+  return sp;
 }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -327,8 +385,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(2, 2))) void
 gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__ sA_,
             const uint8_t* __restrict__ B, int64_t ldb, const void* __restrict__ sB_,
-            uint16_t* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K, int tiles_m,
-            int tiles_n, float* __restrict__ part, int64_t ldp) {
+            uint16_t* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+            const UnitPlan plan) {
   const float* __restrict__ sA = static_cast<const float*>(sA_);
   const float* __restrict__ sB = static_cast<const float*>(sB_);
   // MODE 3: 1x128 groups like MODE 0, with the scale tensor stored K-block
@@ -346,18 +404,15 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
   const int wn = wave / kWavesM;
   const int g = lane >> 4, r16 = lane & 15;
 
-  int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = static_cast<int64_t>(tm) * BM;
-  const int64_t n0 = static_cast<int64_t>(tn) * BN;
   const int64_t KB = K / BK;
   const int64_t MBk = (M + 127) / 128, NBk = (N + 127) / 128;
-  // split-K: blockIdx.y selects a contiguous range of K blocks; with more
-  // than one split the fp32 tile goes to part[split] and a second kernel
-  // sums the splits in order.
-  const int splits = gridDim.y, split = blockIdx.y;  // 32-bit: KB * splits < 2^31
-  const int kb_begin = static_cast<int>((split * static_cast<int>(KB)) / splits);
-  const int kb_end = static_cast<int>(((split + 1) * static_cast<int>(KB)) / splits);
+  // this workgroup's unit: a tile and a range of its K blocks; a split
+  // unit's fp32 sum goes to part[split] and a second kernel sums the splits
+  // in order
+  int tm, tn, kb_begin, kb_end;
+  const int split = plan_unit(plan, blockIdx.x, static_cast<int>(KB), tm, tn, kb_begin, kb_end);
+  const int64_t m0 = static_cast<int64_t>(tm) * BM;
+  const int64_t n0 = static_cast<int64_t>(tn) * BN;
 
   Operand<A_KM> opa;
   Operand<B_KM> opb;
@@ -585,11 +640,12 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
   // the copies issued during the last block must land before the stages
   // are reused for the output
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  if (part != nullptr) {
+  if (split >= 0) {
     // split-K partial: 4 consecutive fp32 columns per lane, 16-byte stores
-    float* pbase = part + static_cast<int64_t>(split) * M * ldp;
+    const int64_t ldp = (N + 3) & ~int64_t(3);
+    float* pbase = plan.part + partial_row(plan, split, m0, M, ldp);
     if (m0 + wm * WM + WM <= M && n0 + wn * WN + WN <= N) {
-      float* dst = pbase + (m0 + wm * WM + r16) * ldp + n0 + wn * WN + 4 * g;
+      float* dst = pbase + (wm * WM + r16) * ldp + n0 + wn * WN + 4 * g;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -605,7 +661,7 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
       for (int j = 0; j < TN; ++j) {
         const int64_t n = n0 + wn * WN + 16 * j + 4 * g;
         if (n < N) {
-          float* dst = pbase + m * ldp + n;
+          float* dst = pbase + (m - m0) * ldp + n;
 #pragma unroll
           for (int r = 0; r < 4; ++r) dst[r] = acc[i][j][r];
         }
@@ -708,7 +764,9 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
   const int64_t MBk = (M + 127) / 128, NBk = (N + 127) / 128;
   // Persistent: this workgroup runs the work units blockIdx.x, blockIdx.x +
   // gridDim.x, ... (a unit: one 256x256 output tile and one split-K range of
-  // its K blocks; units tiles .. 2 tiles - 1 are split 1, and so on).  The
+  // its K blocks; units tiles .. 2 tiles - 1 are split 1, and so on: every
+  // tile is split alike, so the unit decode stays a few scalar operations
+  // in a kernel that uses its whole register file).  The
   // last K block of a unit copies the next unit's first block, and the
   // output of a unit is stored while those copies land, so neither the
   // copy latency of a tile's first block nor a new workgroup's start sits
@@ -719,7 +777,7 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
   auto unit_tile = [&](int v, int64_t& um0, int64_t& un0, int& ukb0, int& ukb1) {
     const int sp = v / tiles;
     int tm, tn;
-    tile_coords(v - sp * tiles, tiles, tiles_m, tiles_n, tm, tn);
+    tile_walk(undeal(v - sp * tiles, tiles), tiles_m, tiles_n, tm, tn);
     um0 = static_cast<int64_t>(tm) * BM;
     un0 = static_cast<int64_t>(tn) * BN;
     ukb0 = static_cast<int>((sp * static_cast<int>(KB)) / splits);
@@ -1046,19 +1104,22 @@ __global__ __launch_bounds__(256) void fill_zero_bf16_kernel(uint16_t* __restric
   C[r * ldc + c] = 0;
 }
 
-// Sum of the split-K partials in split order, rounded to bf16 (RNE).
+// Sum of the split-K partials in split order, rounded to bf16 (RNE), for
+// output rows [row0, M) (the rows of the split tiles; partial row r holds
+// output row row0 + r).
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
                                                             int64_t ldp, int64_t splits,
                                                             uint16_t* __restrict__ C, int64_t ldc,
-                                                            int64_t M, int64_t N) {
-  const int64_t quads = (N + 3) / 4;
+                                                            int64_t row0, int64_t M, int64_t N) {
+  const int64_t quads = (N + 3) / 4, rows = M - row0;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= M * quads) return;
-  const int64_t m = i / quads, n = (i - m * quads) * 4;
-  const float* p = part + m * ldp + n;
+  if (i >= rows * quads) return;
+  const int64_t r = i / quads, n = (i - r * quads) * 4;
+  const int64_t m = row0 + r;
+  const float* p = part + r * ldp + n;
   v4f acc = *reinterpret_cast<const v4f*>(p);
   for (int64_t s = 1; s < splits; ++s) {
-    const v4f v = *reinterpret_cast<const v4f*>(p + s * M * ldp);
+    const v4f v = *reinterpret_cast<const v4f*>(p + s * rows * ldp);
     acc[0] += v[0]; acc[1] += v[1]; acc[2] += v[2]; acc[3] += v[3];
   }
   const uint32_t w0 = pack_bf16x2(acc[0], acc[1]), w1 = pack_bf16x2(acc[2], acc[3]);
@@ -1074,19 +1135,19 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }  // namespace
 
 template <bool A_KM, bool B_KM, bool MX>
-static bfp8_status launch_layout(const GemmArgs& a, dim3 grid, dim3 pgrid, int tm, int tn, int S,
-                                 float* part, int64_t ldp, hipStream_t stream) {
+static bfp8_status launch_layout(const GemmArgs& a, dim3 grid, dim3 pgrid, const UnitPlan& plan,
+                                 hipStream_t stream) {
 // float32 scales: the 8-wave kernel; E8M0 scales: the 4-wave kernel
 #define BFP8_LAUNCH(MA, MB)                                                                   \
   do {                                                                                        \
     if constexpr (MX)                                                                         \
       return launch(&gemm_mx4_kernel<A_KM, B_KM, MA, MB>, pgrid, dim3(k4Threads), stream,    \
-                    a.A, a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K, tm, tn, S, \
-                    part, ldp);                                                               \
+                    a.A, a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K,            \
+                    plan.tiles_m, plan.tiles_n, plan.splits, plan.part,                       \
+                    (a.N + 3) & ~int64_t(3));                                                 \
     else                                                                                      \
       return launch(&gemm_kernel<A_KM, B_KM, MA, MB>, grid, dim3(kThreads), stream, a.A,      \
-                    a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K, tm, tn, part,   \
-                    ldp);                                                                     \
+                    a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K, plan);          \
   } while (0)
   // mode 3 (K-block-major act scales) is mode 0 for a K-major operand
   const int ma = (A_KM && a.modeA == 3) ? 0 : a.modeA;
@@ -1121,42 +1182,69 @@ static bfp8_status launch_layout(const GemmArgs& a, dim3 grid, dim3 pgrid, int t
   return BFP8_ERR_SCALE_MODE;
 }
 
-// Split-K plan for shapes whose 256x256 tiles under-fill the chip: choose
-// the split count that minimises (waves of tiles) x (K blocks per split)
-// plus the cost of moving the fp32 partials.  Splits keep >= 8 K blocks.
+// Split-K plan for shapes whose 256x256 tiles under-fill the chip.  The
+// candidates: every tile split evenly into S ranges of K blocks, or whole
+// waves of tiles run unsplit and only the tiles left over for a last,
+// partial wave split into S ranges (so their units fill that wave).  Each is
+// priced by a model of one workgroup per CU -- a unit costs a fixed
+// prologue/epilogue plus a per-K-block time, units run in waves of 256 --
+// plus the fp32 partials' round trip through HBM and the reduction's launch;
+// the cheapest wins if it beats the unsplit plan by 5 %.  Splits keep >= 8
+// K blocks.  The plan depends only on the shape, so the workspace query
+// and every launch agree.
 static int64_t split_ldp(int64_t N) { return (N + 3) & ~int64_t(3); }
 
-int gemm_splits(int64_t M, int64_t N, int64_t K) {
-  constexpr double kCUs = 256.0;       // MI355X compute units
-  constexpr double kBlockUs = 2.4;     // one 256x256x128 step of one tile, measured order
+GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, bool mx) {
+  constexpr int64_t kCUs = 256;      // MI355X compute units: workgroups per wave
+  constexpr double kBlockUs = 1.6;   // one 256x256x128 K block of one tile, measured order
+  constexpr double kUnitUs = 5.0;    // a unit's prologue and epilogue
   constexpr double kBytesPerUs = 4.0e6;
-  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  constexpr double kReduceUs = 4.0;  // the reduction kernel's launch
+  const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int64_t tiles = tiles_m * tiles_n;
   const int64_t KB = K / BK;
-  if (tiles == 0 || KB == 0) return 1;
-  auto cost = [&](int64_t S) {
-    const double waves = static_cast<double>((tiles * S + 255) / 256);
-    double t = waves * (static_cast<double>(KB) / S) * kBlockUs;
-    if (S > 1)
-      t += (static_cast<double>(S) * M * split_ldp(N) * 8.0 + M * N * 2.0) / kBytesPerUs + 4.0;
-    return t;
+  GemmPlan plan{tiles, 1, 0};
+  if (tiles == 0 || KB == 0) return plan;
+  auto waves = [&](int64_t units) { return static_cast<double>((units + kCUs - 1) / kCUs); };
+  auto unit_us = [&](int64_t kblocks) { return kblocks * kBlockUs + kUnitUs; };
+  auto partial_us = [&](int64_t S, int64_t rows) {
+    return (static_cast<double>(S) * rows * split_ldp(N) * 8.0 + rows * N * 2.0) / kBytesPerUs +
+           kReduceUs;
   };
-  (void)kCUs;
-  int best = 1;
-  double best_t = cost(1);
-  for (int S : {2, 3, 4, 6, 8}) {
+  const double unsplit = waves(tiles) * unit_us(KB);
+  double best_t = unsplit * 0.95;
+  // whole waves first: a multiple of the CU count that is also a multiple of
+  // the tile walk's row groups, so the split tiles are whole rows of tiles
+  const int64_t full = (tiles / kCUs) * kCUs;
+  // (the persistent power-of-two kernel splits every tile alike)
+  const bool hybrid = !mx && full > 0 && full < tiles && full % (kGroupM * tiles_n) == 0;
+  for (int64_t S : {2, 3, 4, 6, 8}) {
     if (KB / S < 8) break;
-    const double t = cost(S);
-    if (t < best_t * 0.95) {
-      best_t = t;
-      best = S;
+    if (KB % S != 0) continue;  // equal ranges of K blocks
+    if (tiles * S >= (int64_t(1) << 30)) break;
+    const int64_t piece = KB / S;
+    const double even = waves(tiles * S) * unit_us(piece) + partial_us(S, M);
+    if (even < best_t) {
+      best_t = even;
+      plan = GemmPlan{0, static_cast<int>(S), 0};
+    }
+    if (hybrid) {
+      const int64_t row0 = (full / tiles_n) * BM;
+      const double t = waves(full) * unit_us(KB) + waves((tiles - full) * S) * unit_us(piece) +
+                       partial_us(S, M - row0);
+      if (t < best_t) {
+        best_t = t;
+        plan = GemmPlan{full, static_cast<int>(S), row0};
+      }
     }
   }
-  return best;
+  return plan;
 }
 
-size_t gemm_split_workspace(int64_t M, int64_t N, int64_t K) {
-  const int S = gemm_splits(M, N, K);
-  return S > 1 ? static_cast<size_t>(S) * M * split_ldp(N) * sizeof(float) : 0;
+size_t gemm_split_workspace(int64_t M, int64_t N, int64_t K, bool mx) {
+  const GemmPlan p = gemm_plan(M, N, K, mx);
+  return p.splits > 1 ? static_cast<size_t>(p.splits) * (M - p.row0) * split_ldp(N) * sizeof(float)
+                      : 0;
 }
 
 bfp8_status launch_gemm(const GemmArgs& a, void* workspace, size_t workspace_bytes,
@@ -1165,40 +1253,48 @@ bfp8_status launch_gemm(const GemmArgs& a, void* workspace, size_t workspace_byt
   const int64_t tiles_n = (a.N + BN - 1) / BN;
   const int64_t nblk = tiles_m * tiles_n;
   if (nblk == 0) return BFP8_OK;
-  int S = gemm_splits(a.M, a.N, a.K);
-  if (S > 1 && (workspace == nullptr || workspace_bytes < gemm_split_workspace(a.M, a.N, a.K)))
-    S = 1;  // no room for partials: run unsplit
-  float* part = S > 1 ? static_cast<float*>(workspace) : nullptr;
+  GemmPlan gp = gemm_plan(a.M, a.N, a.K, a.mx);
+  if (gp.splits > 1 &&
+      (workspace == nullptr || workspace_bytes < gemm_split_workspace(a.M, a.N, a.K, a.mx)))
+    gp = GemmPlan{nblk, 1, 0};  // no room for partials: run unsplit
+  UnitPlan plan;
+  plan.tiles_m = static_cast<int>(tiles_m);
+  plan.tiles_n = static_cast<int>(tiles_n);
+  plan.full = static_cast<int>(gp.full);
+  plan.splits = gp.splits;
+  plan.piece = static_cast<int>(a.K / BK / gp.splits);
+  plan.trow0 = static_cast<int>(gp.row0 / BM);
+  plan.part = gp.splits > 1 ? static_cast<float*>(workspace) : nullptr;
   const int64_t ldp = split_ldp(a.N);
-  const dim3 grid(static_cast<unsigned>(nblk), static_cast<unsigned>(S));
+  const int64_t units = gp.full + (nblk - gp.full) * gp.splits;
+  const dim3 grid(static_cast<unsigned>(units));
   // the power-of-two kernel is persistent: one workgroup per compute unit
   // (its LDS stages fill a CU), a multiple of the 8 XCDs, each running every
-  // gridDim-th tile-and-split unit
+  // gridDim-th unit
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     return BFP8_ERR_HIP;
-  const int64_t units = nblk * S;
   const int64_t wgs = cus >= kXcds ? (cus / kXcds) * kXcds : cus;
   const dim3 pgrid(static_cast<unsigned>(units < wgs ? units : wgs));
-  const int tm = static_cast<int>(tiles_m), tn = static_cast<int>(tiles_n);
   bfp8_status st;
   if (a.mx) {
-    if (!a.a_kmajor && !a.b_kmajor) st = launch_layout<false, false, true>(a, grid, pgrid, tm, tn, S, part, ldp, stream);
-    else if (!a.a_kmajor && a.b_kmajor) st = launch_layout<false, true, true>(a, grid, pgrid, tm, tn, S, part, ldp, stream);
-    else if (a.a_kmajor && a.b_kmajor) st = launch_layout<true, true, true>(a, grid, pgrid, tm, tn, S, part, ldp, stream);
+    if (!a.a_kmajor && !a.b_kmajor) st = launch_layout<false, false, true>(a, grid, pgrid, plan, stream);
+    else if (!a.a_kmajor && a.b_kmajor) st = launch_layout<false, true, true>(a, grid, pgrid, plan, stream);
+    else if (a.a_kmajor && a.b_kmajor) st = launch_layout<true, true, true>(a, grid, pgrid, plan, stream);
     else return BFP8_ERR_LAYOUT;
   } else {
-    if (!a.a_kmajor && !a.b_kmajor) st = launch_layout<false, false, false>(a, grid, pgrid, tm, tn, S, part, ldp, stream);
-    else if (!a.a_kmajor && a.b_kmajor) st = launch_layout<false, true, false>(a, grid, pgrid, tm, tn, S, part, ldp, stream);
-    else if (a.a_kmajor && a.b_kmajor) st = launch_layout<true, true, false>(a, grid, pgrid, tm, tn, S, part, ldp, stream);
+    if (!a.a_kmajor && !a.b_kmajor) st = launch_layout<false, false, false>(a, grid, pgrid, plan, stream);
+    else if (!a.a_kmajor && a.b_kmajor) st = launch_layout<false, true, false>(a, grid, pgrid, plan, stream);
+    else if (a.a_kmajor && a.b_kmajor) st = launch_layout<true, true, false>(a, grid, pgrid, plan, stream);
     else return BFP8_ERR_LAYOUT;
   }
-  if (st != BFP8_OK || S == 1) return st;
-  const int64_t n = a.M * ((a.N + 3) / 4);
+  if (st != BFP8_OK || gp.splits == 1) return st;
+  const int64_t n = (a.M - gp.row0) * ((a.N + 3) / 4);
   return launch(&splitk_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
-                stream, part, ldp, static_cast<int64_t>(S), a.C, a.ldc, a.M, a.N);
+                stream, plan.part, ldp, static_cast<int64_t>(gp.splits), a.C, a.ldc, gp.row0,
+                a.M, a.N);
 }
 
 // ---- split-K partials in a static device array -------------------------
@@ -1235,7 +1331,7 @@ bfp8_status scratch_address(void** out) {
 }  // namespace
 
 bfp8_status launch_gemm_static_scratch(const GemmArgs& a, hipStream_t stream) {
-  const size_t need = gemm_split_workspace(a.M, a.N, a.K);
+  const size_t need = gemm_split_workspace(a.M, a.N, a.K, a.mx);
   if (need > static_cast<size_t>(BFP8_STATIC_SCRATCH_BYTES)) return BFP8_ERR_WORKSPACE;
   void* ws = nullptr;
   if (need > 0) {

@@ -338,8 +338,8 @@ bfp8_status bfp8_gemm_mx(bfp8_layout layout, int64_t M, int64_t N, int64_t K, co
  * process ends).  Results are bit-identical to bfp8_gemm given the workspace
  * bfp8_gemm_workspace_bytes asks for.  Arguments, layouts and errors as for
  * bfp8_gemm; in addition BFP8_ERR_WORKSPACE, before any HIP call and with
- * nothing launched, when the problem's split-K partials
- * (bfp8_gemm_workspace_bytes) exceed BFP8_STATIC_SCRATCH_BYTES -- such a
+ * nothing launched, when bfp8_gemm's split-K partials for the problem
+ * (at most bfp8_gemm_workspace_bytes) exceed BFP8_STATIC_SCRATCH_BYTES -- such a
  * problem can run allocation-free through bfp8_gemm with a NULL workspace
  * (unsplit).  Allocates nothing and never synchronises.  The array's device
  * address is looked up on the calling thread's current device, which must be
@@ -354,9 +354,12 @@ bfp8_status bfp8_gemm_static_scratch(bfp8_layout layout, int64_t M, int64_t N, i
                                      const float* sB, bfp8_scale_mode modeB, void* C, int64_t ldc,
                                      hipStream_t stream);
 
-/* Workspace bytes that let bfp8_gemm (or bfp8_gemm_mx) use its split-K plan
- * for this problem (0 when the problem runs unsplit).  Returns (size_t)-1 for
- * an invalid layout, scale mode or size. */
+/* Workspace bytes that let bfp8_gemm and bfp8_gemm_mx use their split-K
+ * plans for this problem (0 when both run unsplit; the larger of the two
+ * when the plans differ: bfp8_gemm may run whole waves of tiles unsplit and
+ * split only the tiles of a last, partial wave, while the persistent
+ * bfp8_gemm_mx kernel splits every tile alike).  Returns (size_t)-1 for an
+ * invalid layout, scale mode or size. */
 size_t bfp8_gemm_workspace_bytes(bfp8_layout layout, bfp8_scale_mode modeA,
                                  bfp8_scale_mode modeB, int64_t M, int64_t N, int64_t K);
 

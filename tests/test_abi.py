@@ -205,6 +205,11 @@ def test_workspace_query(L):
     # few output tiles and a long K: fp32 split-K partials are requested
     ws = L.bfp8_gemm_workspace_bytes(1, 0, 0, 2048, 2048, 16384)
     assert ws > 0 and ws % (2048 * 2048 * 4) == 0
+    # 48 x 8 tiles: one whole wave of 256 tiles runs unsplit, and only the
+    # remaining 16 rows of tiles (4096 output rows) are split (in 2 along K)
+    assert L.bfp8_gemm_workspace_bytes(1, 0, 0, 12288, 2048, 16384) == 2 * 4096 * 2048 * 4
+    # 8 x 24 tiles under-fill the GPU but splitting costs more: unsplit
+    assert L.bfp8_gemm_workspace_bytes(1, 0, 0, 2048, 6144, 16384) == 0
     assert L.bfp8_gemm_workspace_bytes(3, 0, 1, 1, 1, 128) == ctypes.c_size_t(-1).value
     assert L.bfp8_gemm_workspace_bytes(1, 0, 1, 1, 1, 100) == ctypes.c_size_t(-1).value
     assert L.bfp8_gemm_workspace_bytes(1, 5, 1, 1, 1, 128) == ctypes.c_size_t(-1).value
@@ -267,14 +272,14 @@ def test_gemm_mx_errors(L):
 def test_static_scratch_gemm_rejects_before_any_launch(L):
     """bfp8_gemm_static_scratch validates like bfp8_gemm and refuses, on the
     host, a problem whose split-K partials exceed the static array."""
-    def call(layout=1, M=12288, N=2048, K=16384, A=P, sA=P, ma=0, B=P, sB=P, mb=0, C=P, ldc=2048):
+    def call(layout=1, M=3072, N=4096, K=65536, A=P, sA=P, ma=0, B=P, sB=P, mb=0, C=P, ldc=4096):
         return L.bfp8_gemm_static_scratch(layout, M, N, K, A, K, sA, ma, B, K, sB, mb, C, ldc,
                                           None)
     assert call(layout=7) == LAYOUT
     assert call(ma=2) == SMODE
     assert call(C=None) == NULL
     assert call(K=100) == SHAPE
-    assert bfp8.gemm_workspace_bytes("NT", "act", "act", 12288, 2048, 16384) > bfp8.STATIC_SCRATCH_BYTES
+    assert bfp8.gemm_workspace_bytes("NT", "act", "act", 3072, 4096, 65536) > bfp8.STATIC_SCRATCH_BYTES
     assert call() == WS
     assert "BFP8_STATIC_SCRATCH_BYTES (64u << 20)" in open(HEADER).read()
     assert bfp8.STATIC_SCRATCH_BYTES == 64 << 20

@@ -156,3 +156,32 @@ def test_split_k_matches_oracle_and_unsplit(M, N, K, modes):
     gate.check(split.float().cpu().numpy(), *parts, ("split", M, N, K), R=R)
     gate.check(unsplit.float().cpu().numpy(), *parts, ("unsplit", M, N, K), R=R)
     assert torch.equal(split, again)  # deterministic reduction order
+
+
+@pytest.mark.parametrize("modes", [("act", "act"), ("act", "block")])
+def test_hybrid_split_plan(modes):
+    """A tile grid one wave and a bit (33 x 8 tiles of 256 x 256 at K = 4096):
+    the first 256 tiles run unsplit and only the last row of 8 tiles is split
+    along K (its fp32 partials, rows 8192..8447 only, summed in split order).
+    The unsplit tiles must equal the unsplit plan's bytes; every sampled row,
+    the split rows included, must meet the parity bound."""
+    M, N, K = 8448, 2048, 4096
+    ma, mb = modes
+    rng = np.random.default_rng(17 + len(mb))
+    qa, sa, qb, sb = random_operands(rng, "NT", M, N, K, ma, mb)
+    ws = bfp8.gemm_workspace_bytes("NT", ma, mb, M, N, K)
+    split_rows = M - 8192
+    assert ws > 0 and ws % (split_rows * N * 4) == 0 and ws // (split_rows * N * 4) < 9, ws
+    t = dev_padded
+    args = (t(qa), dense(sa), t(qb), dense(sb), ma, mb)
+    hybrid = bfp8.gemm("NT", *args)
+    unsplit = bfp8.gemm("NT", *args, split_k=False)
+    again = bfp8.gemm("NT", *args)
+    torch.cuda.synchronize()
+    assert torch.equal(hybrid, again)  # deterministic reduction order
+    assert torch.equal(hybrid[:8192].view(torch.int16), unsplit[:8192].view(torch.int16))
+    rows = np.r_[0:8192:61, 8192:M]
+    bc, bsc = oracle.logical_operand(qb, sb, "B", "T", mb)
+    ac, asc = oracle.logical_operand(qa[rows], sa[rows], "A", "N", ma)  # 1x128 A scales
+    for name, C in (("hybrid", hybrid), ("unsplit", unsplit)):
+        gate.check(C.float().cpu().numpy()[rows], ac, asc, bc, bsc, (name, M, N, K, modes))

@@ -57,10 +57,10 @@ def test_static_scratch_gemm_matches_workspace_gemm(shapes):
 
 
 def test_static_scratch_rejects_partials_beyond_the_array():
-    """gate/up wgrad at 16384 tokens: 192 MiB of split-K partials, more than
-    the array holds -> BFP8_ERR_WORKSPACE before any launch; the output is
-    untouched."""
-    M, N, K = 12288, 2048, 16384
+    """3072 x 4096 x 65536 (12 x 16 tiles, each split 4 ways along K): 192 MiB
+    of split-K partials, more than the array holds -> BFP8_ERR_WORKSPACE
+    before any launch; the output is untouched."""
+    M, N, K = 3072, 4096, 65536
     assert bfp8.gemm_workspace_bytes("NT", "act", "act", M, N, K) > bfp8.STATIC_SCRATCH_BYTES
     qa = torch.zeros((M, K), dtype=torch.uint8, device="cuda")
     qb = torch.zeros((N, K), dtype=torch.uint8, device="cuda")
