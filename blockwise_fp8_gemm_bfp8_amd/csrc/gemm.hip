@@ -1107,20 +1107,26 @@ __global__ __launch_bounds__(256) void fill_zero_bf16_kernel(uint16_t* __restric
 // Sum of the split-K partials in split order, rounded to bf16 (RNE), for
 // output rows [row0, M) (the rows of the split tiles; partial row r holds
 // output row row0 + r).
+template <int S>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
-                                                            int64_t ldp, int64_t splits,
-                                                            uint16_t* __restrict__ C, int64_t ldc,
-                                                            int64_t row0, int64_t M, int64_t N) {
+                                                            int64_t ldp, uint16_t* __restrict__ C,
+                                                            int64_t ldc, int64_t row0, int64_t M,
+                                                            int64_t N) {
   const int64_t quads = (N + 3) / 4, rows = M - row0;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= rows * quads) return;
   const int64_t r = i / quads, n = (i - r * quads) * 4;
   const int64_t m = row0 + r;
   const float* p = part + r * ldp + n;
-  v4f acc = *reinterpret_cast<const v4f*>(p);
-  for (int64_t s = 1; s < splits; ++s) {
-    const v4f v = *reinterpret_cast<const v4f*>(p + s * rows * ldp);
-    acc[0] += v[0]; acc[1] += v[1]; acc[2] += v[2]; acc[3] += v[3];
+  // every split's load in flight at once (each partial is read once)
+  v4f v[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+    v[s] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p + s * rows * ldp));
+  v4f acc = v[0];
+#pragma unroll
+  for (int s = 1; s < S; ++s) {
+    acc[0] += v[s][0]; acc[1] += v[s][1]; acc[2] += v[s][2]; acc[3] += v[s][3];
   }
   const uint32_t w0 = pack_bf16x2(acc[0], acc[1]), w1 = pack_bf16x2(acc[2], acc[3]);
   uint16_t* dst = C + m * ldc + n;
@@ -1292,9 +1298,20 @@ bfp8_status launch_gemm(const GemmArgs& a, void* workspace, size_t workspace_byt
   }
   if (st != BFP8_OK || gp.splits == 1) return st;
   const int64_t n = (a.M - gp.row0) * ((a.N + 3) / 4);
-  return launch(&splitk_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
-                stream, plan.part, ldp, static_cast<int64_t>(gp.splits), a.C, a.ldc, gp.row0,
-                a.M, a.N);
+  const dim3 rgrid(static_cast<unsigned>((n + 255) / 256));
+#define BFP8_REDUCE(S_)                                                                      \
+  case S_:                                                                                   \
+    return launch(&splitk_reduce_kernel<S_>, rgrid, dim3(256), stream, plan.part, ldp, a.C, \
+                  a.ldc, gp.row0, a.M, a.N)
+  switch (gp.splits) {
+    BFP8_REDUCE(2);
+    BFP8_REDUCE(3);
+    BFP8_REDUCE(4);
+    BFP8_REDUCE(6);
+    BFP8_REDUCE(8);
+  }
+#undef BFP8_REDUCE
+  return BFP8_ERR_HIP;  // no plan has another split count
 }
 
 // ---- split-K partials in a static device array -------------------------
