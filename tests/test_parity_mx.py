@@ -294,23 +294,3 @@ def test_mx_linear_layer_end_to_end(group):
     gate.check(dx.float().cpu().numpy()[rows], *pdx, ("mx dgrad", group))
     gate.check(dw.float().cpu().numpy(), *pdw, ("mx wgrad", group))
 
-
-def test_gemm_mx_hybrid_split_plan():
-    """33 x 8 tiles at K = 4096 on the persistent power-of-two kernel: 256
-    whole tiles, then the last row of 8 tiles split along K; the whole tiles
-    equal the unsplit plan's bytes and sampled rows (all split rows
-    included) meet the parity bound."""
-    M, N, K = 8448, 2048, 4096
-    rng = np.random.default_rng(23)
-    qa, sa, qb, sb = pins_mx.random_mx_operands(rng, "NT", "act", "act", M, N, K)
-    ws = bfp8.gemm_workspace_bytes("NT", "act", "act", M, N, K)
-    assert ws > 0 and ws % ((M - 8192) * N * 4) == 0 and ws // ((M - 8192) * N * 4) < 9, ws
-    hybrid = run_mx("NT", qa, sa, "act", qb, sb, "act")
-    unsplit = run_mx("NT", qa, sa, "act", qb, sb, "act", split_k=False)
-    again = run_mx("NT", qa, sa, "act", qb, sb, "act")
-    assert torch.equal(hybrid, again)
-    assert torch.equal(hybrid[:8192].view(torch.int16), unsplit[:8192].view(torch.int16))
-    rows = np.r_[0:8192:61, 8192:M]
-    parts = gate.operand_parts("NT", qa[rows], sa[rows], "act", qb, sb, "act", mx=True)
-    for name, C in (("hybrid", hybrid), ("unsplit", unsplit)):
-        gate.check(C.float().cpu().numpy()[rows], *parts, (name, M, N, K), mx=True)
