@@ -158,20 +158,22 @@ def test_split_k_matches_oracle_and_unsplit(M, N, K, modes):
     assert torch.equal(split, again)  # deterministic reduction order
 
 
-@pytest.mark.parametrize("modes", [("act", "act"), ("act", "block")])
-def test_hybrid_split_plan(modes):
-    """A tile grid one wave and a bit (33 x 8 tiles of 256 x 256 at K = 4096):
-    the first 256 tiles run unsplit and only the last row of 8 tiles is split
-    along K (its fp32 partials, rows 8192..8447 only, summed in split order).
-    The unsplit tiles must equal the unsplit plan's bytes; every sampled row,
-    the split rows included, must meet the parity bound."""
-    M, N, K = 8448, 2048, 4096
+@pytest.mark.parametrize("M,N,modes", [(8448, 2048, ("act", "act")), (8448, 2048, ("act", "block")),
+                                        (8348, 2000, ("act", "act"))])
+def test_hybrid_split_plan(M, N, modes):
+    """A tile grid one wave and a bit (33 x 8 tiles of 256 x 256 at K = 4096,
+    the last row and column of tiles ragged in the third case): the first 256
+    tiles run unsplit and only the last row of 8 tiles is split along K (its
+    fp32 partials, rows 8192.. only, summed in split order).  The unsplit
+    tiles must equal the unsplit plan's bytes; every sampled row, the split
+    rows included, must meet the parity bound."""
+    K = 4096
     ma, mb = modes
     rng = np.random.default_rng(17 + len(mb))
     qa, sa, qb, sb = random_operands(rng, "NT", M, N, K, ma, mb)
     ws = bfp8.gemm_workspace_bytes("NT", ma, mb, M, N, K)
-    split_rows = M - 8192
-    assert ws > 0 and ws % (split_rows * N * 4) == 0 and ws // (split_rows * N * 4) < 9, ws
+    split_rows, ldp = M - 8192, (N + 3) // 4 * 4
+    assert ws > 0 and ws % (split_rows * ldp * 4) == 0 and ws // (split_rows * ldp * 4) < 9, ws
     t = dev_padded
     args = (t(qa), dense(sa), t(qb), dense(sb), ma, mb)
     hybrid = bfp8.gemm("NT", *args)
