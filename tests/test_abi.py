@@ -210,6 +210,10 @@ def test_workspace_query(L):
     assert L.bfp8_gemm_workspace_bytes(1, 0, 0, 12288, 2048, 16384) == 2 * 4096 * 2048 * 4
     # 8 x 24 tiles under-fill the GPU but splitting costs more: unsplit
     assert L.bfp8_gemm_workspace_bytes(1, 0, 0, 2048, 6144, 16384) == 0
+    # 1x32 modes exist only for the persistent E8M0 kernel, which splits every
+    # tile alike and runs this one unsplit; 1x128 modes get the larger plan
+    assert L.bfp8_gemm_workspace_bytes(1, 2, 2, 12288, 2048, 16384) == 0
+    assert L.bfp8_gemm_workspace_bytes(1, 2, 2, 2048, 2048, 16384) == 4 * 2048 * 2048 * 4
     assert L.bfp8_gemm_workspace_bytes(3, 0, 1, 1, 1, 128) == ctypes.c_size_t(-1).value
     assert L.bfp8_gemm_workspace_bytes(1, 0, 1, 1, 1, 100) == ctypes.c_size_t(-1).value
     assert L.bfp8_gemm_workspace_bytes(1, 5, 1, 1, 1, 128) == ctypes.c_size_t(-1).value
