@@ -35,8 +35,12 @@ def call_static(qa, sa, qb, sb, out):
         ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
 
 
-@pytest.mark.parametrize("shapes", [[(2048, 2048, 16384), (1024, 512, 16384)]])
+@pytest.mark.parametrize("shapes", [[(2048, 2048, 16384), (1024, 512, 16384)],
+                                    [(2048, 2048, 16384), (8448, 2048, 4096)]])
 def test_static_scratch_gemm_matches_workspace_gemm(shapes):
+    """Every tile split (2048 x 2048 and 1024 x 512 at K = 16384), or 256
+    whole tiles and only the last row of tiles split (8448 x 2048 x 4096);
+    each pair: two calls in a row, the second with fewer input bytes."""
     g = torch.Generator(device="cuda").manual_seed(5)
     for M, N, K in shapes:
         need = bfp8.gemm_workspace_bytes("NT", "act", "act", M, N, K)
@@ -49,7 +53,7 @@ def test_static_scratch_gemm_matches_workspace_gemm(shapes):
         ref = bfp8.gemm("NT", qa, sa, qb, sb, "act", "act")   # allocates its workspace
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), (M, N, K)
-        rows = np.arange(0, M, M // 16)
+        rows = np.r_[0:M:M // 16, M - 64:M]   # the last rows lie in split tiles
         ac, asc = oracle.logical_operand(qa[rows].cpu().numpy(), sa[rows].cpu().numpy(),
                                          "A", "N", "act")
         bc, bsc = oracle.logical_operand(qb.cpu().numpy(), sb.cpu().numpy(), "B", "T", "act")
