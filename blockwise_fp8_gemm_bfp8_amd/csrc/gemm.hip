@@ -745,7 +745,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(k4Threads, k4Threads),
 gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__ sA_,
                 const uint8_t* __restrict__ B, int64_t ldb, const void* __restrict__ sB_,
                 uint16_t* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K, int tiles_m,
-                int tiles_n, int splits, float* __restrict__ part, int64_t ldp) {
+                int tiles_n, int splits, float* __restrict__ part, int64_t ldp, int64_t pstride) {
   const uint8_t* __restrict__ eA = static_cast<const uint8_t*>(sA_);
   const uint8_t* __restrict__ eB = static_cast<const uint8_t*>(sB_);
   // MODE 3: 1x128 groups, scale bytes stored K-block major ([K/128][rows])
@@ -990,7 +990,7 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
   // ---- epilogue pieces ----------------------------------------------------------
   // split-K partial: 4 consecutive fp32 columns per lane, 16-byte stores
   auto store_partial = [&]() {
-    float* pbase = part + static_cast<int64_t>(split) * M * ldp;
+    float* pbase = part + static_cast<int64_t>(split) * pstride;  // splits pstride apart
     if (m0 + wm * W4M + W4M <= M && n0 + wn * W4N + W4N <= N) {
       float* dst = pbase + (m0 + wm * W4M + r16) * ldp + n0 + wn * W4N + 4 * g;
 #pragma unroll
@@ -1104,25 +1104,25 @@ __global__ __launch_bounds__(256) void fill_zero_bf16_kernel(uint16_t* __restric
   C[r * ldc + c] = 0;
 }
 
-// Sum of the split-K partials in split order, rounded to bf16 (RNE), for
-// output rows [row0, M) (the rows of the split tiles; partial row r holds
-// output row row0 + r).
+// Sum of the split-K partials in split order, rounded to bf16 (RNE): rows
+// [0, rows) of C (the rows of the split tiles, C already pointing at the
+// first) from partial rows [0, rows) of each split, splits pstride elements
+// apart.
 template <int S>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
-                                                            int64_t ldp, uint16_t* __restrict__ C,
-                                                            int64_t ldc, int64_t row0, int64_t M,
-                                                            int64_t N) {
-  const int64_t quads = (N + 3) / 4, rows = M - row0;
+                                                            int64_t ldp, int64_t pstride,
+                                                            uint16_t* __restrict__ C, int64_t ldc,
+                                                            int64_t rows, int64_t N) {
+  const int64_t quads = (N + 3) / 4;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= rows * quads) return;
-  const int64_t r = i / quads, n = (i - r * quads) * 4;
-  const int64_t m = row0 + r;
-  const float* p = part + r * ldp + n;
+  const int64_t m = i / quads, n = (i - m * quads) * 4;
+  const float* p = part + m * ldp + n;
   // every split's load in flight at once (each partial is read once)
   v4f v[S];
 #pragma unroll
   for (int s = 0; s < S; ++s)
-    v[s] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p + s * rows * ldp));
+    v[s] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p + s * pstride));
   v4f acc = v[0];
 #pragma unroll
   for (int s = 1; s < S; ++s) {
@@ -1142,7 +1142,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 
 template <bool A_KM, bool B_KM, bool MX>
 static bfp8_status launch_layout(const GemmArgs& a, dim3 grid, dim3 pgrid, const UnitPlan& plan,
-                                 hipStream_t stream) {
+                                 int64_t pstride, hipStream_t stream) {
 // float32 scales: the 8-wave kernel; E8M0 scales: the 4-wave kernel
 #define BFP8_LAUNCH(MA, MB)                                                                   \
   do {                                                                                        \
@@ -1150,7 +1150,7 @@ static bfp8_status launch_layout(const GemmArgs& a, dim3 grid, dim3 pgrid, const
       return launch(&gemm_mx4_kernel<A_KM, B_KM, MA, MB>, pgrid, dim3(k4Threads), stream,    \
                     a.A, a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K,            \
                     plan.tiles_m, plan.tiles_n, plan.splits, plan.part,                       \
-                    (a.N + 3) & ~int64_t(3));                                                 \
+                    (a.N + 3) & ~int64_t(3), pstride);                                        \
     else                                                                                      \
       return launch(&gemm_kernel<A_KM, B_KM, MA, MB>, grid, dim3(kThreads), stream, a.A,      \
                     a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K, plan);          \
@@ -1222,8 +1222,11 @@ GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, bool mx) {
   // whole waves first: a multiple of the CU count that is also a multiple of
   // the tile walk's row groups, so the split tiles are whole rows of tiles
   const int64_t full = (tiles / kCUs) * kCUs;
-  // (the persistent power-of-two kernel splits every tile alike)
-  const bool hybrid = !mx && full > 0 && full < tiles && full % (kGroupM * tiles_n) == 0;
+  // (the persistent power-of-two kernel runs such a plan as two launches of
+  // whole rows of tiles, so for it the split rows must not end in a ragged
+  // tile)
+  const bool hybrid = full > 0 && full < tiles && full % (kGroupM * tiles_n) == 0 &&
+                      (!mx || M % BM == 0);
   for (int64_t S : {2, 3, 4, 6, 8}) {
     if (KB / S < 8) break;
     if (KB % S != 0) continue;  // equal ranges of K blocks
@@ -1251,6 +1254,19 @@ size_t gemm_split_workspace(int64_t M, int64_t N, int64_t K, bool mx) {
   const GemmPlan p = gemm_plan(M, N, K, mx);
   return p.splits > 1 ? static_cast<size_t>(p.splits) * (M - p.row0) * split_ldp(N) * sizeof(float)
                       : 0;
+}
+
+// Byte offset of the E8M0 scales of A's row r0 (a multiple of 128), for A
+// stored [M][K] (a_kmajor false) or [K][M], in scale mode `mode`.
+static int64_t mx_scale_row_offset(bool a_kmajor, int mode, int64_t r0, int64_t K) {
+  const int64_t KB = K / BK;
+  if (a_kmajor) return mode == 1 ? r0 / 128 : r0;  // [KB][M/128] or [KB][M]
+  switch (mode) {
+    case 0: return r0 * KB;                         // [M][KB]
+    case 1: return (r0 / 128) * KB;                 // [M/128][KB]
+    case 2: return r0 * (K / 32);                   // [M][K/32]
+    default: return r0;                             // 3: [KB][M]
+  }
 }
 
 bfp8_status launch_gemm(const GemmArgs& a, void* workspace, size_t workspace_bytes,
@@ -1284,25 +1300,58 @@ bfp8_status launch_gemm(const GemmArgs& a, void* workspace, size_t workspace_byt
     return BFP8_ERR_HIP;
   const int64_t wgs = cus >= kXcds ? (cus / kXcds) * kXcds : cus;
   const dim3 pgrid(static_cast<unsigned>(units < wgs ? units : wgs));
+  // splits of the partials: (M - row0) rows apart, the rows of the split tiles
+  const int64_t rows_all = a.M - gp.row0;
+  auto launch_mx = [&](const GemmArgs& g, const UnitPlan& p, dim3 pg, int64_t pst) -> bfp8_status {
+    if (!g.a_kmajor && !g.b_kmajor) return launch_layout<false, false, true>(g, grid, pg, p, pst, stream);
+    if (!g.a_kmajor && g.b_kmajor) return launch_layout<false, true, true>(g, grid, pg, p, pst, stream);
+    if (g.a_kmajor && g.b_kmajor) return launch_layout<true, true, true>(g, grid, pg, p, pst, stream);
+    return BFP8_ERR_LAYOUT;
+  };
+  auto min_wgs = [&](int64_t u) { return dim3(static_cast<unsigned>(u < wgs ? u : wgs)); };
   bfp8_status st;
-  if (a.mx) {
-    if (!a.a_kmajor && !a.b_kmajor) st = launch_layout<false, false, true>(a, grid, pgrid, plan, stream);
-    else if (!a.a_kmajor && a.b_kmajor) st = launch_layout<false, true, true>(a, grid, pgrid, plan, stream);
-    else if (a.a_kmajor && a.b_kmajor) st = launch_layout<true, true, true>(a, grid, pgrid, plan, stream);
+  if (a.mx && gp.splits > 1 && gp.full > 0) {
+    // the persistent kernel splits every tile of a launch alike, so the plan
+    // runs as two launches: the whole tiles (output rows [0, row0)), then the
+    // rows [row0, M) as a GEMM of their own whose operand A, scales and C
+    // start row0 rows in (M itself stays the scales' row count; M - row0 is
+    // a multiple of 256, so no tile of either launch reaches past its rows),
+    // its partials (M - row0) rows per split as in the float32 kernel
+    UnitPlan p1 = plan, p2 = plan;
+    p1.tiles_m = plan.trow0;
+    p1.full = plan.trow0 * plan.tiles_n;
+    p1.splits = 1;
+    p1.part = nullptr;
+    st = launch_mx(a, p1, min_wgs(p1.full), 0);
+    if (st != BFP8_OK) return st;
+    GemmArgs a2 = a;
+    a2.A = a.A + (a.a_kmajor ? gp.row0 : gp.row0 * a.lda);
+    a2.sA = static_cast<const uint8_t*>(a.sA) +
+            mx_scale_row_offset(a.a_kmajor, a.modeA, gp.row0, a.K);
+    a2.C = a.C + gp.row0 * a.ldc;
+    p2.tiles_m = plan.tiles_m - plan.trow0;
+    p2.full = 0;
+    st = launch_mx(a2, p2, min_wgs(static_cast<int64_t>(p2.tiles_m) * p2.tiles_n * p2.splits),
+                   rows_all * ldp);
+  } else if (a.mx) {
+    if (!a.a_kmajor && !a.b_kmajor) st = launch_layout<false, false, true>(a, grid, pgrid, plan, rows_all * ldp, stream);
+    else if (!a.a_kmajor && a.b_kmajor) st = launch_layout<false, true, true>(a, grid, pgrid, plan, rows_all * ldp, stream);
+    else if (a.a_kmajor && a.b_kmajor) st = launch_layout<true, true, true>(a, grid, pgrid, plan, rows_all * ldp, stream);
     else return BFP8_ERR_LAYOUT;
   } else {
-    if (!a.a_kmajor && !a.b_kmajor) st = launch_layout<false, false, false>(a, grid, pgrid, plan, stream);
-    else if (!a.a_kmajor && a.b_kmajor) st = launch_layout<false, true, false>(a, grid, pgrid, plan, stream);
-    else if (a.a_kmajor && a.b_kmajor) st = launch_layout<true, true, false>(a, grid, pgrid, plan, stream);
+    if (!a.a_kmajor && !a.b_kmajor) st = launch_layout<false, false, false>(a, grid, pgrid, plan, rows_all * ldp, stream);
+    else if (!a.a_kmajor && a.b_kmajor) st = launch_layout<false, true, false>(a, grid, pgrid, plan, rows_all * ldp, stream);
+    else if (a.a_kmajor && a.b_kmajor) st = launch_layout<true, true, false>(a, grid, pgrid, plan, rows_all * ldp, stream);
     else return BFP8_ERR_LAYOUT;
   }
   if (st != BFP8_OK || gp.splits == 1) return st;
-  const int64_t n = (a.M - gp.row0) * ((a.N + 3) / 4);
+  const int64_t rows = rows_all, pstride = rows_all * ldp;
+  const int64_t n = rows * ((a.N + 3) / 4);
   const dim3 rgrid(static_cast<unsigned>((n + 255) / 256));
 #define BFP8_REDUCE(S_)                                                                      \
   case S_:                                                                                   \
-    return launch(&splitk_reduce_kernel<S_>, rgrid, dim3(256), stream, plan.part, ldp, a.C, \
-                  a.ldc, gp.row0, a.M, a.N)
+    return launch(&splitk_reduce_kernel<S_>, rgrid, dim3(256), stream, plan.part, ldp,      \
+                  pstride, a.C + gp.row0 * a.ldc, a.ldc, rows, a.N)
   switch (gp.splits) {
     BFP8_REDUCE(2);
     BFP8_REDUCE(3);

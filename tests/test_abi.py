@@ -206,13 +206,13 @@ def test_workspace_query(L):
     ws = L.bfp8_gemm_workspace_bytes(1, 0, 0, 2048, 2048, 16384)
     assert ws > 0 and ws % (2048 * 2048 * 4) == 0
     # 48 x 8 tiles: one whole wave of 256 tiles runs unsplit, and only the
-    # remaining 16 rows of tiles (4096 output rows) are split (in 2 along K)
+    # remaining 16 rows of tiles (4096 output rows) are split (in 2 along K);
+    # the partials cover those rows only, for both GEMM entry points (1x32
+    # modes exist only for the E8M0 one)
     assert L.bfp8_gemm_workspace_bytes(1, 0, 0, 12288, 2048, 16384) == 2 * 4096 * 2048 * 4
+    assert L.bfp8_gemm_workspace_bytes(1, 2, 2, 12288, 2048, 16384) == 2 * 4096 * 2048 * 4
     # 8 x 24 tiles under-fill the GPU but splitting costs more: unsplit
     assert L.bfp8_gemm_workspace_bytes(1, 0, 0, 2048, 6144, 16384) == 0
-    # 1x32 modes exist only for the persistent E8M0 kernel, which splits every
-    # tile alike and runs this one unsplit; 1x128 modes get the larger plan
-    assert L.bfp8_gemm_workspace_bytes(1, 2, 2, 12288, 2048, 16384) == 0
     assert L.bfp8_gemm_workspace_bytes(1, 2, 2, 2048, 2048, 16384) == 4 * 2048 * 2048 * 4
     assert L.bfp8_gemm_workspace_bytes(3, 0, 1, 1, 1, 128) == ctypes.c_size_t(-1).value
     assert L.bfp8_gemm_workspace_bytes(1, 0, 1, 1, 1, 100) == ctypes.c_size_t(-1).value

@@ -165,15 +165,14 @@ def test_hybrid_split_plan(M, N, modes):
     the last row and column of tiles ragged in the third case): the first 256
     tiles run unsplit and only the last row of 8 tiles is split along K (its
     fp32 partials, rows 8192.. only, summed in split order).  The unsplit
-    tiles must equal the unsplit plan's bytes; every sampled row, the split
-    rows included, must meet the parity bound."""
+    tiles must equal the unsplit plan's bytes (a plan that split every tile
+    would sum them in another order); every sampled row, the split rows
+    included, must meet the parity bound."""
     K = 4096
     ma, mb = modes
     rng = np.random.default_rng(17 + len(mb))
     qa, sa, qb, sb = random_operands(rng, "NT", M, N, K, ma, mb)
-    ws = bfp8.gemm_workspace_bytes("NT", ma, mb, M, N, K)
-    split_rows, ldp = M - 8192, (N + 3) // 4 * 4
-    assert ws > 0 and ws % (split_rows * ldp * 4) == 0 and ws // (split_rows * ldp * 4) < 9, ws
+    assert bfp8.gemm_workspace_bytes("NT", ma, mb, M, N, K) > 0  # a split plan
     t = dev_padded
     args = (t(qa), dense(sa), t(qb), dense(sb), ma, mb)
     hybrid = bfp8.gemm("NT", *args)

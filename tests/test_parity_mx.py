@@ -294,3 +294,28 @@ def test_mx_linear_layer_end_to_end(group):
     gate.check(dx.float().cpu().numpy()[rows], *pdx, ("mx dgrad", group))
     gate.check(dw.float().cpu().numpy(), *pdw, ("mx wgrad", group))
 
+
+def test_gemm_mx_hybrid_split_plan():
+    """33 x 8 tiles at K = 4096 on the persistent power-of-two kernel: 256
+    whole tiles in one launch, then the last row of 8 tiles split along K in
+    a second launch that starts 8192 rows into A, its scales and C.  The
+    whole tiles equal the unsplit plan's bytes (a plan that split every tile
+    would sum them in another order); sampled rows, every split row
+    included, meet the parity bound."""
+    M, N, K = 8448, 2048, 4096
+    rng = np.random.default_rng(23)
+    rows = np.r_[0:8192:61, 8192:M]
+    for layout, ma, mb in (("NT", "act", "act"), ("NT", "mx32", "mx32"), ("NT", "act", "block"),
+                           ("TN", "act", "act")):
+        qa, sa, qb, sb = pins_mx.random_mx_operands(rng, layout, ma, mb, M, N, K)
+        assert bfp8.gemm_workspace_bytes(layout, ma, mb, M, N, K) > 0  # a split plan
+        hybrid = run_mx(layout, qa, sa, ma, qb, sb, mb)
+        unsplit = run_mx(layout, qa, sa, ma, qb, sb, mb, split_k=False)
+        again = run_mx(layout, qa, sa, ma, qb, sb, mb)
+        assert torch.equal(hybrid, again)
+        assert torch.equal(hybrid[:8192].view(torch.int16), unsplit[:8192].view(torch.int16))
+        # A's sampled rows: stored rows for 'N', stored columns for 'T' (1x128 scales)
+        qs, ss = (qa[rows], sa[rows]) if layout[0] == "N" else (qa[:, rows], sa[:, rows])
+        parts = gate.operand_parts(layout, qs, ss, ma, qb, sb, mb, mx=True)
+        for name, C in (("hybrid", hybrid), ("unsplit", unsplit)):
+            gate.check(C.float().cpu().numpy()[rows], *parts, (name, layout, ma, mb), mx=True)
