@@ -356,10 +356,10 @@ bfp8_status bfp8_gemm_static_scratch(bfp8_layout layout, int64_t M, int64_t N, i
 
 /* Workspace bytes that let bfp8_gemm and bfp8_gemm_mx use their split-K
  * plans for this problem (0 when both run unsplit; the larger of the two
- * when the plans differ: bfp8_gemm may run whole waves of tiles unsplit and
- * split only the tiles of a last, partial wave, while the persistent
- * bfp8_gemm_mx kernel splits every tile alike).  Returns (size_t)-1 for an
- * invalid layout, scale mode or size. */
+ * when the plans differ: both may run whole waves of tiles unsplit and split
+ * only the tiles of a last, partial wave, bfp8_gemm_mx only when M is a
+ * multiple of 256).  Returns (size_t)-1 for an invalid layout, scale mode or
+ * size. */
 size_t bfp8_gemm_workspace_bytes(bfp8_layout layout, bfp8_scale_mode modeA,
                                  bfp8_scale_mode modeB, int64_t M, int64_t N, int64_t K);
 
