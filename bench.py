@@ -653,15 +653,17 @@ def _short_kernel_name(name):
     return (m.group(1) + (m.group(2) or "")) if m else name[:80]
 
 
-def summarize_trace(db, warmup, steps):
+def summarize_trace(db, warmup, steps, workload=DEFAULT_WORKLOAD):
     """Markdown summary of a rocprofv3 --kernel-trace database of this
     script: every kernel over the whole run, then the timed passes alone.
 
     The first dispatches of the run are the W warm-up passes, then the K
     headline passes, then the K instrumented passes; a pass is found as the
-    period of the dispatch sequence.  A GEMM call is its gemm kernel plus the
-    split-K reduction that follows it, which is what the line's event timing
-    brackets."""
+    period of the dispatch sequence.  A GEMM call is its gemm kernel
+    launches (two when the power-of-two kernel runs a split plan as whole
+    tiles, then split tiles) plus the split-K reduction that follows, which
+    is what the line's event timing brackets: the mean call is the pass's
+    GEMM and reduction time over the workload's GEMM count."""
     import sqlite3
 
     con = sqlite3.connect(db)
@@ -703,9 +705,13 @@ def summarize_trace(db, warmup, steps):
     for n, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
         out.append(f"| `{n}` | {len(v)} | {sum(v) / len(v):.2f} | {statistics.median(v):.2f} |")
     if calls:
-        out += ["", f"GEMM calls per pass: {len(calls) // steps}; mean GEMM call (kernel + its "
-                f"split-K reduction) {sum(calls) / len(calls):.2f} us; mean gemm kernel alone "
-                f"{sum(kern) / len(kern):.2f} us."]
+        from workloads import WORKLOADS
+
+        n_calls = len(WORKLOADS[workload].gemms) * steps
+        out += ["", f"GEMM calls per pass: {n_calls // steps} ({len(kern) // steps} gemm kernel "
+                f"launches); mean GEMM call (its kernel launches + split-K reduction) "
+                f"{sum(calls) / n_calls:.2f} us; gemm kernels alone {sum(kern) / n_calls:.2f} us "
+                f"per call."]
     return "\n".join(out)
 
 
@@ -744,7 +750,7 @@ def main():
     args = ap.parse_args()
 
     if args.summarize_trace:
-        print(summarize_trace(args.summarize_trace, args.warmup, args.steps))
+        print(summarize_trace(args.summarize_trace, args.warmup, args.steps, args.workload))
         return
     if args.summarize_pmc:
         print(summarize_pmc(args.summarize_pmc, args.write_traffic, args.workload))

@@ -111,3 +111,29 @@ def test_rel_errors_normwise_and_worst_element():
     e = bench.rel_errors(C, R)
     assert e["normwise"] == 0.1 and e["max_over_rms"] == 0.2
     assert bench.rel_errors(C.astype(np.float32), R)["normwise"] == 0.1
+
+
+def test_trace_summary_counts_a_two_launch_gemm_call_once(tmp_path):
+    """--summarize-trace: a pass of the tiny workload (one GEMM) whose call
+    is two gemm kernel launches and a split-K reduction (the power-of-two
+    kernel's whole-wave plan) gives one call whose time is all three."""
+    import sqlite3
+
+    db = tmp_path / "t.db"
+    con = sqlite3.connect(db)
+    con.execute("create table kernels (name text, start integer, duration integer)")
+    t = 0
+    # 1 warm-up + 2 headline + 2 instrumented passes of 4 dispatches each
+    for _ in range(5):
+        for name, d in (("quantize_dual_ct_kernel<0, 128, true, true>", 5000),
+                        ("gemm_mx4_kernel<false, false, 3, 3>", 100000),
+                        ("gemm_mx4_kernel<false, false, 3, 3>", 40000),
+                        ("splitk_reduce_kernel<2>", 10000)):
+            con.execute("insert into kernels values (?, ?, ?)", (name, t, d))
+            t += d
+    con.commit()
+    con.close()
+    md = bench.summarize_trace(str(db), 1, 2, "tiny_256x512x384")
+    line = [x for x in md.splitlines() if x.startswith("GEMM calls per pass")][0]
+    assert "GEMM calls per pass: 1 (2 gemm kernel launches)" in line, line
+    assert "150.00 us" in line and "140.00 us per call" in line, line
