@@ -1118,11 +1118,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   if (i >= rows * quads) return;
   const int64_t m = i / quads, n = (i - m * quads) * 4;
   const float* p = part + m * ldp + n;
-  // every split's load in flight at once (each partial is read once)
+  // every split's load in flight at once (plain loads: the partials were
+  // just written and are read from the caches; non-temporal loads and
+  // non-temporal partial stores both measured slower)
   v4f v[S];
 #pragma unroll
-  for (int s = 0; s < S; ++s)
-    v[s] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p + s * pstride));
+  for (int s = 0; s < S; ++s) v[s] = *reinterpret_cast<const v4f*>(p + s * pstride);
   v4f acc = v[0];
 #pragma unroll
   for (int s = 1; s < S; ++s) {
