@@ -380,13 +380,27 @@ __device__ __forceinline__ void load_mx_scale_bytes(const uint8_t* s, int64_t by
                make_rsrc(s, (bytes + 3) & ~int64_t(3)));
 }
 
-template <bool A_KM, bool B_KM, int MODE_A, int MODE_B>
+template <bool A_KM, bool B_KM, int MODE_A, int MODE_B, int BNT>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(2, 2))) void
 gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__ sA_,
             const uint8_t* __restrict__ B, int64_t ldb, const void* __restrict__ sB_,
             uint16_t* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K,
             const UnitPlan plan) {
+  // BNT: output columns per tile, 256, or 192 (wave tile 64 x 96) for
+  // K-contiguous B with 1x128 scales, whose 192 rows of B fill the copy
+  // pieces of 8 waves evenly and whose scales are per column (a wave's 96
+  // columns may straddle two 128-column weight blocks)
+  static_assert(BNT == 256 || (BNT == 192 && !B_KM && (MODE_B == 0 || MODE_B == 3)),
+                "192-column tiles: K-contiguous B with 1x128 scales");
+  constexpr int WNT = BNT / kWavesN;          // 128 or 96
+  constexpr int TNT = WNT / 16;               // 8 or 6 column subtiles
+  constexpr int kTileBBytesT = BNT * BK;      // 32 or 24 KiB
+  constexpr int kStageBytesT = kTileABytes + kTileBBytesT + kScaleBytes;
+  constexpr int kEpiRowBytesT = WNT * 2 + 8;  // bf16 row of a wave tile, padded
+  constexpr int kEpiSlotBytesT = WM * kEpiRowBytesT;
+  static_assert(4 * kEpiSlotBytesT <= kStageBytesT, "four epilogue slots per stage");
+  constexpr int kPiecesB = BNT / 64;          // 1 KiB copies of B per wave and K block
   const float* __restrict__ sA = static_cast<const float*>(sA_);
   const float* __restrict__ sB = static_cast<const float*>(sB_);
   // MODE 3: 1x128 groups like MODE 0, with the scale tensor stored K-block
@@ -394,8 +408,8 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
   constexpr int MA = MODE_A == 3 ? 0 : MODE_A, MB = MODE_B == 3 ? 0 : MODE_B;
   constexpr bool SKA = A_KM || MODE_A == 3, SKB = B_KM || MODE_B == 3;
   // Two pipeline stages; block kb lives in stage kb % 2.
-  __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytesT];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytesT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -412,17 +426,18 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
   int tm, tn, kb_begin, kb_end;
   const int split = plan_unit(plan, blockIdx.x, static_cast<int>(KB), tm, tn, kb_begin, kb_end);
   const int64_t m0 = static_cast<int64_t>(tm) * BM;
-  const int64_t n0 = static_cast<int64_t>(tn) * BN;
+  const int64_t n0 = static_cast<int64_t>(tn) * BNT;
 
   Operand<A_KM> opa;
-  Operand<B_KM> opb;
+  Operand<B_KM, kPiecesB> opb;
   opa.init(A, lda, m0, M, K, wave, lane);
   opb.init(B, ldb, n0, N, K, wave, lane);
 
   // The copy of one K block is split into 9 pieces per wave (4 x 1 KiB of
-  // A, 4 x 1 KiB of B, one dword per lane of act-mode scales) so the pieces
-  // can be spread over the MFMA issue slots of the block before.
-  constexpr int kLoadPieces = 9;
+  // A, 4 x 1 KiB of B -- 3 for 192-column tiles -- and one dword per lane of
+  // act-mode scales) so the pieces can be spread over the MFMA issue slots
+  // of the block before.
+  constexpr int kLoadPieces = 4 + kPiecesB + 1;
   i32x4 rsrc_a, rsrc_b;  // descriptors of the K block being copied
 
   // float32 scales: the one dword-per-lane copy this wave makes per K block
@@ -479,10 +494,10 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
   auto issue_piece = [&](int64_t kb, uint8_t* st, int piece) {
     if (piece < 4) {
       opa.load_piece(rsrc_a, st, wave, piece);
-    } else if (piece < 8) {
+    } else if (piece < 4 + kPiecesB) {
       opb.load_piece(rsrc_b, st + kTileABytes, wave, piece - 4);
     } else {
-      uint8_t* sdst = st + kTileABytes + kTileBBytes;
+      uint8_t* sdst = st + kTileABytes + kTileBBytesT;
       if (sc_active) {
         copy4_to_lds(__builtin_amdgcn_readfirstlane(lds_addr(sdst) + sc_lds), sc_voff,
                      advanced_rsrc(sc_base, kb, sc_stride, sc_ext));
@@ -500,7 +515,7 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
   // (a wave's 64 rows / 128 columns sit in one 128-block); every scale
   // comes from the K block's LDS stage, copied with its codes
   auto row_mults = [&](const uint8_t* st, float (&ra)[TM]) {
-    const float* s_lds = reinterpret_cast<const float*>(st + kTileABytes + kTileBBytes);
+    const float* s_lds = reinterpret_cast<const float*>(st + kTileABytes + kTileBBytesT);
     const float sb = MB == 1 ? s_lds[BM + wn] : 1.0f;
     if (MA == 0) {
 #pragma unroll
@@ -513,17 +528,17 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
   };
   auto col_mults = [&](const uint8_t* st, int j, float (&cb)[4]) {
     if (MB == 0) {
-      const float* s_lds = reinterpret_cast<const float*>(st + kTileABytes + kTileBBytes);
-      const float4 v = *reinterpret_cast<const float4*>(s_lds + BM + wn * WN + 16 * j + 4 * g);
+      const float* s_lds = reinterpret_cast<const float*>(st + kTileABytes + kTileBBytesT);
+      const float4 v = *reinterpret_cast<const float4*>(s_lds + BM + wn * WNT + 16 * j + 4 * g);
       cb[0] = v.x; cb[1] = v.y; cb[2] = v.z; cb[3] = v.w;
     }
   };
 
-  v4f acc[TM][TN];
+  v4f acc[TM][TNT];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TNT; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // Promotion of one 16x16 partial: acc += P * (row multiplier * column
   // multiplier).  The partial of subtile (i, j) is promoted right after the
@@ -552,7 +567,7 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
   float ra[TM];
 #pragma unroll
   for (int i = 0; i < TM; ++i) af[i] = opa.frag(stage0, wm * WM + 16 * i, lane);
-  bq = opb.frag(stage0 + kTileABytes, wn * WN, lane);
+  bq = opb.frag(stage0 + kTileABytes, wn * WNT, lane);
   row_mults(stage0, ra);
 
   // Partials are promoted kLag MFMAs behind their issue (subtile order
@@ -583,9 +598,9 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
       rsrc_b.z = 0;
     }
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
+    for (int j = 0; j < TNT; ++j) {
       v8i bn = bq;
-      if (j + 1 < TN) bn = opb.frag(cur + kTileABytes, wn * WN + 16 * (j + 1), lane);
+      if (j + 1 < TNT) bn = opb.frag(cur + kTileABytes, wn * WNT + 16 * (j + 1), lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) cm_prev[r] = cm_cur[r];
       col_mults(cur, j, cm_cur);
@@ -612,7 +627,7 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
       bq = bn;
     }
     // all MFMAs of this K block are issued; the last kLag subtiles (all in
-    // column TN-1) are pending with this block's multipliers
+    // column TNT-1) are pending with this block's multipliers
 #pragma unroll
     for (int i = 0; i < TM; ++i) ra_last[i] = ra[i];
     if (more) {
@@ -620,15 +635,15 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
       __syncthreads();                     // everyone's did, and `cur` is free
       // B fragment and A row 0 first: the next block's first MFMA needs
       // only those two
-      bq = opb.frag(nxt + kTileABytes, wn * WN, lane);
+      bq = opb.frag(nxt + kTileABytes, wn * WNT, lane);
 #pragma unroll
       for (int i = 0; i < TM; ++i) af[i] = opa.frag(nxt, wm * WM + 16 * i, lane);
       row_mults(nxt, ra);
     }
 #pragma unroll
     for (int q = 0; q < kLag; ++q) {
-      const int t = TM * TN - kLag + q;
-      promote(acc[t % TM][TN - 1], pend[t % kLag], ra_last[t % TM], cm_cur);
+      const int t = TM * TNT - kLag + q;
+      promote(acc[t % TM][TNT - 1], pend[t % kLag], ra_last[t % TM], cm_cur);
     }
   };
 
@@ -644,12 +659,12 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
     // split-K partial: 4 consecutive fp32 columns per lane, 16-byte stores
     const int64_t ldp = (N + 3) & ~int64_t(3);
     float* pbase = plan.part + partial_row(plan, split, m0, M, ldp);
-    if (m0 + wm * WM + WM <= M && n0 + wn * WN + WN <= N) {
-      float* dst = pbase + (wm * WM + r16) * ldp + n0 + wn * WN + 4 * g;
+    if (m0 + wm * WM + WM <= M && n0 + wn * WNT + WNT <= N) {
+      float* dst = pbase + (wm * WM + r16) * ldp + n0 + wn * WNT + 4 * g;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TNT; ++j)
           *reinterpret_cast<v4f*>(dst + 16 * i * ldp + 16 * j) = acc[i][j];
       return;
     }
@@ -658,8 +673,8 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
       const int64_t m = m0 + wm * WM + 16 * i + r16;
       if (m >= M) continue;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t n = n0 + wn * WN + 16 * j + 4 * g;
+      for (int j = 0; j < TNT; ++j) {
+        const int64_t n = n0 + wn * WNT + 16 * j + 4 * g;
         if (n < N) {
           float* dst = pbase + (m - m0) * ldp + n;
 #pragma unroll
@@ -677,40 +692,44 @@ gemm_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restrict__
   // kernel, and keeping it out of L2 leaves the operand tiles other
   // workgroups still stream there.
   __syncthreads();  // every wave is done reading both stages
-  uint8_t* slot = (wave < 4 ? stage0 : stage1) + (wave & 3) * kEpiSlotBytes;
+  uint8_t* slot = (wave < 4 ? stage0 : stage1) + (wave & 3) * kEpiSlotBytesT;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      *reinterpret_cast<uint2*>(slot + (16 * i + r16) * kEpiRowBytes + (16 * j + 4 * g) * 2) =
+    for (int j = 0; j < TNT; ++j) {
+      *reinterpret_cast<uint2*>(slot + (16 * i + r16) * kEpiRowBytesT + (16 * j + 4 * g) * 2) =
           make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]),
                      pack_bf16x2(acc[i][j][2], acc[i][j][3]));
     }
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's slot is written
   __builtin_amdgcn_wave_barrier();
-  const int64_t mw = m0 + wm * WM, nw = n0 + wn * WN;
+  const int64_t mw = m0 + wm * WM, nw = n0 + wn * WNT;
   const int chunk = lane & 15;  // 8 bf16 columns
-  if (mw + WM <= M && nw + WN <= N) {
+  // a 96-column wave tile has 12 chunks per row: lanes 12..15 of each row idle
+  const bool chunk_ok = WNT == 128 || chunk < WNT / 8;
+  if (mw + WM <= M && nw + WNT <= N) {
     // whole wave tile inside C: all row reads first, then the stores, with
     // no per-row tests (a read-then-test loop waits out the LDS latency
     // once per row)
     v4u v[WM / 4];
 #pragma unroll
     for (int u = 0; u < WM / 4; ++u)
-      v[u] = lds_read16_a8(slot + (4 * u + (lane >> 4)) * kEpiRowBytes + chunk * 16);
+      v[u] = lds_read16_a8(slot + (4 * u + (lane >> 4)) * kEpiRowBytesT + chunk * 16);
     uint16_t* dst = C + (mw + (lane >> 4)) * ldc + nw + chunk * 8;
+    if (chunk_ok) {
 #pragma unroll
-    for (int u = 0; u < WM / 4; ++u)
-      __builtin_nontemporal_store(v[u], reinterpret_cast<v4u*>(dst + 4 * u * ldc));
+      for (int u = 0; u < WM / 4; ++u)
+        __builtin_nontemporal_store(v[u], reinterpret_cast<v4u*>(dst + 4 * u * ldc));
+    }
     return;
   }
 #pragma unroll
   for (int u = 0; u < WM / 4; ++u) {
     const int row = 4 * u + (lane >> 4);
-    const v4u v = lds_read16_a8(slot + row * kEpiRowBytes + chunk * 16);
+    const v4u v = lds_read16_a8(slot + row * kEpiRowBytesT + chunk * 16);
     const int64_t m = mw + row, n = nw + chunk * 8;
-    if (m >= M) continue;
+    if (m >= M || !chunk_ok) continue;
     uint16_t* dst = C + m * ldc + n;
     if (n + 7 < N) {
       __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(dst));
@@ -1153,7 +1172,7 @@ static bfp8_status launch_layout(const GemmArgs& a, dim3 grid, dim3 pgrid, const
                     plan.tiles_m, plan.tiles_n, plan.splits, plan.part,                       \
                     (a.N + 3) & ~int64_t(3), pstride);                                        \
     else                                                                                      \
-      return launch(&gemm_kernel<A_KM, B_KM, MA, MB>, grid, dim3(kThreads), stream, a.A,      \
+      return launch(&gemm_kernel<A_KM, B_KM, MA, MB, 256>, grid, dim3(kThreads), stream, a.A, \
                     a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K, plan);          \
   } while (0)
   // mode 3 (K-block-major act scales) is mode 0 for a K-major operand
@@ -1270,8 +1289,47 @@ static int64_t mx_scale_row_offset(bool a_kmajor, int mode, int64_t r0, int64_t 
   }
 }
 
+// 256 x 192 tiles for the float32 kernel (NT, 1x128 scales on B): taken
+// when N is a multiple of 192, the 256-column plan runs unsplit, and the
+// narrower tiles fill whole waves where the 256-column ones leave CUs idle
+// (the 2048 x 6144 wgrad output: 256 tiles instead of 192).  A K block of
+// such a tile is priced at 0.75 of a 256 x 256 block times 1.15 for its
+// larger copy and fragment bytes per flop.
+static bool use_192_columns(int64_t M, int64_t N, int64_t K) {
+  constexpr int64_t kCUs = 256;
+  constexpr double kBlockUs = 1.6, kUnitUs = 5.0;
+  if (N % 192 != 0 || gemm_plan(M, N, K, false).splits > 1) return false;
+  const int64_t KB = K / BK, tiles_m = (M + BM - 1) / BM;
+  const int64_t t256 = tiles_m * ((N + BN - 1) / BN), t192 = tiles_m * (N / 192);
+  if (t192 >= (int64_t(1) << 31)) return false;
+  auto waves = [&](int64_t u) { return static_cast<double>((u + kCUs - 1) / kCUs); };
+  const double c256 = waves(t256) * (KB * kBlockUs + kUnitUs);
+  const double c192 = waves(t192) * (KB * kBlockUs * 0.75 * 1.15 + kUnitUs);
+  return c192 < 0.95 * c256;
+}
+
 bfp8_status launch_gemm(const GemmArgs& a, void* workspace, size_t workspace_bytes,
                         hipStream_t stream) {
+  if (!a.mx && !a.a_kmajor && !a.b_kmajor && (a.modeB == 0 || a.modeB == 3) &&
+      (a.modeA == 0 || a.modeA == 3) && use_192_columns(a.M, a.N, a.K)) {
+    UnitPlan p;
+    p.tiles_m = static_cast<int>((a.M + BM - 1) / BM);
+    p.tiles_n = static_cast<int>(a.N / 192);
+    p.full = p.tiles_m * p.tiles_n;
+    p.splits = 1;
+    p.piece = static_cast<int>(a.K / BK);
+    p.trow0 = 0;
+    p.part = nullptr;
+    const dim3 g(static_cast<unsigned>(p.full));
+#define BFP8_LAUNCH192(MA, MB)                                                                 \
+  return launch(&gemm_kernel<false, false, MA, MB, 192>, g, dim3(kThreads), stream, a.A,       \
+                a.lda, a.sA, a.B, a.ldb, a.sB, a.C, a.ldc, a.M, a.N, a.K, p)
+    if (a.modeA == 0 && a.modeB == 0) BFP8_LAUNCH192(0, 0);
+    if (a.modeA == 0 && a.modeB == 3) BFP8_LAUNCH192(0, 3);
+    if (a.modeA == 3 && a.modeB == 0) BFP8_LAUNCH192(3, 0);
+    BFP8_LAUNCH192(3, 3);
+#undef BFP8_LAUNCH192
+  }
   const int64_t tiles_m = (a.M + BM - 1) / BM;
   const int64_t tiles_n = (a.N + BN - 1) / BN;
   const int64_t nblk = tiles_m * tiles_n;

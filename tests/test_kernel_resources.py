@@ -16,9 +16,11 @@ import pytest
 from blockwise_fp8_gemm_bfp8_amd import build as bfp8_build
 
 HOT = {
-    "fprop NT act x block": r"111gemm_kernelILb0ELb0ELi0ELi1EE",
-    "dgrad NN act x block": r"111gemm_kernelILb0ELb1ELi0ELi1EE",
-    "wgrad NT act x act": r"111gemm_kernelILb0ELb0ELi0ELi0EE",
+    "fprop NT act x block": r"111gemm_kernelILb0ELb0ELi0ELi1ELi256EE",
+    "dgrad NN act x block": r"111gemm_kernelILb0ELb1ELi0ELi1ELi256EE",
+    "wgrad NT act x act": r"111gemm_kernelILb0ELb0ELi0ELi0ELi256EE",
+    # 256 x 192 tiles (the 2048 x 6144 wgrad output), K-block-major act scales
+    "wgrad NT act x act, 192 columns": r"111gemm_kernelILb0ELb0ELi3ELi3ELi192EE",
     # power-of-two (E8M0) scales, hardware-scaled MFMA, 4 waves
     "mx fprop NT act x block": r"gemm_mx4_kernelILb0ELb0ELi0ELi1EE",
     "mx dgrad NN act x block": r"gemm_mx4_kernelILb0ELb1ELi0ELi1EE",

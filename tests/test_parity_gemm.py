@@ -186,3 +186,30 @@ def test_hybrid_split_plan(M, N, modes):
     ac, asc = oracle.logical_operand(qa[rows], sa[rows], "A", "N", ma)  # 1x128 A scales
     for name, C in (("hybrid", hybrid), ("unsplit", unsplit)):
         gate.check(C.float().cpu().numpy()[rows], ac, asc, bc, bsc, (name, M, N, K, modes))
+
+
+@pytest.mark.parametrize("M,modes", [(2048, ("act", "act")), (2000, ("act", "act")),
+                                     (2048, ("act_km", "act_km")), (2048, ("act", "act_km"))])
+def test_192_column_tiles(M, modes):
+    """An NT GEMM with 1x128 scales on B and N = 6144 (the 2048 x 6144 wgrad
+    output) runs as 256 x 192 tiles, 8 x 32 of them, where 256-column tiles
+    would leave 64 CUs idle.  Every output is summed in the same order as
+    with 256-column tiles, so the bytes must equal those of N = 6152 (which
+    does not divide by 192 and runs 256-column tiles) on the shared columns;
+    sampled rows, the ragged last row tile included, meet the parity bound."""
+    N, K = 6144, 2048
+    ma, mb = modes
+    rng = np.random.default_rng(M + len(ma) + 3 * len(mb))
+    base = [m.replace("_km", "") for m in modes]
+    qa, sa, qb, sb = random_operands(rng, "NT", M, N + 8, K, *base)
+    sa_d = dense(sa) if ma == "act" else dense(np.ascontiguousarray(sa.T))   # [K/128][M]
+    sbk = sb if mb == "act" else np.ascontiguousarray(sb.T)                  # [K/128][N]
+    narrow = bfp8.gemm("NT", dev_padded(qa), sa_d, dev_padded(qb[:N]),
+                       dense(sbk[:N] if mb == "act" else sbk[:, :N]), ma, mb)
+    wide = bfp8.gemm("NT", dev_padded(qa), sa_d, dev_padded(qb), dense(sbk), ma, mb)
+    torch.cuda.synchronize()
+    assert torch.equal(narrow.view(torch.int16), wide[:, :N].view(torch.int16))
+    rows = np.r_[0:M:37, M - 16:M]
+    ac, asc = oracle.logical_operand(qa[rows], sa[rows], "A", "N", "act")
+    bc, bsc = oracle.logical_operand(qb[:N], sb[:N], "B", "T", "act")
+    gate.check(narrow.float().cpu().numpy()[rows], ac, asc, bc, bsc, ("192 columns", M, modes))
