@@ -29,7 +29,12 @@
 //   * XCD-aware tile order: consecutive tiles go to the same XCD (the
 //     hardware deals workgroups to the 8 XCDs round robin) and tiles are
 //     grouped along M so concurrent tiles on an XCD share A rows and B
-//     columns in that XCD's L2.
+//     columns in that XCD's L2;
+//   * grids that under-fill the GPU: whole waves of tiles run unsplit and
+//     only the tiles of a last, partial wave are split along K (fp32
+//     partials summed in split order by a second kernel), or, for NT
+//     problems with 1x128 scales on B, 256 x 192 tiles where they fill
+//     whole waves that 256 x 256 tiles would leave partly idle.
 //
 // Operands whose scales are powers of two stored as E8M0 bytes (Puro-2B
 // translation, section 3.2: the SM120 runs used power-of-two block scales on
