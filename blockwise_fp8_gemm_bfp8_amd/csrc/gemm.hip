@@ -1275,22 +1275,29 @@ GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, bool mx) {
   return plan;
 }
 
-size_t gemm_split_workspace(int64_t M, int64_t N, int64_t K, bool mx) {
-  const GemmPlan p = gemm_plan(M, N, K, mx);
-  return p.splits > 1 ? static_cast<size_t>(p.splits) * (M - p.row0) * split_ldp(N) * sizeof(float)
-                      : 0;
+// Bytes of the fp32 partials of a plan, rounded up to 256.
+static size_t partial_bytes(const GemmPlan& p, int64_t M, int64_t N) {
+  const size_t b = static_cast<size_t>(p.splits) * (M - p.row0) * split_ldp(N) * sizeof(float);
+  return (b + 255) & ~size_t(255);
 }
 
-// Byte offset of the E8M0 scales of A's row r0 (a multiple of 128), for A
-// stored [M][K] (a_kmajor false) or [K][M], in scale mode `mode`.
-static int64_t mx_scale_row_offset(bool a_kmajor, int mode, int64_t r0, int64_t K) {
+size_t gemm_split_workspace(int64_t M, int64_t N, int64_t K, bool mx) {
+  const GemmPlan p = gemm_plan(M, N, K, mx);
+  if (p.splits == 1) return 0;
+  // the power-of-two kernel's whole-wave plan also copies A's K-block-major
+  // scale bytes of the split rows: K/128 x (M - row0) bytes at most
+  const size_t extra = (mx && p.full > 0) ? static_cast<size_t>(K / BK) * (M - p.row0) : 0;
+  return partial_bytes(p, M, N) + extra;
+}
+
+// Byte offset of the E8M0 scales of row r0 (a multiple of 128) of an A
+// stored [M][K] with row-major scales in mode `mode` (0, 1 or 2).
+static int64_t mx_scale_row_offset(int mode, int64_t r0, int64_t K) {
   const int64_t KB = K / BK;
-  if (a_kmajor) return mode == 1 ? r0 / 128 : r0;  // [KB][M/128] or [KB][M]
   switch (mode) {
-    case 0: return r0 * KB;                         // [M][KB]
     case 1: return (r0 / 128) * KB;                 // [M/128][KB]
     case 2: return r0 * (K / 32);                   // [M][K/32]
-    default: return r0;                             // 3: [KB][M]
+    default: return r0 * KB;                        // 0: [M][KB]
   }
 }
 
@@ -1377,10 +1384,12 @@ bfp8_status launch_gemm(const GemmArgs& a, void* workspace, size_t workspace_byt
   if (a.mx && gp.splits > 1 && gp.full > 0) {
     // the persistent kernel splits every tile of a launch alike, so the plan
     // runs as two launches: the whole tiles (output rows [0, row0)), then the
-    // rows [row0, M) as a GEMM of their own whose operand A, scales and C
-    // start row0 rows in (M itself stays the scales' row count; M - row0 is
-    // a multiple of 256, so no tile of either launch reaches past its rows),
-    // its partials (M - row0) rows per split as in the float32 kernel
+    // rows [row0, M) as an (M - row0)-row GEMM of their own whose operand A,
+    // its scales and C start row0 rows in, its partials (M - row0) rows per
+    // split as in the float32 kernel.  Row-major scales ([rows][...]) are
+    // used in place; K-block-major ones ([K/128][rows or row blocks], whose
+    // row count is their stride) are first copied, rows [row0, M) of every
+    // K block, to the end of the workspace.  M - row0 is a multiple of 256.
     UnitPlan p1 = plan, p2 = plan;
     p1.tiles_m = plan.trow0;
     p1.full = plan.trow0 * plan.tiles_n;
@@ -1389,10 +1398,23 @@ bfp8_status launch_gemm(const GemmArgs& a, void* workspace, size_t workspace_byt
     st = launch_mx(a, p1, min_wgs(p1.full), 0);
     if (st != BFP8_OK) return st;
     GemmArgs a2 = a;
+    a2.M = a.M - gp.row0;
     a2.A = a.A + (a.a_kmajor ? gp.row0 : gp.row0 * a.lda);
-    a2.sA = static_cast<const uint8_t*>(a.sA) +
-            mx_scale_row_offset(a.a_kmajor, a.modeA, gp.row0, a.K);
     a2.C = a.C + gp.row0 * a.ldc;
+    const uint8_t* sa8 = static_cast<const uint8_t*>(a.sA);
+    if (!a.a_kmajor && a.modeA != 3) {
+      a2.sA = sa8 + mx_scale_row_offset(a.modeA, gp.row0, a.K);
+    } else {
+      const bool blk = a.modeA == 1;
+      const int64_t cols = blk ? a.M / 128 : a.M, sub = blk ? a2.M / 128 : a2.M;
+      const int64_t off = blk ? gp.row0 / 128 : gp.row0;
+      uint8_t* dst = static_cast<uint8_t*>(workspace) + partial_bytes(gp, a.M, a.N);
+      if (hipMemcpy2DAsync(dst, static_cast<size_t>(sub), sa8 + off, static_cast<size_t>(cols),
+                           static_cast<size_t>(sub), static_cast<size_t>(a.K / BK),
+                           hipMemcpyDeviceToDevice, stream) != hipSuccess)
+        return BFP8_ERR_HIP;
+      a2.sA = dst;
+    }
     p2.tiles_m = plan.tiles_m - plan.trow0;
     p2.full = 0;
     st = launch_mx(a2, p2, min_wgs(static_cast<int64_t>(p2.tiles_m) * p2.tiles_n * p2.splits),

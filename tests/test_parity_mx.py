@@ -301,13 +301,18 @@ def test_gemm_mx_hybrid_split_plan():
     a second launch that starts 8192 rows into A, its scales and C.  The
     whole tiles equal the unsplit plan's bytes (a plan that split every tile
     would sum them in another order); sampled rows, every split row
-    included, meet the parity bound."""
+    included, meet the parity bound.  K-block-major A scales are copied,
+    rows 8192.. of every K block, before the second launch."""
     M, N, K = 8448, 2048, 4096
     rng = np.random.default_rng(23)
     rows = np.r_[0:8192:61, 8192:M]
     for layout, ma, mb in (("NT", "act", "act"), ("NT", "mx32", "mx32"), ("NT", "act", "block"),
-                           ("TN", "act", "act")):
-        qa, sa, qb, sb = pins_mx.random_mx_operands(rng, layout, ma, mb, M, N, K)
+                           ("TN", "act", "act"), ("NT", "act_km", "act_km")):
+        base = (ma.replace("_km", ""), mb.replace("_km", ""))
+        qa, sa, qb, sb = pins_mx.random_mx_operands(rng, layout, *base, M, N, K)
+        if ma == "act_km":  # K-block-major scale bytes, [K/128][rows]
+            sa_r, sb_r = sa, sb
+            sa, sb = np.ascontiguousarray(sa.T), np.ascontiguousarray(sb.T)
         assert bfp8.gemm_workspace_bytes(layout, ma, mb, M, N, K) > 0  # a split plan
         hybrid = run_mx(layout, qa, sa, ma, qb, sb, mb)
         unsplit = run_mx(layout, qa, sa, ma, qb, sb, mb, split_k=False)
@@ -315,7 +320,10 @@ def test_gemm_mx_hybrid_split_plan():
         assert torch.equal(hybrid, again)
         assert torch.equal(hybrid[:8192].view(torch.int16), unsplit[:8192].view(torch.int16))
         # A's sampled rows: stored rows for 'N', stored columns for 'T' (1x128 scales)
-        qs, ss = (qa[rows], sa[rows]) if layout[0] == "N" else (qa[:, rows], sa[:, rows])
-        parts = gate.operand_parts(layout, qs, ss, ma, qb, sb, mb, mx=True)
+        if ma == "act_km":
+            parts = gate.operand_parts(layout, qa[rows], sa_r[rows], "act", qb, sb_r, "act", mx=True)
+        else:
+            qs, ss = (qa[rows], sa[rows]) if layout[0] == "N" else (qa[:, rows], sa[:, rows])
+            parts = gate.operand_parts(layout, qs, ss, ma, qb, sb, mb, mx=True)
         for name, C in (("hybrid", hybrid), ("unsplit", unsplit)):
             gate.check(C.float().cpu().numpy()[rows], *parts, (name, layout, ma, mb), mx=True)
