@@ -1285,8 +1285,10 @@ size_t gemm_split_workspace(int64_t M, int64_t N, int64_t K, bool mx) {
   const GemmPlan p = gemm_plan(M, N, K, mx);
   if (p.splits == 1) return 0;
   // the power-of-two kernel's whole-wave plan also copies A's K-block-major
-  // scale bytes of the split rows: K/128 x (M - row0) bytes at most
-  const size_t extra = (mx && p.full > 0) ? static_cast<size_t>(K / BK) * (M - p.row0) : 0;
+  // scale bytes of the split rows: K/128 x (M - row0) bytes at most, read as
+  // aligned 32-bit words (so up to 3 bytes past the copy)
+  const size_t extra =
+      (mx && p.full > 0) ? (static_cast<size_t>(K / BK) * (M - p.row0) + 4 + 255) & ~size_t(255) : 0;
   return partial_bytes(p, M, N) + extra;
 }
 

@@ -316,7 +316,11 @@ bfp8_status bfp8_quantize_mx_weight_batch(const bfp8_mx_weight_job* jobs, int n,
  * rounded to bf16 (RNE).  On gfx950 the scales ride in the matrix-core
  * instruction itself (v_mfma_scale_f32_16x16x128_f8f6f4), so the exact
  * power-of-two scaling replaces the per-128-K promotion of bfp8_gemm.
- * Same layouts, shapes, leading-dimension and workspace rules as bfp8_gemm;
+ * Same layouts, shapes, leading-dimension and workspace rules as bfp8_gemm
+ * (the workspace may also receive a copy of part of A's scales: under the
+ * plan that splits only the tiles past whole waves, the split rows run as a
+ * GEMM of their own, and K-block-major scales of those rows are copied for
+ * it; bfp8_gemm_workspace_bytes counts this);
  * scale tensors are uint8 E8M0 in the layouts of the table at the top of
  * this file, with BFP8_SCALE_1x32 as [rows][K/32] (K-contiguous operands
  * only: A of NN/NT, B of NT; otherwise BFP8_ERR_SCALE_MODE).  Each scale

@@ -210,8 +210,8 @@ def test_workspace_query(L):
     # the partials cover those rows only, for both GEMM entry points (1x32
     # modes exist only for the E8M0 one, which also keeps room to copy the
     # split rows' K-block-major scale bytes: 128 K blocks x 4096 rows)
-    assert L.bfp8_gemm_workspace_bytes(1, 2, 2, 12288, 2048, 16384) == 2 * 4096 * 2048 * 4 + 128 * 4096
-    assert L.bfp8_gemm_workspace_bytes(1, 0, 0, 12288, 2048, 16384) == 2 * 4096 * 2048 * 4 + 128 * 4096
+    assert L.bfp8_gemm_workspace_bytes(1, 2, 2, 12288, 2048, 16384) == 2 * 4096 * 2048 * 4 + 128 * 4096 + 256
+    assert L.bfp8_gemm_workspace_bytes(1, 0, 0, 12288, 2048, 16384) == 2 * 4096 * 2048 * 4 + 128 * 4096 + 256
     # 8 x 24 tiles under-fill the GPU but splitting costs more: unsplit
     assert L.bfp8_gemm_workspace_bytes(1, 0, 0, 2048, 6144, 16384) == 0
     assert L.bfp8_gemm_workspace_bytes(1, 2, 2, 2048, 2048, 16384) == 4 * 2048 * 2048 * 4
