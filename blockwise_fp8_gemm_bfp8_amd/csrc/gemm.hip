@@ -909,11 +909,14 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
       const uint32_t o = static_cast<uint32_t>(kbw * M + cm0) & 3u;
       return sb[o + wm * W4M + 16 * i + r16];
     }
+    // 1x32 groups: the row's word holds its four 32-deep chunks; the lane
+    // reads the byte of its own chunk g
+    if constexpr (MA == 2) return sb[4 * (wm * W4M + 16 * i + r16) + g];
     const uint32_t* w = reinterpret_cast<const uint32_t*>(sb);
     return MA == 1 ? w[(wm * W4M) / 128] : w[wm * W4M + 16 * i + r16];
   };
   auto byte_a = [&](uint32_t word, int64_t kb, int i) -> int {
-    if constexpr (kBytesA) return static_cast<int>(word);
+    if constexpr (kBytesA || MA == 2) return static_cast<int>(word);
     const uint32_t ka = kterm(MA, SKA, M, MBk, kb);
     const uint32_t sh = MA == 2 ? 8u * g : 8u * (((pack_a >> (2 * i)) + ka) & 3u);
     return static_cast<int>((word >> sh) & 0xFFu);
@@ -924,11 +927,12 @@ gemm_mx4_kernel(const uint8_t* __restrict__ A, int64_t lda, const void* __restri
       const uint32_t o = static_cast<uint32_t>(kbw * N + cn0) & 3u;
       return sb[o + wn * W4N + 16 * j + r16];
     }
+    if constexpr (MB == 2) return sb[4 * (wn * W4N + 16 * j + r16) + g];
     const uint32_t* w = reinterpret_cast<const uint32_t*>(sb);
     return MB == 1 ? w[(wn * W4N) / 128] : w[wn * W4N + 16 * j + r16];
   };
   auto byte_b = [&](uint32_t word, int64_t kb, int j) -> int {
-    if constexpr (kBytesB) return static_cast<int>(word);
+    if constexpr (kBytesB || MB == 2) return static_cast<int>(word);
     const uint32_t kbb = kterm(MB, SKB, N, NBk, kb);
     const uint32_t sh = MB == 2 ? 8u * g : 8u * (((pack_b >> (2 * j)) + kbb) & 3u);
     return static_cast<int>((word >> sh) & 0xFFu);
